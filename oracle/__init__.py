@@ -1,0 +1,136 @@
+"""CPU oracle of the leaky-tanh sparse-graph recurrence (fp64, plain C + OpenMP).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, by the smoke check and by
+the benchmark's CPU-baseline leg, never by the product package.  It shares no
+code with the HIP library.  What it computes is stated in ``ck_oracle.c``,
+following the connectome-kernels README (introduction: the proposal/update
+equations; "Use": argument shapes and edge order; "Design notes": the saved
+state and pre-activation).
+
+Parity: the forward is pinned by a dense brute-force recurrence, by the tanh
+Elman RNN special case (torch.nn.RNN) and by closed forms; the gradient is
+pinned by central finite differences, by torch autograd on dense fp64
+formulations and by closed forms (see tests/test_oracle_pins.py).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libckoracle.so")
+_lib = None
+
+# Status values of the documented error convention (restated, not shared).
+STATUS = {0: "ok", 1: "null_arg", 2: "bad_size", 3: "index_range", 4: "dup_input",
+          5: "too_large", 7: "nomem"}
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"oracle status {code} ({STATUS.get(code, '?')})")
+        self.code = code
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.ckor_validate.restype = ctypes.c_int
+        lib.ckor_validate.argtypes = [i64, i64, p, p, i64, p]
+        lib.ckor_build.restype = ctypes.c_int
+        lib.ckor_build.argtypes = [i64, i64, p, p, i64, p] + [p] * 7
+        lib.ckor_run.restype = ctypes.c_int
+        lib.ckor_run.argtypes = [i64, i64, p, p, i64, p, p, p, p, p, p, i64, i64, i64,
+                                 p, p, p, p, p, p, p, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def validate(src, dst, num_nodes, input_nodes) -> int:
+    """Status code the documented validation rules give for this graph."""
+    src, dst, inp = _i64(src), _i64(dst), _i64(input_nodes)
+    if src.shape != dst.shape:
+        return 2
+    return int(_load().ckor_validate(num_nodes, src.size, _ptr(src), _ptr(dst), inp.size, _ptr(inp)))
+
+
+def build_graph(src, dst, num_nodes: int, input_nodes):
+    """CSR by destination and transposed CSR by source, ties by caller index.
+
+    Returns a dict of int32 arrays: row_ptr, col_idx, perm, t_row_ptr,
+    t_col_idx, t_perm, input_slot.
+    """
+    src, dst, inp = _i64(src), _i64(dst), _i64(input_nodes)
+    if src.shape != dst.shape:
+        raise OracleError(2)
+    N, E = int(num_nodes), src.size
+    n = max(N, 0)
+    res = {
+        "row_ptr": np.zeros(n + 1, np.int32), "col_idx": np.zeros(E, np.int32),
+        "perm": np.zeros(E, np.int32), "t_row_ptr": np.zeros(n + 1, np.int32),
+        "t_col_idx": np.zeros(E, np.int32), "t_perm": np.zeros(E, np.int32),
+        "input_slot": np.zeros(n, np.int32),
+    }
+    rc = _load().ckor_build(N, E, _ptr(src), _ptr(dst), inp.size, _ptr(inp),
+                            *[_ptr(res[k]) for k in ("row_ptr", "col_idx", "perm", "t_row_ptr",
+                                                     "t_col_idx", "t_perm", "input_slot")])
+    if rc:
+        raise OracleError(rc)
+    return res
+
+
+def run(src, dst, num_nodes: int, input_nodes, edge_values, leak, bias, drives, state0,
+        microsteps: int, grad_out=None, nthreads: int = 0):
+    """Forward (and, with grad_out, the gradient of sum(out * grad_out)).
+
+    Shapes: edge_values[E] (caller order), leak[N], bias[N], drives[T, n_in, B],
+    state0[B, N], grad_out[T, B, N].  Returns a dict with ``out`` [T, B, N] and,
+    with grad_out, ``g_edge_values``, ``g_leak``, ``g_bias``, ``g_drives``,
+    ``g_state0`` -- all float64.
+    """
+    src, dst, inp = _i64(src), _i64(dst), _i64(input_nodes)
+    v, lk, bs = _f64(edge_values), _f64(leak), _f64(bias)
+    st0 = _f64(state0)
+    N, E, n_in = int(num_nodes), src.size, inp.size
+    B = st0.shape[0]
+    dr = _f64(drives)
+    T = dr.shape[0]
+    if dr.shape != (T, n_in, B) or st0.shape != (B, N) or v.shape != (E,) \
+            or lk.shape != (N,) or bs.shape != (N,):
+        raise OracleError(2)
+    out = np.zeros((T, B, N), np.float64)
+    res = {"out": out}
+    G = None
+    args_g = [None] * 5
+    if grad_out is not None:
+        G = _f64(grad_out)
+        if G.shape != (T, B, N):
+            raise OracleError(2)
+        res.update(g_edge_values=np.zeros(E), g_leak=np.zeros(N), g_bias=np.zeros(N),
+                   g_drives=np.zeros((T, n_in, B)), g_state0=np.zeros((B, N)))
+        args_g = [res[k] for k in ("g_edge_values", "g_leak", "g_bias", "g_drives", "g_state0")]
+    rc = _load().ckor_run(N, E, _ptr(src), _ptr(dst), n_in, _ptr(inp), _ptr(v), _ptr(lk), _ptr(bs),
+                          _ptr(dr), _ptr(st0), T, B, int(microsteps), _ptr(G), _ptr(out),
+                          *[_ptr(a) for a in args_g], int(nthreads))
+    if rc:
+        raise OracleError(rc)
+    return res

@@ -1,0 +1,26 @@
+"""Compile the CPU oracle (plain C, fp64, OpenMP) into oracle/libckoracle.so.
+
+Test infrastructure: the oracle is built so that the test suite, the smoke
+check and the benchmark's CPU-baseline leg can call it; the product never does.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "ck_oracle.c")
+LIB = os.path.join(HERE, "libckoracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
+           "-fno-fast-math", "-o", LIB, SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)
