@@ -1,0 +1,185 @@
+"""Benchmark: forward + backward training step of the leaky-tanh recurrence at
+the FlyGPT launch shape (N=5,000 nodes, E=524,324 edges, B=32, T=64 input
+steps x 2 microsteps, fp32) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu]
+
+One step = ck_recurrence_forward + ck_recurrence_backward over the whole
+window on one HIP stream; inputs, graph and buffers are resident in HBM
+before timing starts (graph construction and input generation are excluded).
+Prints one JSON line with:
+  value        edge-visits/s = S * E * B / t_step  (S = T * M microsteps)
+  ms_per_step  mean time of one step over the K timed steps (HIP events)
+  roofline     the dominant kernel's algorithmic bytes per launch / its mean
+               launch duration (HIP events around each launch, recorded by the
+               library's measurement hook on the stream the kernels run on)
+               against the MI355X HBM peak of 8 TB/s
+  cpu_baseline the CPU oracle's rate on the same workload (host cores)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "ms per fwd+bwd step & edge-visits/s, N=5k E=524k B=32 T×M=64×2; HBM GB/s"
+
+
+def algorithmic_bytes(N, E, n_in, B, T, M):
+    """Byte yardstick of the method's kernel structure: each pass reads its
+    operands once and writes its results once (gathers beyond the first read
+    of a row count as cache hits).  Returns per-microstep forward and backward
+    bytes and the per-step total."""
+    NB = N * B
+    fwd = 8 * E + 4 * (N + 1) + 12 * N + 4 * n_in * B + 12 * NB
+    k1 = 16 * NB + 24 * N + 8 * n_in * B               # elementwise + leak/bias reductions
+    k2 = 8 * E + 4 * (N + 1) + 4 * N + 12 * NB         # transposed product
+    k3 = 12 * E + 4 * (N + 1) + 8 * NB                 # edge dot product (gv read-modify-write)
+    bwd = k1 + k2 + k3
+    once = 8 * T * NB + 36 * E + 16 * NB               # out/G, value permutations + scatter, state0
+    S = T * M
+    return fwd, bwd, S * (fwd + bwd) + once
+
+
+def cpu_baseline(w, budget_s: float = 20.0):
+    """The CPU oracle (fp64, OpenMP over all host cores) on the same workload:
+    whole forward+backward windows, repeated until about budget_s seconds."""
+    import oracle
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    S, E, B = w.T * w.microsteps, w.num_edges, w.B
+    runs, total = 0, 0.0
+    while runs == 0 or (total < budget_s and runs < 5):
+        t0 = time.perf_counter()
+        oracle.run(w.src, w.dst, w.num_nodes, w.input_nodes, w.edge_values, w.leak, w.bias,
+                   w.drives, w.state0, w.microsteps, grad_out=w.grad_out, nthreads=threads)
+        total += time.perf_counter() - t0
+        runs += 1
+    per = total / runs
+    return {"value": S * E * B / per, "unit": "edge-visits/s", "cores": threads, "kind": "oracle",
+            "sample": f"{runs} full forward+backward window(s) of the benchmark workload "
+                      f"(all {B} batch columns, {S} microsteps), fp64, {per:.2f} s each"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--workload", default="flygpt")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the recurrence would "
+              f"shard over the batch across GPUs, which this build does not implement.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_graph_recurrent_amd as sgr
+    import synthetic
+
+    torch.cuda.set_device(0)
+    w = synthetic.make(args.workload)
+    N, E, n_in, B, T, M = w.num_nodes, w.num_edges, w.n_in, w.B, w.T, w.microsteps
+    S = T * M
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    graph = sgr.SparseGraph(dev(w.src), dev(w.dst), N, dev(w.input_nodes))
+    ev, lk, bs, dr, st, G = (dev(x) for x in (w.edge_values, w.leak, w.bias, w.drives, w.state0,
+                                               w.grad_out))
+    sb, wb = sgr.recurrence_sizes(graph, T, B, M)
+    out = torch.empty((T, B, N), dtype=torch.float32, device="cuda")
+    saved = torch.empty(sb, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(wb, dtype=torch.uint8, device="cuda")
+    f = dict(dtype=torch.float32, device="cuda")
+    grads = {"g_edge_values": torch.empty(E, **f), "g_leak": torch.empty(N, **f),
+             "g_bias": torch.empty(N, **f), "g_drives": torch.empty((T, n_in, B), **f),
+             "g_state0": torch.empty((B, N), **f)}
+
+    def step():
+        sgr.recurrence_forward(graph, ev, lk, bs, dr, st, M, out=out, saved=saved, workspace=ws)
+        sgr.recurrence_backward(graph, ev, lk, st, M, saved, G, workspace=ws, grads=grads)
+
+    run = step
+    if args.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            step()
+        run = cg.replay
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-launch kernel durations: HIP events around every per-microstep launch
+    sgr.profile_collect()
+    sgr.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    sgr.profile_enable(False)
+    prof = sgr.profile_collect()
+    fwd_us = 1e3 * prof["fwd_ms"] / max(prof["fwd_launches"], 1)
+    bwd_us = 1e3 * prof["bwd_ms"] / max(prof["bwd_launches"], 1)
+
+    fwd_b, bwd_b, Q = algorithmic_bytes(N, E, n_in, B, T, M)
+    # the backward kernel dominates; its launch S+1 of each step has no edge
+    # pass, so the per-launch average is taken over all S+1 launches of
+    # S microsteps' worth of backward bytes
+    bwd_per_launch_b = bwd_b * S / (S + 1)
+    if prof["bwd_ms"] >= prof["fwd_ms"]:
+        name, per_b, us = "bwd_step", bwd_per_launch_b, bwd_us
+    else:
+        name, per_b, us = "fwd_step", fwd_b, fwd_us
+    achieved = per_b / (us * 1e-6) / 1e9
+    visits = S * E * B
+    res = {
+        "metric": METRIC,
+        "value": visits / (ms * 1e-3),
+        "unit": "edge-visits/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: N={N} E={E} n_in={n_in} B={B} T={T} "
+                               f"microsteps={M} (seed {w.seed})",
+                   "parallelism": "single GPU", "hip_graph": bool(args.graph)},
+        "yardstick_GBps": Q / (ms * 1e-3) / 1e9,
+        "yardstick_frac_of_hbm_peak": Q / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernels": {"fwd_step_us": fwd_us, "bwd_step_us": bwd_us,
+                    "fwd_launches_per_step": S, "bwd_launches_per_step": S + 1},
+        "roofline": {"bound": "hbm", "kernel": name, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

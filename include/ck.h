@@ -1,0 +1,179 @@
+/*
+ * ck.h -- C ABI of the MI355X (gfx950) leaky-tanh sparse-graph recurrence library.
+ *
+ * The method (connectome-kernels README, introduction): every node i of a fixed
+ * sparse directed graph carries one scalar state per batch column and every
+ * edge one trainable scalar value.  For each input step t = 0..T-1 the update
+ *
+ *     proposal_i = tanh( sum_j W_ij h_j + drive_i + bias_i )
+ *     h_i       <- (1 - leak_i) h_i + leak_i * proposal_i
+ *
+ * is applied `microsteps` (M) times, every node reading the previous
+ * microstep's states.  An edge e (src[e] -> dst[e]) contributes its value to
+ * W[dst[e]][src[e]]; parallel edges add and self-loops are allowed.  drives
+ * enter only at the designated input nodes and are held for all M microsteps
+ * of a step.  out[t] is the state after the last microstep of step t.  The
+ * gradient (all five inputs: edge values, leak, bias, drives, initial state)
+ * is that of a scalar loss given its upstream gradient grad_out = dL/dout.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is caller-owned device memory (hipMalloc'ed or
+ *     torch CUDA storage), contiguous, fp32 for values and int64 for indices.
+ *     A NULL pointer is accepted only for a tensor of zero elements.
+ *   - Errors are returned as ck_status; no exception crosses the ABI.
+ *     ck_last_error() gives a thread-local detail string of the last failure.
+ *   - Forward and backward are asynchronous on `stream` and validate only
+ *     scalars and pointers on the host.  NaN/Inf inputs are not checked; they
+ *     propagate.
+ *   - Sizes: num_nodes and num_edges must be below 2^31, and num_nodes times
+ *     the padded batch width (B rounded up to a multiple of 4) must be below
+ *     2^31; otherwise CK_ERR_TOO_LARGE.
+ *   - A graph handle is immutable after creation and may be used from several
+ *     streams at once provided each call has its own `saved` and `workspace`.
+ *   - Calls that share a `saved` or `workspace` buffer must be ordered on one
+ *     stream (or otherwise synchronised) by the caller.
+ */
+#ifndef CK_H
+#define CK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ck_graph* ck_graph_t;
+
+typedef enum {
+  CK_OK = 0,
+  CK_ERR_NULL_ARG = 1,    /* NULL pointer for a non-empty tensor or an output handle */
+  CK_ERR_BAD_SIZE = 2,    /* num_nodes <= 0, negative counts, T/B/microsteps <= 0 */
+  CK_ERR_INDEX_RANGE = 3, /* src/dst/input_nodes outside [0, num_nodes) */
+  CK_ERR_DUP_INPUT = 4,   /* the same node listed twice in input_nodes */
+  CK_ERR_TOO_LARGE = 5,   /* a size that would overflow 32-bit indexing */
+  CK_ERR_WORKSPACE = 6,   /* workspace_bytes below what ck_recurrence_sizes reports */
+  CK_ERR_NOMEM = 7,       /* device or host allocation failed */
+  CK_ERR_HIP = 8,         /* a HIP runtime call failed; see ck_last_error() */
+  CK_ERR_BAD_HANDLE = 9   /* NULL or destroyed graph handle */
+} ck_status;
+
+/*
+ * Build the graph structures on the device (connectome-kernels README, "Use":
+ * any directed graph as int64 src/dst lists plus num_nodes and input_nodes;
+ * "Design notes": the transposed CSR used by the backward).
+ *
+ *   src, dst     int64[num_edges] device, caller edge order (edge e: src[e] -> dst[e])
+ *   input_nodes  int64[num_inputs] device; node input_nodes[k] receives drives[t][k][:]
+ *   stream       HIP stream the build runs on; the call synchronises it
+ *   out          receives the new handle (owned by the caller; free with ck_graph_destroy)
+ *
+ * Internally: the CSR by destination (rows ordered by (src, caller index)),
+ * the transposed CSR by source (rows ordered by (dst, caller index)), both
+ * edge permutations, the input-slot map and the degree-balanced row schedules.
+ * The caller's edge order is kept for edge values and their gradient: the
+ * permutation is invisible outside.  Validation failures return
+ * CK_ERR_BAD_SIZE, CK_ERR_TOO_LARGE, CK_ERR_NULL_ARG, CK_ERR_INDEX_RANGE or
+ * CK_ERR_DUP_INPUT, checked in that order.
+ */
+ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int64_t num_edges,
+                          int64_t num_nodes, const int64_t* input_nodes, int64_t num_inputs,
+                          hipStream_t stream, ck_graph_t* out);
+
+/* Release a handle and its device arrays (synchronises the device).  NULL is accepted. */
+ck_status ck_graph_destroy(ck_graph_t g);
+
+/* Sizes the graph was created with (any output pointer may be NULL). */
+ck_status ck_graph_sizes(ck_graph_t g, int64_t* num_nodes, int64_t* num_edges,
+                         int64_t* num_inputs);
+
+/*
+ * Copy the internal graph arrays into caller device buffers (int32):
+ *   row_ptr[N+1], col_idx[E] (= src), perm[E] (= caller edge index)      CSR by dst
+ *   t_row_ptr[N+1], t_col_idx[E] (= dst), t_perm[E]                      CSR by src
+ *   input_slot[N] (k if node is input_nodes[k], else -1)
+ * Any pointer may be NULL to skip that array.  Asynchronous on `stream`.
+ */
+ck_status ck_graph_export(ck_graph_t g, int32_t* row_ptr, int32_t* col_idx, int32_t* perm,
+                          int32_t* t_row_ptr, int32_t* t_col_idx, int32_t* t_perm,
+                          int32_t* input_slot, hipStream_t stream);
+
+/*
+ * Buffer sizes for a window of T input steps, batch B and `microsteps` M.
+ *   saved_bytes      the saved-activation arena written by forward and read by
+ *                    backward: the state and the pre-activation after every
+ *                    microstep (connectome-kernels README, "Design notes"),
+ *                    2 * T * M * N * Bp * 4 bytes with Bp = B rounded up to a
+ *                    multiple of 4 (= 2*T*M*N*B*4 when B % 4 == 0).
+ *   workspace_bytes  scratch needed by either forward or backward.
+ */
+ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int64_t microsteps,
+                              size_t* saved_bytes, size_t* workspace_bytes);
+
+/*
+ * Forward over the whole window (connectome-kernels README, introduction and
+ * "Use"): one fused launch per microstep.
+ *
+ *   edge_values  fp32[E]           caller edge order
+ *   leak, bias   fp32[N]
+ *   drives       fp32[T][n_in][B]
+ *   state0       fp32[B][N]
+ *   out          fp32[T][B][N]     written: the state after each input step
+ *   saved        saved_bytes       written; must be kept for backward
+ *   workspace    workspace_bytes   scratch, contents undefined afterwards
+ */
+ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_values, const float* leak,
+                                const float* bias, const float* drives, const float* state0,
+                                int64_t T, int64_t B, int64_t microsteps, float* out,
+                                void* saved, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * Gradient of L given grad_out = dL/dout, for all five inputs
+ * (connectome-kernels README, introduction and "Design notes": elementwise
+ * gradients with per-node leak/bias reductions, the transposed sparse product
+ * for the state gradient, the per-edge batch dot product for the edge
+ * gradient; no sparse tensor is formed).  `saved` must come from the forward
+ * call with the same graph, edge values, leak, state0, T, B and microsteps.
+ *
+ *   grad_out          fp32[T][B][N]
+ *   grad_edge_values  fp32[E] caller edge order   (all five outputs are
+ *   grad_leak         fp32[N]                      overwritten, not
+ *   grad_bias         fp32[N]                      accumulated)
+ *   grad_drives       fp32[T][n_in][B]
+ *   grad_state0       fp32[B][N]
+ */
+ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_values, const float* leak,
+                                 const float* state0, int64_t T, int64_t B, int64_t microsteps,
+                                 const void* saved, const float* grad_out,
+                                 float* grad_edge_values, float* grad_leak, float* grad_bias,
+                                 float* grad_drives, float* grad_state0, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Measurement hook (changes no result).  While enabled (process-wide),
+ * forward and backward record a pair of HIP events on the caller's stream
+ * around every launch of the per-microstep kernels: the fused forward
+ * microstep kernel and the fused backward step kernel.  ck_profile_collect
+ * waits for the recorded events, returns the summed kernel durations in
+ * milliseconds and the launch counts since the last collect, and releases the
+ * events.  Any output pointer may be NULL.  Not meant for concurrent use from
+ * several threads.
+ */
+ck_status ck_profile_enable(int enable);
+ck_status ck_profile_collect(double* fwd_ms, int64_t* fwd_launches, double* bwd_ms,
+                             int64_t* bwd_launches);
+
+/* Static name of a status value. */
+const char* ck_status_string(ck_status s);
+
+/* Thread-local detail message of the last failing call on this thread ("" if none). */
+const char* ck_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CK_H */

@@ -20,8 +20,11 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libckoracle.so")
-_lib = None
+# "f64" is the oracle; "f32" is the same code evaluated in fp32, used only to
+# measure the fp32 rounding floor of the method (never as a parity reference).
+_LIB_PATHS = {"f64": os.path.join(_HERE, "libckoracle.so"),
+              "f32": os.path.join(_HERE, "libckoracle_f32.so")}
+_libs = {}
 
 # Status values of the documented error convention (restated, not shared).
 STATUS = {0: "ok", 1: "null_arg", 2: "bad_size", 3: "index_range", 4: "dup_input",
@@ -34,13 +37,13 @@ class OracleError(RuntimeError):
         self.code = code
 
 
-def _load():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+def _load(precision: str = "f64"):
+    path = _LIB_PATHS[precision]
+    if path not in _libs:
+        if not os.path.exists(path):
             from . import build as _b
             _b.build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(path)
         i64, p = ctypes.c_int64, ctypes.c_void_p
         lib.ckor_validate.restype = ctypes.c_int
         lib.ckor_validate.argtypes = [i64, i64, p, p, i64, p]
@@ -49,8 +52,8 @@ def _load():
         lib.ckor_run.restype = ctypes.c_int
         lib.ckor_run.argtypes = [i64, i64, p, p, i64, p, p, p, p, p, p, i64, i64, i64,
                                  p, p, p, p, p, p, p, ctypes.c_int]
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return _libs[path]
 
 
 def _ptr(a):
@@ -99,13 +102,14 @@ def build_graph(src, dst, num_nodes: int, input_nodes):
 
 
 def run(src, dst, num_nodes: int, input_nodes, edge_values, leak, bias, drives, state0,
-        microsteps: int, grad_out=None, nthreads: int = 0):
+        microsteps: int, grad_out=None, nthreads: int = 0, precision: str = "f64"):
     """Forward (and, with grad_out, the gradient of sum(out * grad_out)).
 
     Shapes: edge_values[E] (caller order), leak[N], bias[N], drives[T, n_in, B],
     state0[B, N], grad_out[T, B, N].  Returns a dict with ``out`` [T, B, N] and,
     with grad_out, ``g_edge_values``, ``g_leak``, ``g_bias``, ``g_drives``,
-    ``g_state0`` -- all float64.
+    ``g_state0`` -- all float64.  precision="f32" evaluates the same steps in
+    fp32 (rounding-floor measurement only).
     """
     src, dst, inp = _i64(src), _i64(dst), _i64(input_nodes)
     v, lk, bs = _f64(edge_values), _f64(leak), _f64(bias)
@@ -128,7 +132,7 @@ def run(src, dst, num_nodes: int, input_nodes, edge_values, leak, bias, drives, 
         res.update(g_edge_values=np.zeros(E), g_leak=np.zeros(N), g_bias=np.zeros(N),
                    g_drives=np.zeros((T, n_in, B)), g_state0=np.zeros((B, N)))
         args_g = [res[k] for k in ("g_edge_values", "g_leak", "g_bias", "g_drives", "g_state0")]
-    rc = _load().ckor_run(N, E, _ptr(src), _ptr(dst), n_in, _ptr(inp), _ptr(v), _ptr(lk), _ptr(bs),
+    rc = _load(precision).ckor_run(N, E, _ptr(src), _ptr(dst), n_in, _ptr(inp), _ptr(v), _ptr(lk), _ptr(bs),
                           _ptr(dr), _ptr(st0), T, B, int(microsteps), _ptr(G), _ptr(out),
                           *[_ptr(a) for a in args_g], int(nthreads))
     if rc:

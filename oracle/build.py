@@ -10,14 +10,17 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "ck_oracle.c")
 LIB = os.path.join(HERE, "libckoracle.so")
+# Same source evaluated in fp32: measures the method's fp32 rounding floor only.
+LIB_F32 = os.path.join(HERE, "libckoracle_f32.so")
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
-           "-fno-fast-math", "-o", LIB, SRC, "-lm"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    for out, extra in ((LIB, []), (LIB_F32, ["-DOR_REAL=float"])):
+        cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+               "-ffp-contract=off"] + extra + ["-o", out, SRC, "-lm"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
     return LIB
 
 

@@ -39,12 +39,17 @@
  * depend on the OpenMP thread count.  Inputs arrive as fp64; the fp32 values
  * the GPU sees convert to fp64 exactly.
  *
+ * The working precision is `real`: double by default.  Built with
+ * -DOR_REAL=float the same code evaluates every step in fp32 (inputs rounded
+ * to fp32); that build only measures the fp32 rounding floor of the method
+ * and is never a parity reference.
+ *
  * The graph builder orders edges by (dst, src, caller index) for the CSR and by
  * (src, dst, caller index) for the transposed CSR; both are total orders, so the
  * arrays are unique and any correct builder must reproduce them bit for bit.
  */
-#include <math.h>
 #include <stdint.h>
+#include <tgmath.h>
 #include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -61,6 +66,11 @@ enum {
   OR_ERR_TOO_LARGE = 5,
   OR_ERR_NOMEM = 7
 };
+
+#ifndef OR_REAL
+#define OR_REAL double
+#endif
+typedef OR_REAL real;
 
 static const int64_t OR_INT32_LIMIT = 2147483647LL; /* sizes must stay below 2^31 */
 
@@ -140,9 +150,9 @@ int ckor_build(int64_t N, int64_t E, const int64_t* src, const int64_t* dst, int
 
 /* sech^2(x) = 1 / cosh^2(x); cosh overflows to +inf for large |x| and the
  * result then correctly becomes 0. */
-static double or_sech2(double x) {
-  double c = cosh(x);
-  return 1.0 / (c * c);
+static real or_sech2(real x) {
+  real c = cosh(x);
+  return (real)1 / (c * c);
 }
 
 /*
@@ -155,16 +165,16 @@ static double or_sech2(double x) {
  * Gradient outputs are overwritten.  nthreads <= 0 uses the OpenMP default.
  */
 int ckor_run(int64_t N, int64_t E, const int64_t* src, const int64_t* dst, int64_t n_in,
-             const int64_t* inputs, const double* v, const double* leak, const double* bias,
-             const double* drives, const double* state0, int64_t T, int64_t B, int64_t M,
-             const double* G, double* out, double* g_v, double* g_leak, double* g_bias,
-             double* g_drives, double* g_state0, int nthreads) {
+             const int64_t* inputs, const double* v_in, const double* leak_in,
+             const double* bias_in, const double* drives_in, const double* state0, int64_t T,
+             int64_t B, int64_t M, const double* G_in, double* out, double* g_v, double* g_leak,
+             double* g_bias, double* g_drives, double* g_state0, int nthreads) {
   int rc = ckor_validate(N, E, src, dst, n_in, inputs);
   if (rc != OR_OK) return rc;
   if (T <= 0 || B <= 0 || M <= 0) return OR_ERR_BAD_SIZE;
-  if (!leak || !bias || !state0 || !out || (E > 0 && !v) || (n_in > 0 && !drives))
+  if (!leak_in || !bias_in || !state0 || !out || (E > 0 && !v_in) || (n_in > 0 && !drives_in))
     return OR_ERR_NULL_ARG;
-  if (G && (!g_leak || !g_bias || !g_state0 || (E > 0 && !g_v) || (n_in > 0 && !g_drives)))
+  if (G_in && (!g_leak || !g_bias || !g_state0 || (E > 0 && !g_v) || (n_in > 0 && !g_drives)))
     return OR_ERR_NULL_ARG;
 #ifdef _OPENMP
   int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
@@ -174,95 +184,114 @@ int ckor_run(int64_t N, int64_t E, const int64_t* src, const int64_t* dst, int64
 #endif
   const int64_t S = T * M;
   const int64_t BN = B * N;
+  const int64_t ND = T * n_in * B;
   int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
-  double* hs = (double*)malloc(sizeof(double) * (size_t)((S + 1) * BN)); /* h^(0..S) */
-  double* as = (double*)malloc(sizeof(double) * (size_t)(S * BN));       /* a^(1..S) */
-  if (!slot || !hs || !as) {
-    free(slot); free(hs); free(as);
+  real* v = (real*)malloc(sizeof(real) * (size_t)(E > 0 ? E : 1));
+  real* leak = (real*)malloc(sizeof(real) * (size_t)N);
+  real* bias = (real*)malloc(sizeof(real) * (size_t)N);
+  real* drives = (real*)malloc(sizeof(real) * (size_t)(ND > 0 ? ND : 1));
+  real* hs = (real*)malloc(sizeof(real) * (size_t)((S + 1) * BN)); /* h^(0..S) */
+  real* as = (real*)malloc(sizeof(real) * (size_t)(S * BN));       /* a^(1..S) */
+  if (!slot || !v || !leak || !bias || !drives || !hs || !as) {
+    free(slot); free(v); free(leak); free(bias); free(drives); free(hs); free(as);
     return OR_ERR_NOMEM;
   }
-  for (int64_t i = 0; i < N; ++i) slot[i] = -1;
+  for (int64_t e = 0; e < E; ++e) v[e] = (real)v_in[e];
+  for (int64_t i = 0; i < N; ++i) {
+    leak[i] = (real)leak_in[i];
+    bias[i] = (real)bias_in[i];
+    slot[i] = -1;
+  }
+  for (int64_t x = 0; x < ND; ++x) drives[x] = (real)drives_in[x];
   for (int64_t k = 0; k < n_in; ++k) slot[inputs[k]] = k;
-  memcpy(hs, state0, sizeof(double) * (size_t)BN);
+  for (int64_t x = 0; x < BN; ++x) hs[x] = (real)state0[x];
 
   /* ---- forward ---- */
   for (int64_t s = 1; s <= S; ++s) {
     const int64_t t = (s - 1) / M;
-    const double* hp = hs + (s - 1) * BN;
-    double* hn = hs + s * BN;
-    double* a = as + (s - 1) * BN;
+    const real* hp = hs + (s - 1) * BN;
+    real* hn = hs + s * BN;
+    real* a = as + (s - 1) * BN;
 #pragma omp parallel for num_threads(nt) schedule(static)
     for (int64_t b = 0; b < B; ++b) {
-      double* acc = a + b * N;
-      const double* hb = hp + b * N;
-      for (int64_t i = 0; i < N; ++i) acc[i] = 0.0;
+      real* acc = a + b * N;
+      const real* hb = hp + b * N;
+      for (int64_t i = 0; i < N; ++i) acc[i] = 0;
       for (int64_t e = 0; e < E; ++e) acc[dst[e]] += v[e] * hb[src[e]];
       for (int64_t i = 0; i < N; ++i) {
-        double drive = slot[i] >= 0 ? drives[(t * n_in + slot[i]) * B + b] : 0.0;
-        double x = acc[i] + drive + bias[i];
+        real drive = slot[i] >= 0 ? drives[(t * n_in + slot[i]) * B + b] : (real)0;
+        real x = acc[i] + drive + bias[i];
         acc[i] = x;
-        hn[b * N + i] = (1.0 - leak[i]) * hb[i] + leak[i] * tanh(x);
+        hn[b * N + i] = ((real)1 - leak[i]) * hb[i] + leak[i] * tanh(x);
       }
     }
-    if (s % M == 0) memcpy(out + t * BN, hn, sizeof(double) * (size_t)BN);
+    if (s % M == 0)
+      for (int64_t x = 0; x < BN; ++x) out[t * BN + x] = (double)hn[x];
   }
 
-  if (G) {
+  if (G_in) {
     /* ---- backward ---- */
-    double* g = (double*)calloc((size_t)BN, sizeof(double));
-    double* gn = (double*)malloc(sizeof(double) * (size_t)BN);
-    double* ga = (double*)malloc(sizeof(double) * (size_t)BN);
-    if (!g || !gn || !ga) {
-      free(g); free(gn); free(ga); free(slot); free(hs); free(as);
+    real* g = (real*)calloc((size_t)BN, sizeof(real));
+    real* gn = (real*)malloc(sizeof(real) * (size_t)BN);
+    real* ga = (real*)malloc(sizeof(real) * (size_t)BN);
+    real* gv = (real*)calloc((size_t)(E > 0 ? E : 1), sizeof(real));
+    real* gl_ = (real*)calloc((size_t)N, sizeof(real));
+    real* gb_ = (real*)calloc((size_t)N, sizeof(real));
+    real* gd = (real*)calloc((size_t)(ND > 0 ? ND : 1), sizeof(real));
+    if (!g || !gn || !ga || !gv || !gl_ || !gb_ || !gd) {
+      free(g); free(gn); free(ga); free(gv); free(gl_); free(gb_); free(gd);
+      free(slot); free(v); free(leak); free(bias); free(drives); free(hs); free(as);
       return OR_ERR_NOMEM;
     }
-    for (int64_t e = 0; e < E; ++e) g_v[e] = 0.0;
-    for (int64_t i = 0; i < N; ++i) g_leak[i] = g_bias[i] = 0.0;
-    for (int64_t x = 0; x < T * n_in * B; ++x) g_drives[x] = 0.0;
-
     for (int64_t s = S; s >= 1; --s) {
       const int64_t t = (s - 1) / M;
-      const double* q = hs + (s - 1) * BN;
-      const double* a = as + (s - 1) * BN;
+      const real* q = hs + (s - 1) * BN;
+      const real* a = as + (s - 1) * BN;
       if (s % M == 0)
-        for (int64_t x = 0; x < BN; ++x) g[x] += G[t * BN + x];
+        for (int64_t x = 0; x < BN; ++x) g[x] += (real)G_in[t * BN + x];
 #pragma omp parallel for num_threads(nt) schedule(static)
       for (int64_t i = 0; i < N; ++i) {
-        double gl = 0.0, gb = 0.0;
+        real gl = 0, gb = 0;
         for (int64_t b = 0; b < B; ++b) {
           const int64_t x = b * N + i;
-          const double p = tanh(a[x]);
+          const real p = tanh(a[x]);
           gl += g[x] * (p - q[x]);
           ga[x] = g[x] * leak[i] * or_sech2(a[x]);
           gb += ga[x];
         }
-        g_leak[i] += gl;
-        g_bias[i] += gb;
+        gl_[i] += gl;
+        gb_[i] += gb;
       }
 #pragma omp parallel for num_threads(nt) schedule(static)
       for (int64_t k = 0; k < n_in; ++k)
-        for (int64_t b = 0; b < B; ++b) g_drives[(t * n_in + k) * B + b] += ga[b * N + inputs[k]];
+        for (int64_t b = 0; b < B; ++b) gd[(t * n_in + k) * B + b] += ga[b * N + inputs[k]];
 #pragma omp parallel for num_threads(nt) schedule(static)
       for (int64_t e = 0; e < E; ++e) {
-        double d = 0.0;
+        real d = 0;
         for (int64_t b = 0; b < B; ++b) d += ga[b * N + dst[e]] * q[b * N + src[e]];
-        g_v[e] += d;
+        gv[e] += d;
       }
 #pragma omp parallel for num_threads(nt) schedule(static)
       for (int64_t b = 0; b < B; ++b) {
-        double* gnb = gn + b * N;
-        const double* gb_ = g + b * N;
-        const double* gab = ga + b * N;
-        for (int64_t j = 0; j < N; ++j) gnb[j] = (1.0 - leak[j]) * gb_[j];
+        real* gnb = gn + b * N;
+        const real* gb_row = g + b * N;
+        const real* gab = ga + b * N;
+        for (int64_t j = 0; j < N; ++j) gnb[j] = ((real)1 - leak[j]) * gb_row[j];
         for (int64_t e = 0; e < E; ++e) gnb[src[e]] += v[e] * gab[dst[e]];
       }
-      double* tmp = g;
+      real* tmp = g;
       g = gn;
       gn = tmp;
     }
-    memcpy(g_state0, g, sizeof(double) * (size_t)BN);
-    free(g); free(gn); free(ga);
+    for (int64_t e = 0; e < E; ++e) g_v[e] = (double)gv[e];
+    for (int64_t i = 0; i < N; ++i) {
+      g_leak[i] = (double)gl_[i];
+      g_bias[i] = (double)gb_[i];
+    }
+    for (int64_t x = 0; x < ND; ++x) g_drives[x] = (double)gd[x];
+    for (int64_t x = 0; x < BN; ++x) g_state0[x] = (double)g[x];
+    free(g); free(gn); free(ga); free(gv); free(gl_); free(gb_); free(gd);
   }
-  free(slot); free(hs); free(as);
+  free(slot); free(v); free(leak); free(bias); free(drives); free(hs); free(as);
   return OR_OK;
 }

@@ -1,0 +1,500 @@
+// graph_build.hip -- ck_graph_create and friends: validation, CSR / transposed
+// CSR construction with a stable LSD radix sort, input-slot map and the
+// degree-balanced, XCD-aware row schedules.
+//
+// The graph is given as caller-ordered src/dst lists (connectome-kernels
+// README, "Use"); parameters stay in that order and the internal permutation is
+// invisible.  The backward's state gradient needs the transposed CSR
+// ("Design notes").  Edge order inside a row is (other endpoint, caller index):
+// a total order, so every array produced here is unique.
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "ck_internal.h"
+
+namespace ckhip {
+
+static thread_local char g_last_error[1024] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+ck_status check_graph(const ck_graph* g) {
+  if (g == nullptr || g->magic != kGraphMagic) {
+    set_error("invalid or destroyed graph handle");
+    return CK_ERR_BAD_HANDLE;
+  }
+  return CK_OK;
+}
+
+namespace {
+
+constexpr int64_t kInt32Limit = 2147483647LL;
+
+// ---------------------------------------------------------------- validation
+// flags bit 0: an index outside [0, N); bit 1: a duplicate input node.
+__global__ void validate_edges(const int64_t* __restrict__ src, const int64_t* __restrict__ dst,
+                               int64_t E, int64_t N, unsigned* flags) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  int64_t s = src[e], d = dst[e];
+  if (s < 0 || s >= N || d < 0 || d >= N) atomicOr(flags, 1u);
+}
+
+__global__ void validate_inputs(const int64_t* __restrict__ inputs, int64_t n_in, int64_t N,
+                                int32_t* __restrict__ seen, unsigned* flags) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= n_in) return;
+  int64_t i = inputs[k];
+  if (i < 0 || i >= N) {
+    atomicOr(flags, 1u);
+    return;
+  }
+  if (atomicAdd(&seen[i], 1) != 0) atomicOr(flags, 2u);
+}
+
+__global__ void fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void set_input_slots(const int64_t* __restrict__ inputs, int64_t n_in,
+                                int32_t* __restrict__ slot) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < n_in) slot[inputs[k]] = (int32_t)k;
+}
+
+// key = major * N + minor, value = caller index (ascending, so ties keep it)
+__global__ void make_keys(const int64_t* __restrict__ major, const int64_t* __restrict__ minor,
+                          int64_t E, int64_t N, uint64_t* __restrict__ keys,
+                          int32_t* __restrict__ vals) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  keys[e] = (uint64_t)major[e] * (uint64_t)N + (uint64_t)minor[e];
+  vals[e] = (int32_t)e;
+}
+
+// ---------------------------------------------------------------- radix sort
+// Stable LSD radix sort, 4-bit digits, tiles of 2048 keys (256 threads x 8).
+constexpr int kRsThreads = 256;
+constexpr int kRsItems = 8;
+constexpr int kRsTile = kRsThreads * kRsItems;
+constexpr int kRsRadix = 16;
+
+__global__ __launch_bounds__(kRsThreads) void rs_histogram(const uint64_t* __restrict__ keys,
+                                                           int64_t n, int shift,
+                                                           uint32_t* __restrict__ hist,
+                                                           int64_t nblocks) {
+  __shared__ uint32_t cnt[kRsRadix];
+  if (threadIdx.x < kRsRadix) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kRsTile;
+  for (int i = threadIdx.x; i < kRsTile; i += kRsThreads) {
+    int64_t k = base + i;
+    if (k < n) atomicAdd(&cnt[(keys[k] >> shift) & (kRsRadix - 1)], 1u);
+  }
+  __syncthreads();
+  if (threadIdx.x < kRsRadix) hist[threadIdx.x * nblocks + blockIdx.x] = cnt[threadIdx.x];
+}
+
+// Exclusive scan of m uint32 values in place; one workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void exclusive_scan_u32(uint32_t* __restrict__ data, int64_t m) {
+  __shared__ uint32_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t chunk = (m + 1023) / 1024;
+  const int64_t b = std::min<int64_t>(m, (int64_t)t * chunk);
+  const int64_t e = std::min<int64_t>(m, b + chunk);
+  uint32_t s = 0;
+  for (int64_t i = b; i < e; ++i) s += data[i];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    uint32_t add = t >= off ? part[t - off] : 0u;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  uint32_t run = t ? part[t - 1] : 0u;
+  for (int64_t i = b; i < e; ++i) {
+    uint32_t x = data[i];
+    data[i] = run;
+    run += x;
+  }
+}
+
+__global__ __launch_bounds__(kRsThreads) void rs_scatter(
+    const uint64_t* __restrict__ kin, const int32_t* __restrict__ vin, uint64_t* __restrict__ kout,
+    int32_t* __restrict__ vout, int64_t n, int shift, const uint32_t* __restrict__ goff,
+    int64_t nblocks) {
+  // pos[d][t]: elements of this tile with digit < d, plus those with digit d in
+  // threads < t.  Thread t owns the items t*8 .. t*8+7 of the tile, in order.
+  __shared__ uint32_t pos[kRsRadix][kRsThreads + 1];
+  __shared__ uint32_t sums[kRsThreads];
+  __shared__ uint32_t dstart[kRsRadix];
+  const int t = threadIdx.x;
+  for (int d = 0; d < kRsRadix; ++d) pos[d][t] = 0;
+  const int64_t base = (int64_t)blockIdx.x * kRsTile + (int64_t)t * kRsItems;
+  uint64_t key[kRsItems];
+  int32_t val[kRsItems];
+#pragma unroll
+  for (int i = 0; i < kRsItems; ++i) {
+    int64_t idx = base + i;
+    if (idx < n) {
+      key[i] = kin[idx];
+      val[i] = vin[idx];
+      pos[(key[i] >> shift) & (kRsRadix - 1)][t] += 1;
+    }
+  }
+  __syncthreads();
+  // exclusive scan over the 16 x 256 counts in digit-major order:
+  // thread u scans the 16 consecutive entries [16u, 16u + 16)
+  const int d0 = t / 16, t0 = (t % 16) * 16;
+  uint32_t local = 0;
+  for (int j = 0; j < 16; ++j) local += pos[d0][t0 + j];
+  sums[t] = local;
+  __syncthreads();
+  for (int off = 1; off < kRsThreads; off <<= 1) {
+    uint32_t add = t >= off ? sums[t - off] : 0u;
+    __syncthreads();
+    sums[t] += add;
+    __syncthreads();
+  }
+  uint32_t run = t ? sums[t - 1] : 0u;
+  for (int j = 0; j < 16; ++j) {
+    uint32_t c = pos[d0][t0 + j];
+    pos[d0][t0 + j] = run;
+    run += c;
+  }
+  __syncthreads();
+  if (t < kRsRadix) dstart[t] = pos[t][0];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRsItems; ++i) {
+    int64_t idx = base + i;
+    if (idx < n) {
+      int d = (int)((key[i] >> shift) & (kRsRadix - 1));
+      uint32_t rank = pos[d][t] - dstart[d];
+      pos[d][t] += 1;
+      int64_t o = (int64_t)goff[d * nblocks + blockIdx.x] + rank;
+      kout[o] = key[i];
+      vout[o] = val[i];
+    }
+  }
+}
+
+// row_ptr[i] = number of keys below i * N (keys sorted ascending), i in [0, N]
+__global__ void row_starts(const uint64_t* __restrict__ keys, int64_t E, int64_t N,
+                           int32_t* __restrict__ ptr) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i > N) return;
+  const uint64_t target = (uint64_t)i * (uint64_t)N;
+  int64_t lo = 0, hi = E;
+  while (lo < hi) {
+    int64_t mid = (lo + hi) >> 1;
+    if (keys[mid] < target) lo = mid + 1;
+    else hi = mid;
+  }
+  ptr[i] = (int32_t)lo;
+}
+
+__global__ void split_keys(const uint64_t* __restrict__ keys, const int32_t* __restrict__ vals,
+                           int64_t E, int64_t N, int32_t* __restrict__ minor,
+                           int32_t* __restrict__ perm) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= E) return;
+  minor[k] = (int32_t)(keys[k] % (uint64_t)N);
+  perm[k] = vals[k];
+}
+
+inline unsigned grid_for(int64_t n, int threads) {
+  return (unsigned)std::max<int64_t>(1, (n + threads - 1) / threads);
+}
+
+// Sort the E edges by key major*N + minor (stable: ties keep caller order) and
+// write ptr[N+1], idx[E] = minor, prm[E] = caller index.
+ck_status build_compressed(const int64_t* major, const int64_t* minor, int64_t E, int64_t N,
+                           int32_t* ptr, int32_t* idx, int32_t* prm, hipStream_t st) {
+  if (E == 0) {
+    fill_i32<<<grid_for(N + 1, 256), 256, 0, st>>>(ptr, N + 1, 0);
+    CK_HIP_TRY(hipGetLastError());
+    return CK_OK;
+  }
+  const int64_t nblocks = (E + kRsTile - 1) / kRsTile;
+  uint64_t *k0 = nullptr, *k1 = nullptr;
+  int32_t *v0 = nullptr, *v1 = nullptr;
+  uint32_t* hist = nullptr;
+  auto cleanup = [&]() {
+    (void)hipFree(k0); (void)hipFree(k1); (void)hipFree(v0); (void)hipFree(v1);
+    (void)hipFree(hist);
+  };
+  if (hipMalloc(&k0, E * 8) != hipSuccess || hipMalloc(&k1, E * 8) != hipSuccess ||
+      hipMalloc(&v0, E * 4) != hipSuccess || hipMalloc(&v1, E * 4) != hipSuccess ||
+      hipMalloc(&hist, nblocks * kRsRadix * 4) != hipSuccess) {
+    cleanup();
+    (void)hipGetLastError();
+    set_error("device allocation of %lld bytes of sort scratch failed", (long long)(E * 24));
+    return CK_ERR_NOMEM;
+  }
+  make_keys<<<grid_for(E, 256), 256, 0, st>>>(major, minor, E, N, k0, v0);
+  const uint64_t maxkey = (uint64_t)N * (uint64_t)N - 1;
+  int bits = 0;
+  while (bits < 64 && (maxkey >> bits) != 0) ++bits;
+  for (int shift = 0; shift < bits; shift += 4) {
+    rs_histogram<<<(unsigned)nblocks, kRsThreads, 0, st>>>(k0, E, shift, hist, nblocks);
+    exclusive_scan_u32<<<1, 1024, 0, st>>>(hist, nblocks * kRsRadix);
+    rs_scatter<<<(unsigned)nblocks, kRsThreads, 0, st>>>(k0, v0, k1, v1, E, shift, hist, nblocks);
+    std::swap(k0, k1);
+    std::swap(v0, v1);
+  }
+  row_starts<<<grid_for(N + 1, 256), 256, 0, st>>>(k0, E, N, ptr);
+  split_keys<<<grid_for(E, 256), 256, 0, st>>>(k0, v0, E, N, idx, prm);
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess) err = hipStreamSynchronize(st);
+  cleanup();
+  if (err != hipSuccess) {
+    set_error("graph sort failed: %s", hipGetErrorString(err));
+    return CK_ERR_HIP;
+  }
+  return CK_OK;
+}
+
+// Degree-balanced, XCD-aware schedule (host side, from the row pointers).
+// Rows are cut into kXcds contiguous ranges of about equal cost (edges plus a
+// per-row constant); workgroup w runs on XCD w % kXcds and takes that XCD's
+// (w / kXcds)-th item.  Inside a range, rows go heaviest first: long rows one
+// per workgroup, the rest kWaves per workgroup.
+ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, Schedule* out) {
+  constexpr int64_t kRowCost = 16;
+  std::vector<int64_t> deg(N);
+  int64_t total = 0;
+  for (int64_t i = 0; i < N; ++i) {
+    deg[i] = ptr[i + 1] - ptr[i];
+    total += deg[i] + kRowCost;
+  }
+  std::vector<int64_t> cut(kXcds + 1, N);
+  cut[0] = 0;
+  {
+    int64_t acc = 0;
+    int x = 1;
+    for (int64_t i = 0; i < N && x < kXcds; ++i) {
+      acc += deg[i] + kRowCost;
+      while (x < kXcds && acc * kXcds >= total * x) cut[x++] = i + 1;
+    }
+  }
+  std::vector<int32_t> rows;
+  rows.reserve(N);
+  std::vector<std::vector<int2>> lists(kXcds);
+  for (int x = 0; x < kXcds; ++x) {
+    std::vector<int32_t> r;
+    for (int64_t i = cut[x]; i < cut[x + 1]; ++i) r.push_back((int32_t)i);
+    std::stable_sort(r.begin(), r.end(), [&](int32_t a, int32_t b) { return deg[a] > deg[b]; });
+    size_t j = 0;
+    for (; j < r.size() && deg[r[j]] > kLongRow; ++j) {
+      lists[x].push_back(make_int2((int)rows.size(), -1));
+      rows.push_back(r[j]);
+    }
+    while (j < r.size()) {
+      int cnt = (int)std::min<size_t>(kWaves, r.size() - j);
+      lists[x].push_back(make_int2((int)rows.size(), cnt));
+      for (int q = 0; q < cnt; ++q) rows.push_back(r[j + q]);
+      j += cnt;
+    }
+  }
+  size_t nmax = 1;
+  for (auto& l : lists) nmax = std::max(nmax, l.size());
+  std::vector<int2> items(nmax * kXcds, make_int2(0, 0));
+  for (size_t r = 0; r < nmax; ++r)
+    for (int x = 0; x < kXcds; ++x)
+      if (r < lists[x].size()) items[r * kXcds + x] = lists[x][r];
+  out->num_items = (int)items.size();
+  CK_HIP_TRY(hipMalloc(&out->items, items.size() * sizeof(int2)));
+  CK_HIP_TRY(hipMalloc(&out->rows, std::max<size_t>(1, rows.size()) * sizeof(int32_t)));
+  CK_HIP_TRY(hipMemcpy(out->items, items.data(), items.size() * sizeof(int2), hipMemcpyHostToDevice));
+  if (!rows.empty())
+    CK_HIP_TRY(hipMemcpy(out->rows, rows.data(), rows.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  return CK_OK;
+}
+
+void free_graph_arrays(ck_graph* g) {
+  int32_t* arrs[] = {g->row_ptr, g->col_idx, g->perm, g->t_row_ptr, g->t_col_idx, g->t_perm,
+                     g->input_slot, g->fwd.rows, g->bwd.rows};
+  for (int32_t* p : arrs) (void)hipFree(p);
+  (void)hipFree(g->fwd.items);
+  (void)hipFree(g->bwd.items);
+}
+
+}  // namespace
+}  // namespace ckhip
+
+using namespace ckhip;
+
+extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int64_t num_edges,
+                                     int64_t num_nodes, const int64_t* input_nodes,
+                                     int64_t num_inputs, hipStream_t stream, ck_graph_t* out) {
+  clear_error();
+  if (out == nullptr) {
+    set_error("out handle pointer is NULL");
+    return CK_ERR_NULL_ARG;
+  }
+  *out = nullptr;
+  const int64_t N = num_nodes, E = num_edges, n_in = num_inputs;
+  if (N <= 0 || E < 0 || n_in < 0) {
+    set_error("bad sizes: num_nodes=%lld num_edges=%lld num_inputs=%lld", (long long)N,
+              (long long)E, (long long)n_in);
+    return CK_ERR_BAD_SIZE;
+  }
+  if (N >= kInt32Limit || E >= kInt32Limit) {
+    set_error("num_nodes and num_edges must be below 2^31");
+    return CK_ERR_TOO_LARGE;
+  }
+  if ((E > 0 && (src == nullptr || dst == nullptr)) || (n_in > 0 && input_nodes == nullptr)) {
+    set_error("NULL src/dst/input_nodes for a non-empty list");
+    return CK_ERR_NULL_ARG;
+  }
+  ck_graph* g = (ck_graph*)calloc(1, sizeof(ck_graph));
+  if (!g) {
+    set_error("host allocation failed");
+    return CK_ERR_NOMEM;
+  }
+  g->N = N;
+  g->E = E;
+  g->n_in = n_in;
+  (void)hipGetDevice(&g->device);
+  unsigned* flags = nullptr;
+  int32_t* seen = nullptr;
+  ck_status rc = CK_OK;
+  auto fail = [&](ck_status s) {
+    (void)hipFree(flags);
+    (void)hipFree(seen);
+    free_graph_arrays(g);
+    free(g);
+    return s;
+  };
+#define CK_GB_TRY(expr)                                                                     \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) {                                                                 \
+      set_error("%s failed: %s", #expr, hipGetErrorString(e_));                             \
+      return fail(e_ == hipErrorOutOfMemory ? CK_ERR_NOMEM : CK_ERR_HIP);                   \
+    }                                                                                       \
+  } while (0)
+  CK_GB_TRY(hipMalloc(&flags, sizeof(unsigned)));
+  CK_GB_TRY(hipMalloc(&seen, N * sizeof(int32_t)));
+  fill_i32<<<grid_for(1, 64), 64, 0, stream>>>((int32_t*)flags, 1, 0);
+  fill_i32<<<grid_for(N, 256), 256, 0, stream>>>(seen, N, 0);
+  if (E > 0) validate_edges<<<grid_for(E, 256), 256, 0, stream>>>(src, dst, E, N, flags);
+  if (n_in > 0)
+    validate_inputs<<<grid_for(n_in, 256), 256, 0, stream>>>(input_nodes, n_in, N, seen, flags);
+  CK_GB_TRY(hipGetLastError());
+  unsigned hflags = 0;
+  CK_GB_TRY(hipMemcpyAsync(&hflags, flags, sizeof(unsigned), hipMemcpyDeviceToHost, stream));
+  CK_GB_TRY(hipStreamSynchronize(stream));
+  if (hflags & 1u) {
+    set_error("an edge endpoint or input node lies outside [0, %lld)", (long long)N);
+    return fail(CK_ERR_INDEX_RANGE);
+  }
+  if (hflags & 2u) {
+    set_error("input_nodes lists a node more than once");
+    return fail(CK_ERR_DUP_INPUT);
+  }
+  const size_t eb = std::max<int64_t>(E, 1) * sizeof(int32_t);
+  const size_t nb = (N + 1) * sizeof(int32_t);
+  CK_GB_TRY(hipMalloc(&g->row_ptr, nb));
+  CK_GB_TRY(hipMalloc(&g->t_row_ptr, nb));
+  CK_GB_TRY(hipMalloc(&g->col_idx, eb));
+  CK_GB_TRY(hipMalloc(&g->perm, eb));
+  CK_GB_TRY(hipMalloc(&g->t_col_idx, eb));
+  CK_GB_TRY(hipMalloc(&g->t_perm, eb));
+  CK_GB_TRY(hipMalloc(&g->input_slot, N * sizeof(int32_t)));
+  rc = build_compressed(dst, src, E, N, g->row_ptr, g->col_idx, g->perm, stream);
+  if (rc != CK_OK) return fail(rc);
+  rc = build_compressed(src, dst, E, N, g->t_row_ptr, g->t_col_idx, g->t_perm, stream);
+  if (rc != CK_OK) return fail(rc);
+  fill_i32<<<grid_for(N, 256), 256, 0, stream>>>(g->input_slot, N, -1);
+  if (n_in > 0) set_input_slots<<<grid_for(n_in, 256), 256, 0, stream>>>(input_nodes, n_in, g->input_slot);
+  CK_GB_TRY(hipGetLastError());
+  std::vector<int32_t> hptr(N + 1), htptr(N + 1);
+  CK_GB_TRY(hipMemcpyAsync(hptr.data(), g->row_ptr, nb, hipMemcpyDeviceToHost, stream));
+  CK_GB_TRY(hipMemcpyAsync(htptr.data(), g->t_row_ptr, nb, hipMemcpyDeviceToHost, stream));
+  CK_GB_TRY(hipStreamSynchronize(stream));
+  rc = build_schedule(hptr, N, &g->fwd);
+  if (rc != CK_OK) return fail(rc);
+  rc = build_schedule(htptr, N, &g->bwd);
+  if (rc != CK_OK) return fail(rc);
+  (void)hipFree(flags);
+  (void)hipFree(seen);
+  g->magic = kGraphMagic;
+  *out = g;
+  return CK_OK;
+#undef CK_GB_TRY
+}
+
+extern "C" ck_status ck_graph_destroy(ck_graph_t g) {
+  clear_error();
+  if (g == nullptr) return CK_OK;
+  ck_status rc = check_graph(g);
+  if (rc != CK_OK) return rc;
+  (void)hipDeviceSynchronize();
+  free_graph_arrays(g);
+  g->magic = 0;
+  free(g);
+  return CK_OK;
+}
+
+extern "C" ck_status ck_graph_sizes(ck_graph_t g, int64_t* num_nodes, int64_t* num_edges,
+                                    int64_t* num_inputs) {
+  clear_error();
+  ck_status rc = check_graph(g);
+  if (rc != CK_OK) return rc;
+  if (num_nodes) *num_nodes = g->N;
+  if (num_edges) *num_edges = g->E;
+  if (num_inputs) *num_inputs = g->n_in;
+  return CK_OK;
+}
+
+extern "C" ck_status ck_graph_export(ck_graph_t g, int32_t* row_ptr, int32_t* col_idx,
+                                     int32_t* perm, int32_t* t_row_ptr, int32_t* t_col_idx,
+                                     int32_t* t_perm, int32_t* input_slot, hipStream_t stream) {
+  clear_error();
+  ck_status rc = check_graph(g);
+  if (rc != CK_OK) return rc;
+  const size_t nb = (g->N + 1) * sizeof(int32_t), eb = g->E * sizeof(int32_t);
+  struct {
+    int32_t* dst;
+    const int32_t* src;
+    size_t bytes;
+  } copies[] = {{row_ptr, g->row_ptr, nb},     {col_idx, g->col_idx, eb},
+                {perm, g->perm, eb},           {t_row_ptr, g->t_row_ptr, nb},
+                {t_col_idx, g->t_col_idx, eb}, {t_perm, g->t_perm, eb},
+                {input_slot, g->input_slot, g->N * sizeof(int32_t)}};
+  for (auto& c : copies)
+    if (c.dst != nullptr && c.bytes > 0)
+      CK_HIP_TRY(hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, stream));
+  return CK_OK;
+}
+
+extern "C" const char* ck_status_string(ck_status s) {
+  switch (s) {
+    case CK_OK: return "CK_OK";
+    case CK_ERR_NULL_ARG: return "CK_ERR_NULL_ARG";
+    case CK_ERR_BAD_SIZE: return "CK_ERR_BAD_SIZE";
+    case CK_ERR_INDEX_RANGE: return "CK_ERR_INDEX_RANGE";
+    case CK_ERR_DUP_INPUT: return "CK_ERR_DUP_INPUT";
+    case CK_ERR_TOO_LARGE: return "CK_ERR_TOO_LARGE";
+    case CK_ERR_WORKSPACE: return "CK_ERR_WORKSPACE";
+    case CK_ERR_NOMEM: return "CK_ERR_NOMEM";
+    case CK_ERR_HIP: return "CK_ERR_HIP";
+    case CK_ERR_BAD_HANDLE: return "CK_ERR_BAD_HANDLE";
+  }
+  return "CK_ERR_UNKNOWN";
+}
+
+extern "C" const char* ck_last_error(void) { return ckhip::g_last_error; }

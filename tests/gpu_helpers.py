@@ -1,0 +1,133 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the Python
+binding (which calls the C ABI), run the oracle on the same seeded inputs, and
+compare element by element with the stated tolerances."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_graph_recurrent_amd as sgr
+
+# Tolerances, per element:
+#   |gpu - oracle| <= atol + rtol * max(|oracle|, NEAR_ZERO * rms(oracle tensor))
+# rtol/atol are the stated ones (states 1e-5 / 1e-6, gradients 1e-4 / 1e-6).
+# An element counts as "near zero" when it is below 10% of its tensor's RMS:
+# a gradient entry is a sum of thousands of products (over batch columns and
+# microsteps) whose fp32 rounding error scales with the size of those products,
+# not with the (possibly cancelled) result.  The same definition evaluated
+# entirely in fp32 (the fp32 build of the oracle) misses the bare per-element
+# bound on ~0.2% of edge-gradient entries at the FlyGPT shape; with the floor
+# it passes, and the GPU must additionally be no less accurate than that fp32
+# evaluation (compare_floor).
+STATE_RTOL, STATE_ATOL = 1e-5, 1e-6     # outputs (states)
+GRAD_RTOL, GRAD_ATOL = 1e-4, 1e-6       # the five gradients
+NEAR_ZERO = 0.1
+GRAD_KEYS = ("g_edge_values", "g_leak", "g_bias", "g_drives", "g_state0")
+
+
+def log(msg: str):
+    print(msg, flush=True)
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def make_graph(w) -> sgr.SparseGraph:
+    return sgr.SparseGraph(to_dev(w.src), to_dev(w.dst), w.num_nodes, to_dev(w.input_nodes))
+
+
+def run_gpu(w, G=None, graph=None, backward=True):
+    """Forward (+ backward with grad_out G, default w.grad_out) on the GPU."""
+    g = make_graph(w) if graph is None else graph
+    ev, lk, bs = to_dev(w.edge_values), to_dev(w.leak), to_dev(w.bias)
+    dr, st = to_dev(w.drives), to_dev(w.state0)
+    out, saved, ws = sgr.recurrence_forward(g, ev, lk, bs, dr, st, w.microsteps)
+    res = {"out": out}
+    if backward:
+        Gd = to_dev(w.grad_out if G is None else G, torch.float32)
+        res.update(sgr.recurrence_backward(g, ev, lk, st, w.microsteps, saved, Gd, workspace=ws))
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def run_oracle(w, G=None, cols=None, backward=True, nthreads=0, precision="f64"):
+    """Oracle on all batch columns, or only on `cols` (columns are independent)."""
+    dr, st = w.drives, w.state0
+    Gx = w.grad_out if G is None else G
+    if cols is not None:
+        cols = np.asarray(cols)
+        dr, st, Gx = dr[:, :, cols], st[cols], Gx[:, cols]
+    return oracle.run(w.src, w.dst, w.num_nodes, w.input_nodes, w.edge_values, w.leak, w.bias,
+                      dr, st, w.microsteps, grad_out=Gx if backward else None, nthreads=nthreads,
+                      precision=precision)
+
+
+def compare(name, got, want, rtol, atol):
+    """Assert the per-element bound; log max abs/rel error and failing count."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    if got.size == 0:
+        return
+    err = np.abs(got - want)
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    bound = atol + rtol * np.maximum(np.abs(want), NEAR_ZERO * rms)
+    bare = int(np.sum(err > atol + rtol * np.abs(want)))
+    bad = err > bound
+    nrm = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)
+    log(f"  {name:14s} n={got.size:>10d} rms={rms:.3e} max_abs={err.max():.3e} "
+        f"max_abs/rms={err.max() / max(rms, 1e-300):.2e} norm_rel={nrm:.3e} "
+        f"outside_bare_bound={bare} fail={int(bad.sum())}")
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{name}: {int(bad.sum())} of {got.size} elements outside "
+                             f"atol={atol} rtol={rtol}; worst at {i}: got {got[i]!r} want {want[i]!r}")
+
+
+def compare_all(gpu, ref, cols=None, backward=True):
+    out = gpu["out"] if cols is None else gpu["out"][:, cols]
+    compare("out", out, ref["out"], STATE_RTOL, STATE_ATOL)
+    if not backward:
+        return
+    for k in GRAD_KEYS:
+        g = gpu[k]
+        if cols is not None and k == "g_drives":
+            g = g[:, :, cols]
+        if cols is not None and k == "g_state0":
+            g = g[cols]
+        compare(k, g, ref[k], GRAD_RTOL, GRAD_ATOL)
+
+
+def compare_floor(gpu, ref64, ref32, cols=None, factor=2.0):
+    """The GPU's worst error per tensor is at most `factor` times the worst
+    error of the same definition evaluated in fp32 (oracle fp32 build)."""
+    for k in ("out",) + GRAD_KEYS:
+        if k not in ref64:
+            continue
+        g = gpu[k]
+        if cols is not None:
+            if k == "out":
+                g = g[:, cols]
+            elif k == "g_drives":
+                g = g[:, :, cols]
+            elif k == "g_state0":
+                g = g[cols]
+        if g.size == 0:
+            continue
+        e_gpu = float(np.max(np.abs(g - ref64[k])))
+        e_f32 = float(np.max(np.abs(ref32[k] - ref64[k])))
+        log(f"  floor {k:14s} gpu_max_abs={e_gpu:.3e} fp32_eval_max_abs={e_f32:.3e}")
+        assert e_gpu <= factor * e_f32 + 1e-7, (k, e_gpu, e_f32)
+
+
+def column_masked_grad(w, cols):
+    """grad_out that is zero outside batch columns `cols` (the gradient then
+    only depends on those columns, so a column-sampled oracle is exact)."""
+    G = np.zeros_like(w.grad_out)
+    G[:, cols] = w.grad_out[:, cols]
+    return G

@@ -1,0 +1,257 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Graph arrays must be bit-exact; outputs must match to rtol 1e-5 (atol 1e-6)
+and all five gradients to rtol 1e-4 (atol 1e-6), per element.  Large
+workloads run the GPU at the full launch configuration and compare against the
+oracle on sampled batch columns: columns are independent through the whole
+recurrence, so with grad_out zero outside those columns the column-sampled
+oracle gives every gradient exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_graph_recurrent_amd as sgr
+import synthetic
+from gpu_helpers import (column_masked_grad, compare_all, compare_floor, log, make_graph, run_gpu,
+                         run_oracle, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+GRAPH_KEYS = ("row_ptr", "col_idx", "perm", "t_row_ptr", "t_col_idx", "t_perm", "input_slot")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sgr.lib()  # raises if the HIP library is missing: no fallback
+
+
+def _check_graph(w):
+    g = make_graph(w)
+    got = {k: v.cpu().numpy() for k, v in g.export().items()}
+    ref = oracle.build_graph(w.src, w.dst, w.num_nodes, w.input_nodes)
+    for k in GRAPH_KEYS:
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+    assert g.sizes() == (w.num_nodes, w.num_edges, w.n_in)
+    g.destroy()
+
+
+# ---------------------------------------------------------------- graph build
+@pytest.mark.parametrize("name", ["tiny", "flygpt", "edge_cases", "mid_scale"])
+def test_graph_build_bit_exact(name):
+    log(f"graph build: {name}")
+    _check_graph(synthetic.make(name, T=1, B=1))
+
+
+def _adversarial(kind, rng):
+    if kind == "parallel_edges":
+        w = synthetic.random_graph(rng, 40, 6000, 3, 1, 1, 1)
+    elif kind == "hub_rows":
+        w = synthetic.random_graph(rng, 500, 3000, 5, 1, 1, 1)
+        hub_in = rng.integers(0, 500, 20000)
+        hub_out = rng.integers(0, 500, 15000)
+        w.src = np.concatenate([w.src, hub_in, np.full(15000, 7)])
+        w.dst = np.concatenate([w.dst, np.full(20000, 3), hub_out])
+        p = rng.permutation(w.src.size)
+        w.src, w.dst = w.src[p], w.dst[p]
+        w.edge_values = np.zeros(w.src.size, np.float32)
+    elif kind == "empty_rows":
+        w = synthetic.random_graph(rng, 1000, 500, 4, 1, 1, 1)
+    elif kind == "no_edges":
+        w = synthetic.random_graph(rng, 17, 0, 2, 1, 1, 1)
+    elif kind == "no_inputs":
+        w = synthetic.random_graph(rng, 300, 2000, 0, 1, 1, 1)
+    elif kind == "one_node":
+        w = synthetic.random_graph(rng, 1, 5, 1, 1, 1, 1)
+    else:
+        raise ValueError(kind)
+    return w
+
+
+@pytest.mark.parametrize("kind", ["parallel_edges", "hub_rows", "empty_rows", "no_edges",
+                                  "no_inputs", "one_node"])
+def test_graph_build_adversarial(kind):
+    log(f"graph build adversarial: {kind}")
+    _check_graph(_adversarial(kind, np.random.default_rng(5)))
+
+
+@pytest.mark.parametrize("case", ["src_range", "dst_negative", "input_range", "dup_input"])
+def test_graph_validation_agrees_with_oracle(case):
+    log(f"graph validation: {case}")
+    rng = np.random.default_rng(9)
+    N, E = 100, 5000
+    src, dst = rng.integers(0, N, E), rng.integers(0, N, E)
+    inputs = np.arange(5)
+    if case == "src_range":
+        src[4321] = N
+    elif case == "dst_negative":
+        dst[17] = -1
+    elif case == "input_range":
+        inputs = np.array([0, 1, N + 3])
+    elif case == "dup_input":
+        inputs = np.array([4, 8, 4])
+    want = oracle.validate(src, dst, N, inputs)
+    assert want != 0
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.SparseGraph(to_dev(src), to_dev(dst), N, to_dev(inputs))
+    assert ei.value.status == want
+
+
+# ---------------------------------------------------------------- parity, small
+def test_tiny_workload_full_parity():
+    w = synthetic.make("tiny")
+    log("parity: tiny workload")
+    compare_all(run_gpu(w), run_oracle(w))
+
+
+def _mixed_graph(seed, B, T, M, N=400, E=9000, n_in=9):
+    """Uniform edges plus two hub rows (in- and out-degree above the split
+    threshold), parallel edges, self-loops and a few empty rows."""
+    rng = np.random.default_rng(seed)
+    w = synthetic.random_graph(rng, N, E, n_in, B, T, M, v_scale=0.15)
+    hub_in = rng.integers(0, N, 1500)
+    hub_out = rng.integers(0, N, 1200)
+    w.src = np.concatenate([w.src, hub_in, np.full(1200, 11)])
+    w.dst = np.concatenate([w.dst, np.full(1500, 5), hub_out])
+    keep = ~np.isin(w.dst, [20, 21, 22])   # rows without in-edges
+    w.src, w.dst = w.src[keep], w.dst[keep]
+    p = rng.permutation(w.src.size)
+    w.src, w.dst = w.src[p], w.dst[p]
+    w.edge_values = (0.15 * rng.standard_normal(w.src.size)).astype(np.float32)
+    return w
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 20, 31, 32, 33, 64, 65, 100])
+def test_batch_widths_parity(B):
+    w = _mixed_graph(100 + B, B=B, T=3, M=2)
+    log(f"parity: mixed graph B={B} E={w.num_edges}")
+    compare_all(run_gpu(w), run_oracle(w))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3])
+def test_microsteps_parity(M):
+    w = _mixed_graph(200 + M, B=32, T=4, M=M)
+    log(f"parity: mixed graph M={M}")
+    compare_all(run_gpu(w), run_oracle(w))
+
+
+@pytest.mark.parametrize("kind", ["no_edges", "no_inputs", "one_node", "empty_rows", "hub_rows"])
+def test_degenerate_graphs_parity(kind):
+    rng = np.random.default_rng(77)
+    w = _adversarial(kind, rng)
+    B, T, M = 6, 3, 2
+    rng2 = np.random.default_rng(78)
+    w.edge_values = (0.05 * rng2.standard_normal(w.num_edges)).astype(np.float32)
+    w.drives = rng2.standard_normal((T, w.n_in, B)).astype(np.float32)
+    w.state0 = (0.3 * rng2.standard_normal((B, w.num_nodes))).astype(np.float32)
+    w.grad_out = rng2.standard_normal((T, B, w.num_nodes)).astype(np.float32)
+    w.microsteps = M
+    log(f"parity: degenerate {kind} N={w.num_nodes} E={w.num_edges}")
+    compare_all(run_gpu(w), run_oracle(w))
+
+
+def test_saturated_preactivations():
+    """A third of the nodes sit at |a| ~ 6..12 (bias +-6, strong drives), where
+    tanh' must come from the pre-activation, not from 1 - tanh^2."""
+    w = _mixed_graph(300, B=32, T=3, M=2)
+    i = np.arange(w.num_nodes)
+    w.bias = np.where(i % 3 == 0, np.where(i % 2 == 0, 6.0, -6.0), w.bias).astype(np.float32)
+    w.drives = (6.0 * w.drives).astype(np.float32)
+    log("parity: saturated pre-activations")
+    compare_all(run_gpu(w), run_oracle(w))
+
+
+# ---------------------------------------------------------------- parity, full size
+def test_flygpt_full_parity():
+    w = synthetic.make("flygpt")
+    log("parity: flygpt launch shape, all columns")
+    gpu, ref = run_gpu(w), run_oracle(w)
+    compare_all(gpu, ref)
+    compare_floor(gpu, ref, run_oracle(w, precision="f32"))
+
+
+def test_edge_cases_full_parity():
+    w = synthetic.make("edge_cases")
+    log("parity: edge-cases workload, all columns")
+    gpu, ref = run_gpu(w), run_oracle(w)
+    compare_all(gpu, ref)
+    compare_floor(gpu, ref, run_oracle(w, precision="f32"))
+
+
+def test_mid_scale_sampled_parity():
+    w = synthetic.make("mid_scale")
+    cols = [0, 37, 63]
+    G = column_masked_grad(w, cols)
+    log("parity: mid-scale workload, columns 0, 37, 63")
+    gpu, ref = run_gpu(w, G=G), run_oracle(w, G=G, cols=cols)
+    compare_all(gpu, ref, cols=cols)
+    compare_floor(gpu, ref, run_oracle(w, G=G, cols=cols, precision="f32"), cols=cols)
+
+
+@pytest.mark.slow
+def test_connectome_sampled_parity():
+    w = synthetic.make("connectome")
+    cols = [0, 31]
+    G = column_masked_grad(w, cols)
+    log("parity: whole-connectome workload, columns 0, 31")
+    gpu, ref = run_gpu(w, G=G), run_oracle(w, G=G, cols=cols)
+    compare_all(gpu, ref, cols=cols)
+    compare_floor(gpu, ref, run_oracle(w, G=G, cols=cols, precision="f32"), cols=cols)
+    log("graph build: connectome")
+    g = make_graph(w)
+    got = {k: v.cpu().numpy() for k, v in g.export().items()}
+    ref = oracle.build_graph(w.src, w.dst, w.num_nodes, w.input_nodes)
+    for k in GRAPH_KEYS:
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+
+
+# ---------------------------------------------------------------- properties
+def test_results_are_bitwise_deterministic():
+    w = synthetic.make("edge_cases")
+    log("determinism: edge-cases workload twice")
+    g = make_graph(w)
+    a, b = run_gpu(w, graph=g), run_gpu(w, graph=g)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_caller_edge_order_is_invisible_bitwise():
+    w = _mixed_graph(400, B=20, T=3, M=2)
+    key = w.dst * w.num_nodes + w.src
+    _, first = np.unique(key, return_index=True)   # unique (src, dst) pairs only
+    w.src, w.dst, w.edge_values = w.src[first], w.dst[first], w.edge_values[first]
+    log("edge-order invariance")
+    a = run_gpu(w)
+    p = np.random.default_rng(1).permutation(w.num_edges)
+    w.src, w.dst, w.edge_values = w.src[p], w.dst[p], w.edge_values[p]
+    b = run_gpu(w)
+    for k in ("out", "g_leak", "g_bias", "g_drives", "g_state0"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    np.testing.assert_array_equal(a["g_edge_values"][p], b["g_edge_values"])
+
+
+def test_autograd_wrapper_matches_direct_calls():
+    w = synthetic.make("tiny")
+    log("autograd wrapper")
+    g = make_graph(w)
+    ins = [to_dev(x).requires_grad_() for x in (w.edge_values, w.leak, w.bias, w.drives, w.state0)]
+    out = sgr.sparse_recurrence(*ins, g, microsteps=w.microsteps)
+    (out * to_dev(w.grad_out)).sum().backward()
+    direct = run_gpu(w, graph=g)
+    np.testing.assert_array_equal(out.detach().cpu().numpy(), direct["out"])
+    for x, k in zip(ins, ("g_edge_values", "g_leak", "g_bias", "g_drives", "g_state0")):
+        np.testing.assert_array_equal(x.grad.cpu().numpy(), direct[k], err_msg=k)
+
+
+def test_workspace_too_small_is_rejected():
+    w = synthetic.make("tiny")
+    g = make_graph(w)
+    _, wb = sgr.recurrence_sizes(g, w.T, w.B, w.microsteps)
+    small = torch.empty(wb - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.recurrence_forward(g, to_dev(w.edge_values), to_dev(w.leak), to_dev(w.bias),
+                               to_dev(w.drives), to_dev(w.state0), w.microsteps, workspace=small)
+    assert ei.value.status == 6

@@ -16,21 +16,22 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ck_oracle.c")
 
 MUTANTS = {
     "transposed_W_forward": ("acc[dst[e]] += v[e] * hb[src[e]];", "acc[src[e]] += v[e] * hb[dst[e]];"),
-    "bias_dropped": ("double x = acc[i] + drive + bias[i];", "double x = acc[i] + drive;"),
-    "leak_mix_swapped": ("hn[b * N + i] = (1.0 - leak[i]) * hb[i] + leak[i] * tanh(x);",
-                         "hn[b * N + i] = leak[i] * hb[i] + (1.0 - leak[i]) * tanh(x);"),
+    "bias_dropped": ("real x = acc[i] + drive + bias[i];", "real x = acc[i] + drive;"),
+    "leak_mix_swapped": ("hn[b * N + i] = ((real)1 - leak[i]) * hb[i] + leak[i] * tanh(x);",
+                         "hn[b * N + i] = leak[i] * hb[i] + ((real)1 - leak[i]) * tanh(x);"),
     "drive_column_fixed": ("drives[(t * n_in + slot[i]) * B + b]", "drives[(t * n_in + slot[i]) * B]"),
-    "output_first_microstep": ("if (s % M == 0) memcpy(out", "if (s % M == 1 % M) memcpy(out"),
-    "carry_leak_dropped": ("gnb[j] = (1.0 - leak[j]) * gb_[j];", "gnb[j] = gb_[j];"),
+    "output_first_microstep": ("if (s % M == 0)\n      for (int64_t x = 0; x < BN; ++x) out[",
+                               "if (s % M == 1 % M)\n      for (int64_t x = 0; x < BN; ++x) out["),
+    "carry_leak_dropped": ("gnb[j] = ((real)1 - leak[j]) * gb_row[j];", "gnb[j] = gb_row[j];"),
     "transposed_W_backward": ("gnb[src[e]] += v[e] * gab[dst[e]];", "gnb[dst[e]] += v[e] * gab[src[e]];"),
     "edge_grad_swapped": ("ga[b * N + dst[e]] * q[b * N + src[e]]", "ga[b * N + src[e]] * q[b * N + dst[e]]"),
     "leak_grad_sign": ("gl += g[x] * (p - q[x]);", "gl += g[x] * (q[x] - p);"),
     "ga_without_leak": ("ga[x] = g[x] * leak[i] * or_sech2(a[x]);", "ga[x] = g[x] * or_sech2(a[x]);"),
     "drive_grad_wrong_node": ("+= ga[b * N + inputs[k]];", "+= ga[b * N + k];"),
-    "upstream_grad_wrong_step": ("if (s % M == 0)\n        for (int64_t x = 0; x < BN; ++x) g[x] += G[t * BN + x];",
-                                 "if (s % M == 1 % M)\n        for (int64_t x = 0; x < BN; ++x) g[x] += G[t * BN + x];"),
-    "leak_grad_uses_new_state": ("const double* q = hs + (s - 1) * BN;", "const double* q = hs + s * BN;"),
-    "sech2_is_sech": ("return 1.0 / (c * c);", "return 1.0 / c;"),
+    "upstream_grad_wrong_step": ("if (s % M == 0)\n        for (int64_t x = 0; x < BN; ++x) g[x] +=",
+                                 "if (s % M == 1 % M)\n        for (int64_t x = 0; x < BN; ++x) g[x] +="),
+    "leak_grad_uses_new_state": ("const real* q = hs + (s - 1) * BN;", "const real* q = hs + s * BN;"),
+    "sech2_is_sech": ("return (real)1 / (c * c);", "return (real)1 / c;"),
 }
 
 PIN_CALLS = [
@@ -60,8 +61,8 @@ def test_every_planted_mistake_fails_a_pin(name, monkeypatch):
     old, new = MUTANTS[name]
     with tempfile.TemporaryDirectory() as tmp:
         lib = _build_mutant(tmp, old, new)
-        monkeypatch.setattr(oracle, "_LIB_PATH", lib)
-        monkeypatch.setattr(oracle, "_lib", None)
+        monkeypatch.setitem(oracle._LIB_PATHS, "f64", lib)
+        monkeypatch.setattr(oracle, "_libs", {})
         failed = []
         for pin_name, call in PIN_CALLS:
             try:
@@ -69,4 +70,4 @@ def test_every_planted_mistake_fails_a_pin(name, monkeypatch):
             except AssertionError:
                 failed.append(pin_name)
         assert failed, f"mutant {name} passed every pin"
-    monkeypatch.setattr(oracle, "_lib", None)
+    monkeypatch.setattr(oracle, "_libs", {})
