@@ -2,11 +2,14 @@
 the FlyGPT launch shape (N=5,000 nodes, E=524,324 edges, B=32, T=64 input
 steps x 2 microsteps, fp32) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-graph] [--no-cpu]
 
 One step = ck_recurrence_forward + ck_recurrence_backward over the whole
 window on one HIP stream; inputs, graph and buffers are resident in HBM
 before timing starts (graph construction and input generation are excluded).
+By default the step's launches are captured once into a HIP graph (through
+torch.cuda.CUDAGraph on the stream the library launches on) and the graph is
+replayed; --no-graph launches them directly.
 Prints one JSON line with:
   value        edge-visits/s = S * E * B / t_step  (S = T * M microsteps)
   ms_per_step  mean time of one step over the K timed steps (HIP events)
@@ -47,6 +50,32 @@ def algorithmic_bytes(N, E, n_in, B, T, M):
     return fwd, bwd, S * (fwd + bwd) + once
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "flygpt_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "sparse_graph_recurrent_amd", "csrc", "recurrence.hip")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            text = f.read()
+        with open(KERNEL_SOURCE, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != digest:
+        return None
+    v = fields.get(f"{kernel}_bytes_per_launch")
+    return int(v) if v else None
+
+
 def cpu_baseline(w, budget_s: float = 20.0):
     """The CPU oracle (fp64, OpenMP over all host cores) on the same workload:
     whole forward+backward windows, repeated until about budget_s seconds."""
@@ -71,9 +100,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--graph", action="store_true", help="replay each step as a captured HIP graph")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every step directly instead of replaying a captured HIP graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--workload", default="flygpt")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch's plain device copy of MIB MiB three times (the "
+                         "reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the recurrence would "
@@ -88,6 +121,15 @@ def main():
     import synthetic
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4}), flush=True)
+        return
     w = synthetic.make(args.workload)
     N, E, n_in, B, T, M = w.num_nodes, w.num_edges, w.n_in, w.B, w.T, w.microsteps
     S = T * M
@@ -109,7 +151,8 @@ def main():
         sgr.recurrence_backward(graph, ev, lk, st, M, saved, G, workspace=ws, grads=grads)
 
     run = step
-    if args.graph:
+    use_graph = not args.no_graph
+    if use_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -168,13 +211,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: N={N} E={E} n_in={n_in} B={B} T={T} "
                                f"microsteps={M} (seed {w.seed})",
-                   "parallelism": "single GPU", "hip_graph": bool(args.graph)},
+                   "parallelism": "single GPU", "hip_graph": use_graph},
         "yardstick_GBps": Q / (ms * 1e-3) / 1e9,
         "yardstick_frac_of_hbm_peak": Q / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels": {"fwd_step_us": fwd_us, "bwd_step_us": bwd_us,
                     "fwd_launches_per_step": S, "bwd_launches_per_step": S + 1},
         "roofline": {"bound": "hbm", "kernel": name, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(name)},
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w)

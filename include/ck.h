@@ -27,7 +27,7 @@
  *     propagate.
  *   - Sizes: num_nodes and num_edges must be below 2^31, and num_nodes times
  *     the padded batch width (B rounded up to a multiple of 4) must be below
- *     2^31; otherwise CK_ERR_TOO_LARGE.
+ *     2^30 (one state plane under 4 GiB); otherwise CK_ERR_TOO_LARGE.
  *   - A graph handle is immutable after creation and may be used from several
  *     streams at once provided each call has its own `saved` and `workspace`.
  *   - Calls that share a `saved` or `workspace` buffer must be ordered on one
@@ -156,10 +156,10 @@ ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_values, const f
  * Measurement hook (changes no result).  While enabled (process-wide),
  * forward and backward record a pair of HIP events on the caller's stream
  * around every launch of the per-microstep kernels: the fused forward
- * microstep kernel and the fused backward step kernel.  ck_profile_collect
- * waits for the recorded events, returns the summed kernel durations in
- * milliseconds and the launch counts since the last collect, and releases the
- * events.  Any output pointer may be NULL.  Not meant for concurrent use from
+ * microstep kernel and the fused backward step kernel (timing-only events
+ * without a system-scope fence).  ck_profile_collect synchronises the device,
+ * returns the summed kernel durations in milliseconds and the launch counts
+ * since the last collect, and releases the events.  Any output pointer may be NULL.  Not meant for concurrent use from
  * several threads.
  */
 ck_status ck_profile_enable(int enable);

@@ -11,22 +11,41 @@
 
 namespace ckhip {
 
-// Workgroup shape of every hot-path kernel: 4 wave64s.
-constexpr int kWaves = 4;
+// Tuning constants (compile-time; -D overrides exist for sweeps only).
+#ifndef CK_WAVES
+#define CK_WAVES 8
+#endif
+#ifndef CK_SPLIT_EDGES
+#define CK_SPLIT_EDGES 128
+#endif
+#ifndef CK_WGS_PER_CU
+#define CK_WGS_PER_CU 2
+#endif
+// Workgroup shape of the per-microstep kernels: kWaves wave64s.
+constexpr int kWaves = CK_WAVES;
 constexpr int kThreads = kWaves * 64;
-// Rows with more edges than this are split across all waves of a workgroup.
-constexpr int kLongRow = 256;
+// A row is split into pieces (at most kWaves, all in one workgroup) when it
+// holds more than max(kSplitEdges, per-wave share) edges.
+constexpr int kSplitEdges = CK_SPLIT_EDGES;
+// Workgroups per CU the schedule is sized for (one resident round).
+constexpr int kWgsPerCu = CK_WGS_PER_CU;
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X.
 constexpr int kXcds = 8;
 
-// A degree-balanced row schedule for one orientation of the graph.
-//   items[w] = {first, count} for workgroup w: count == -1 -> one long row
-//   rows[first] split across the waves; count in 1..kWaves -> wave i takes
-//   rows[first + i]; count == 0 -> nothing to do (padding).
+// Row schedule of one orientation of the graph.  Wave v (= workgroup * kWaves
+// + wave index) walks its segments segs[v * K .. v * K + K) in order until a
+// segment with row < 0.  Segment = {row, kbeg, kend, info}: the edges
+// [kbeg, kend) of the row's compressed list.
+//   info bits 0..7: for a piece of a split row, the wave (inside the
+//   workgroup) that combines the pieces; bits 8..15: number of pieces;
+//   bit 16: the workgroup holds split rows (all its waves synchronise once at
+//   the end); bit 17: this segment is a piece (always a wave's first segment).
+constexpr int kInfoGroupBit = 1 << 16;
+constexpr int kInfoPieceBit = 1 << 17;
 struct Schedule {
-  int2* items = nullptr;
-  int32_t* rows = nullptr;
-  int num_items = 0;
+  int4* segs = nullptr;  // [num_wgs * kWaves * K]
+  int num_wgs = 0;
+  int K = 0;             // segments per wave (padded with row = -1)
 };
 
 }  // namespace ckhip

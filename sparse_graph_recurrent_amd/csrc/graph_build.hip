@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <queue>
 #include <vector>
 
 #include "ck_internal.h"
@@ -267,12 +268,17 @@ ck_status build_compressed(const int64_t* major, const int64_t* minor, int64_t E
 }
 
 // Degree-balanced, XCD-aware schedule (host side, from the row pointers).
-// Rows are cut into kXcds contiguous ranges of about equal cost (edges plus a
-// per-row constant); workgroup w runs on XCD w % kXcds and takes that XCD's
-// (w / kXcds)-th item.  Inside a range, rows go heaviest first: long rows one
-// per workgroup, the rest kWaves per workgroup.
-ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, Schedule* out) {
+// The grid is sized for one resident round (kWgsPerCu workgroups per CU) and
+// every wave walks a list of row segments.  Rows are cut into kXcds
+// contiguous ranges of about equal cost (edges plus a per-row constant);
+// workgroup g runs on XCD g % kXcds and takes XCD-local workgroup g / kXcds.
+// Inside an XCD, rows above twice the per-wave share become pieces on consecutive
+// waves of one workgroup (combined through LDS at the end of the kernel),
+// then the remaining rows go heaviest first to the least-loaded wave.
+ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, int num_cus,
+                         Schedule* out) {
   constexpr int64_t kRowCost = 16;
+  constexpr int64_t kMinWaveCost = 96;
   std::vector<int64_t> deg(N);
   int64_t total = 0;
   for (int64_t i = 0; i < N; ++i) {
@@ -289,46 +295,94 @@ ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, Schedule* o
       while (x < kXcds && acc * kXcds >= total * x) cut[x++] = i + 1;
     }
   }
-  std::vector<int32_t> rows;
-  rows.reserve(N);
-  std::vector<std::vector<int2>> lists(kXcds);
+  // workgroups per XCD: one resident round, fewer for small graphs
+  const int64_t cap = std::max<int64_t>(1, (int64_t)num_cus / kXcds * kWgsPerCu);
+  const int64_t want = (total / kXcds + kMinWaveCost * kWaves - 1) / (kMinWaveCost * kWaves);
+  const int wg_x = (int)std::max<int64_t>(1, std::min(cap, want));
+  const int waves_x = wg_x * kWaves;
+  struct Seg {
+    int32_t row, kb, ke, info;
+  };
+  std::vector<std::vector<std::vector<Seg>>> lists(kXcds);
+  size_t K = 1;
   for (int x = 0; x < kXcds; ++x) {
+    auto& waves = lists[x];
+    waves.assign(waves_x, {});
+    std::vector<int64_t> load(waves_x, 0);
+    std::vector<bool> wg_group(wg_x, false);
+    int64_t cost_x = 0;
+    for (int64_t i = cut[x]; i < cut[x + 1]; ++i) cost_x += deg[i] + kRowCost;
+    const int64_t share = std::max<int64_t>(kSplitEdges, cost_x / waves_x);
     std::vector<int32_t> r;
     for (int64_t i = cut[x]; i < cut[x + 1]; ++i) r.push_back((int32_t)i);
     std::stable_sort(r.begin(), r.end(), [&](int32_t a, int32_t b) { return deg[a] > deg[b]; });
+    // split rows: pieces on consecutive, still piece-free waves of one workgroup
     size_t j = 0;
-    for (; j < r.size() && deg[r[j]] > kLongRow; ++j) {
-      lists[x].push_back(make_int2((int)rows.size(), -1));
-      rows.push_back(r[j]);
+    int wg = 0, used = 0;
+    for (; j < r.size() && deg[r[j]] > 2 * share; ++j) {
+      const int64_t d = deg[r[j]];
+      const int np = (int)std::min<int64_t>(kWaves, (d + share - 1) / share);
+      if (used + np > kWaves) {
+        ++wg;
+        used = 0;
+      }
+      if (wg >= wg_x) break;  // no room left: the rest are whole rows
+      const int lead = used;
+      for (int q = 0; q < np; ++q) {
+        const int v = wg * kWaves + used++;
+        const int32_t kb = (int32_t)(ptr[r[j]] + d * q / np);
+        const int32_t ke = (int32_t)(ptr[r[j]] + d * (q + 1) / np);
+        waves[v].push_back({r[j], kb, ke, lead | (np << 8) | kInfoPieceBit});
+        load[v] += ke - kb + kRowCost;
+      }
+      wg_group[wg] = true;
     }
-    while (j < r.size()) {
-      int cnt = (int)std::min<size_t>(kWaves, r.size() - j);
-      lists[x].push_back(make_int2((int)rows.size(), cnt));
-      for (int q = 0; q < cnt; ++q) rows.push_back(r[j + q]);
-      j += cnt;
+    // remaining rows: heaviest first to the least-loaded wave
+    using Entry = std::pair<int64_t, int>;
+    std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap;
+    for (int v = 0; v < waves_x; ++v) heap.push({load[v], v});
+    for (; j < r.size(); ++j) {
+      auto [l, v] = heap.top();
+      heap.pop();
+      waves[v].push_back({r[j], ptr[r[j]], ptr[r[j] + 1], 0});
+      heap.push({l + deg[r[j]] + kRowCost, v});
+    }
+    for (int v = 0; v < waves_x; ++v) {
+      if (wg_group[v / kWaves])
+        for (auto& sg : waves[v]) sg.info |= kInfoGroupBit;
+      K = std::max(K, waves[v].size());
     }
   }
-  size_t nmax = 1;
-  for (auto& l : lists) nmax = std::max(nmax, l.size());
-  std::vector<int2> items(nmax * kXcds, make_int2(0, 0));
-  for (size_t r = 0; r < nmax; ++r)
-    for (int x = 0; x < kXcds; ++x)
-      if (r < lists[x].size()) items[r * kXcds + x] = lists[x][r];
-  out->num_items = (int)items.size();
-  CK_HIP_TRY(hipMalloc(&out->items, items.size() * sizeof(int2)));
-  CK_HIP_TRY(hipMalloc(&out->rows, std::max<size_t>(1, rows.size()) * sizeof(int32_t)));
-  CK_HIP_TRY(hipMemcpy(out->items, items.data(), items.size() * sizeof(int2), hipMemcpyHostToDevice));
-  if (!rows.empty())
-    CK_HIP_TRY(hipMemcpy(out->rows, rows.data(), rows.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  const int num_wgs = wg_x * kXcds;
+  std::vector<int4> segs((size_t)num_wgs * kWaves * K, make_int4(-1, 0, 0, 0));
+  for (int x = 0; x < kXcds; ++x)
+    for (int v = 0; v < waves_x; ++v) {
+      const int wgl = v / kWaves, wv = v % kWaves;
+      const size_t gv = ((size_t)(wgl * kXcds + x) * kWaves + wv) * K;
+      const auto& lst = lists[x][v];
+      for (size_t k = 0; k < lst.size(); ++k)
+        segs[gv + k] = make_int4(lst[k].row, lst[k].kb, lst[k].ke, lst[k].info);
+      // an empty wave of a workgroup with split rows must still reach its barrier
+      if (lst.empty()) {
+        bool grp = false;
+        for (int q = 0; q < kWaves; ++q)
+          for (auto& sg : lists[x][wgl * kWaves + q]) grp |= (sg.info & kInfoGroupBit) != 0;
+        if (grp) segs[gv] = make_int4(-1, 0, 0, kInfoGroupBit);
+      }
+    }
+  out->num_wgs = num_wgs;
+  out->K = (int)K;
+  CK_HIP_TRY(hipMalloc(&out->segs, segs.size() * sizeof(int4)));
+  CK_HIP_TRY(hipMemcpy(out->segs, segs.data(), segs.size() * sizeof(int4), hipMemcpyHostToDevice));
   return CK_OK;
 }
 
 void free_graph_arrays(ck_graph* g) {
   int32_t* arrs[] = {g->row_ptr, g->col_idx, g->perm, g->t_row_ptr, g->t_col_idx, g->t_perm,
-                     g->input_slot, g->fwd.rows, g->bwd.rows};
+                     g->input_slot};
   for (int32_t* p : arrs) (void)hipFree(p);
-  (void)hipFree(g->fwd.items);
-  (void)hipFree(g->bwd.items);
+  (void)hipFree(g->fwd.segs);
+  (void)hipFree(g->bwd.segs);
 }
 
 }  // namespace
@@ -425,9 +479,15 @@ extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int
   CK_GB_TRY(hipMemcpyAsync(hptr.data(), g->row_ptr, nb, hipMemcpyDeviceToHost, stream));
   CK_GB_TRY(hipMemcpyAsync(htptr.data(), g->t_row_ptr, nb, hipMemcpyDeviceToHost, stream));
   CK_GB_TRY(hipStreamSynchronize(stream));
-  rc = build_schedule(hptr, N, &g->fwd);
+  int num_cus = 256;
+  {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, g->device) == hipSuccess && prop.multiProcessorCount > 0)
+      num_cus = prop.multiProcessorCount;
+  }
+  rc = build_schedule(hptr, N, num_cus, &g->fwd);
   if (rc != CK_OK) return fail(rc);
-  rc = build_schedule(htptr, N, &g->bwd);
+  rc = build_schedule(htptr, N, num_cus, &g->bwd);
   if (rc != CK_OK) return fail(rc);
   (void)hipFree(flags);
   (void)hipFree(seen);

@@ -46,9 +46,11 @@ ck_status timed_launch(std::vector<std::pair<hipEvent_t, hipEvent_t>>& log, hipS
     launch();
     return CK_OK;
   }
+  // timing-only events: no system-scope fence (cache writeback/invalidate)
+  // around the kernel they bracket
   hipEvent_t a, b;
-  CK_HIP_TRY(hipEventCreate(&a));
-  CK_HIP_TRY(hipEventCreate(&b));
+  CK_HIP_TRY(hipEventCreateWithFlags(&a, hipEventDisableSystemFence));
+  CK_HIP_TRY(hipEventCreateWithFlags(&b, hipEventDisableSystemFence));
   CK_HIP_TRY(hipEventRecord(a, stream));
   launch();
   CK_HIP_TRY(hipEventRecord(b, stream));
@@ -57,6 +59,24 @@ ck_status timed_launch(std::vector<std::pair<hipEvent_t, hipEvent_t>>& log, hipS
 }
 
 constexpr int kChunkCols = 64;  // columns per grid-y chunk when Bp > 64
+// Occupancy targets (waves per SIMD) that bound the register budget of the
+// two per-microstep kernels; 0 leaves the choice to the compiler.
+#ifndef CK_FWD_OCC
+#define CK_FWD_OCC 0
+#endif
+#ifndef CK_BWD_OCC
+#define CK_BWD_OCC 0
+#endif
+#if CK_FWD_OCC > 0
+#define CK_FWD_ATTR __attribute__((amdgpu_waves_per_eu(CK_FWD_OCC)))
+#else
+#define CK_FWD_ATTR
+#endif
+#if CK_BWD_OCC > 0
+#define CK_BWD_ATTR __attribute__((amdgpu_waves_per_eu(CK_BWD_OCC)))
+#else
+#define CK_BWD_ATTR
+#endif
 
 __device__ __forceinline__ float4 f4(float x) { return make_float4(x, x, x, x); }
 __device__ __forceinline__ float4 fma4(float w, float4 h, float4 acc) {
@@ -78,9 +98,6 @@ __device__ __forceinline__ float4 shfl_xor4(float4 v, int m) {
 }
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-}
-__device__ __forceinline__ float4 tanh4(float4 a) {
-  return make_float4(tanhf(a.x), tanhf(a.y), tanhf(a.z), tanhf(a.w));
 }
 // sech^2(a) = 4 e^{-2|a|} / (1 + e^{-2|a|})^2, from the pre-activation itself
 // (not 1 - tanh^2, which cancels badly once |a| is a few units).
@@ -134,10 +151,149 @@ __device__ __forceinline__ float sum_in_slot(float x, int slot) {
   }
 }
 
+// Sum over the L lanes of one slot with DPP lane swizzles (no LDS traffic);
+// every lane of the slot receives the same bits.  L must be a power of two.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+template <int L>
+__device__ __forceinline__ float slot_sum(float x, int slot) {
+  if constexpr (L == 1) {
+    return x;
+  } else if constexpr (is_pow2(L)) {
+    x += dpp<0xB1>(x);                      // quad_perm [1,0,3,2]: pairs
+    if constexpr (L >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: quads
+    if constexpr (L >= 8) x += dpp<0x141>(x);  // row_half_mirror: 8 lanes
+    if constexpr (L >= 16) x += dpp<0x128>(x); // row_ror 8: 16 lanes
+    return x;
+  } else {
+    return sum_in_slot<L>(x, slot);
+  }
+}
+
+// Sum over the epilogue lanes 0 .. 4L-1 (slots 0..3); exact in lane 0.
+template <int L>
+__device__ __forceinline__ float epilogue_sum(float x, int slot) {
+  if constexpr (is_pow2(L)) {
+    x = slot_sum<L>(x, slot);
+    x += __shfl_xor(x, L);
+    x += __shfl_xor(x, 2 * L);
+    return x;
+  } else {
+    float s = __shfl(x, 0);
+    for (int i = 1; i < 4 * L; ++i) s += __shfl(x, i);
+    return s;
+  }
+}
+
+// 16-byte load at a 32-bit byte offset from a uniform base (lets the compiler
+// use the scalar-base addressing form: one VGPR per address).
+__device__ __forceinline__ float4 ld4(const float* base, uint32_t byte_off) {
+  return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+// Bounds-checked build (-DCK_CHECKED, for validating kernel changes): every
+// global access goes through CK_AT / ld4c, an out-of-range index sets a site
+// bit in g_ck_err and is redirected to a scratch cell instead of faulting.
+#ifdef CK_CHECKED
+__device__ unsigned g_ck_err;
+__device__ float4 g_ck_dummy[2];
+template <typename T>
+__device__ __forceinline__ T* ck_at(T* base, size_t i, size_t n, int site) {
+  if (base == nullptr || i >= n) {
+    atomicOr(&g_ck_err, 1u << site);
+    return reinterpret_cast<T*>(g_ck_dummy);
+  }
+  return base + i;
+}
+#define CK_AT(base, i, n, site) (*ck_at((base), (size_t)(i), (size_t)(n), (site)))
+__device__ __forceinline__ float4 ld4c(const float* base, uint32_t byte_off, size_t nfloats,
+                                       int site) {
+  if (base == nullptr || (size_t)byte_off / 4 + 4 > nfloats || (byte_off & 15u)) {
+    atomicOr(&g_ck_err, 1u << site);
+    return g_ck_dummy[0];
+  }
+  return ld4(base, byte_off);
+}
+#else
+#define CK_AT(base, i, n, site) ((base)[(i)])
+__device__ __forceinline__ float4 ld4c(const float* base, uint32_t byte_off, size_t, int) {
+  return ld4(base, byte_off);
+}
+#endif
+
+__device__ __forceinline__ float pick4(float4 v, int q) {
+  return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+}
+
+// Lane roles shared by both kernels.  In the gather loop lane = slot * L + sub
+// holds columns [col, col + 4) of one gathered row.  In the per-row epilogue
+// lane (slot q < 4, sub s) handles the single column colbase + 4 s + q, so 32
+// lanes (not 8) share the transcendental work at B = 32.
+struct Lanes {
+  int lane, wave, slot, sub, col, ecol;
+  bool ok;       // lane takes part in the gather loop
+  bool eok;      // lane owns an epilogue column < Bp
+};
+
+template <int L>
+__device__ __forceinline__ Lanes lanes(int Bp) {
+  Lanes r;
+  r.lane = threadIdx.x & 63;
+  r.wave = threadIdx.x >> 6;
+  r.slot = r.lane / L;
+  r.sub = r.lane % L;
+  const int colbase = blockIdx.y * kChunkCols;
+  r.col = colbase + r.sub * 4;
+  r.ok = r.slot < Geom<L>::P && r.col < Bp;
+  r.ecol = r.col + r.slot;
+  r.eok = r.slot < 4 && r.col < Bp;  // ecol < Bp since Bp is a multiple of 4
+  return r;
+}
+
+// Pull a whole state plane into this XCD's L2 at kernel start: the plane was
+// written by every XCD in the previous launch, so each XCD would otherwise
+// first-touch every gathered row from the memory side.  Workgroup w lives on
+// XCD w % kXcds; the workgroups of one XCD share the plane between them.
+// Returns a value that must be consumed (keeps the loads alive).
+constexpr uint32_t kPrefetchMaxBytes = 2u << 20;
+__device__ __forceinline__ float prefetch_plane(const float* plane, uint32_t bytes) {
+  float keep = 0.f;
+  if (bytes > kPrefetchMaxBytes || blockIdx.y != 0) return keep;
+  const uint32_t per_xcd = gridDim.x / kXcds;
+  if (per_xcd == 0) return keep;
+  const uint32_t slice = blockIdx.x / kXcds;
+  const uint32_t chunk = ((bytes / per_xcd) + 255u) & ~255u;
+  const uint32_t b0 = slice * chunk;
+  const uint32_t b1 = min(bytes, b0 + chunk);
+  // one dword per 128-byte line is enough to fill the line
+  for (uint32_t b = b0 + threadIdx.x * 128u; b < b1; b += kThreads * 128u)
+    keep += CK_AT(plane, b / 4u, bytes / 4u, 25);
+  return keep;
+}
+
+__device__ __forceinline__ void consume(float x) { asm volatile("" ::"v"(x)); }
+
+// Edge indices and values of one batch (lane k: edge kb + k, clamped to the
+// row; lanes past the end get value 0).
+__device__ __forceinline__ void csr_batch(const int32_t* __restrict__ idx,
+                                          const float* __restrict__ val, int kb, int kend,
+                                          int lane, int E, int& c, float& w) {
+  const int e = kb + lane;
+  const int ec = min(e, kend - 1);
+  c = CK_AT(idx, ec, E, 8);
+  w = e < kend ? CK_AT(val, ec, E, 9) : 0.f;
+}
+
+__device__ __forceinline__ int4 seg_at(const int4* __restrict__ segs, int K, int k) {
+  return k < K ? CK_AT(segs, k, K, 10) : make_int4(-1, 0, 0, 0);
+}
+
 struct FwdArgs {
-  const int2* items;
-  const int32_t* rows;
-  const int32_t* row_ptr;
+  const int4* segs;       // schedule: K segments per wave
+  int K;
   const int32_t* col_idx;
   const float* v_csr;
   const float* leak;
@@ -148,95 +304,127 @@ struct FwdArgs {
   float* h_next;          // [N][Bp]
   float* a_next;          // [N][Bp]
   float* out_t;           // [B][N] or nullptr when s is not the last microstep of a step
-  int N, B, Bp;
+  int N, B, Bp, E, n_in;
 };
 
+// Row operands of the forward epilogue (this lane's column).
+struct FwdEpi {
+  float hp, lam, bi, dv;
+};
+
+__device__ __forceinline__ FwdEpi fwd_epi_load(const FwdArgs& p, const Lanes& ln, int row) {
+  FwdEpi e{0.f, 0.f, 0.f, 0.f};
+  if (row < 0 || !ln.eok) return e;
+  [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
+  e.hp = CK_AT(p.h_prev, (size_t)row * p.Bp + ln.ecol, NBp, 0);
+  e.lam = CK_AT(p.leak, row, p.N, 1);
+  e.bi = CK_AT(p.bias, row, p.N, 2);
+  const int ks = CK_AT(p.input_slot, row, p.N, 3);
+  if (ks >= 0 && ln.ecol < p.B)
+    e.dv = CK_AT(p.drives_t, (size_t)ks * p.B + ln.ecol, (size_t)p.n_in * p.B, 4);
+  return e;
+}
+
+// a = (W h)[row] + drive + bias;  h' = (1 - leak) h + leak tanh(a)
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& p, const Lanes& ln, int row,
+                                             float4 acc, const FwdEpi& e) {
+  if (!ln.eok) return;
+  const int c = ln.ecol;
+  const size_t off = (size_t)row * p.Bp + c;
+  const float a = pick4(acc, ln.slot) + e.dv + e.bi;
+  const float h = (1.0f - e.lam) * e.hp + e.lam * tanhf(a);
+  [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
+  CK_AT(p.h_next, off, NBp, 5) = h;
+  CK_AT(p.a_next, off, NBp, 6) = a;
+  if (p.out_t && c < p.B) CK_AT(p.out_t, (size_t)c * p.N + row, (size_t)p.B * p.N, 7) = h;
+}
+
 template <int L>
-__global__ __launch_bounds__(kThreads) void fwd_step(FwdArgs p) {
+__global__ __launch_bounds__(kThreads) CK_FWD_ATTR void fwd_step(FwdArgs p) {
   using G = Geom<L>;
   constexpr int P = G::P, I = G::I, EB = G::EB;
   __shared__ float4 red[kWaves][16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = lane / L, sub = lane % L;
-  const int col = blockIdx.y * kChunkCols + sub * 4;
-  const bool lane_ok = slot < P && col < p.Bp;
-  const int2 it = p.items[blockIdx.x];
-  const bool split = it.y < 0;
-  if (!split && wave >= it.y) return;
-  const int row = p.rows[it.x + (split ? 0 : wave)];
-  int kbeg = p.row_ptr[row], kend = p.row_ptr[row + 1];
-  if (split) {
-    const int n = kend - kbeg, per = (n + kWaves - 1) / kWaves;
-    kbeg = min(kend, kbeg + wave * per);
-    kend = min(kend, kbeg + per);
-  }
+  const Lanes ln = lanes<L>(p.Bp);
+  const int wave = __builtin_amdgcn_readfirstlane(ln.wave);
+  const int colc = ln.ok ? ln.col : 0;  // a valid address for lanes outside the loop
+  const int4* segs = p.segs + ((size_t)blockIdx.x * kWaves + wave) * p.K;
+  const float pf = prefetch_plane(p.h_prev, (uint32_t)p.N * (uint32_t)p.Bp * 4u);
+  int si = 0;
+  int4 d = seg_at(segs, p.K, 0);
+  const int first_info = d.w;
+  FwdEpi eo = fwd_epi_load(p, ln, (d.w & kInfoPieceBit) ? -1 : d.x);
+  int kb = d.y, kend = d.z;
+  int c = 0;
+  float w = 0.f;
+  if (d.x >= 0 && kb < kend) csr_batch(p.col_idx, p.v_csr, kb, kend, ln.lane, p.E, c, w);
   float4 acc = f4(0.f);
-  for (int kb = kbeg; kb < kend; kb += EB) {
-    const int nb = min(EB, kend - kb);
-    int c = 0;
-    float w = 0.f;
-    if (lane < nb) {
-      c = p.col_idx[kb + lane];
-      w = p.v_csr[kb + lane];
+  while (d.x >= 0) {
+    // the batch after this one: rest of this row, or the next segment
+    int nsi = si, nkb = kb + EB, nkend = kend;
+    int4 nd = d;
+    if (nkb >= kend) {
+      nsi = si + 1;
+      nd = seg_at(segs, p.K, nsi);
+      nkb = nd.y;
+      nkend = nd.z;
     }
+    int cn = 0;
+    float wn = 0.f;
+    if (nd.x >= 0 && nkb < nkend)
+      csr_batch(p.col_idx, p.v_csr, nkb, nkend, ln.lane, p.E, cn, wn);
+    FwdEpi en = eo;
+    if (nsi != si) en = fwd_epi_load(p, ln, (nd.w & kInfoPieceBit) ? -1 : nd.x);
+    if (kb < kend) {
+      float4 hv[I];
+      float wj[I];
 #pragma unroll
-    for (int j = 0; j < I; ++j) {
-      const int e = j * P + slot;
-      const int cj = __shfl(c, e);
-      const float wj = __shfl(w, e);
-      if (lane_ok && e < nb) {
-        const float4 hv = *reinterpret_cast<const float4*>(p.h_prev + (size_t)cj * p.Bp + col);
-        acc = fma4(wj, hv, acc);
+      for (int j = 0; j < I; ++j) {
+        const int e = j * P + ln.slot;
+        const int cj = __shfl(c, e);
+        wj[j] = __shfl(w, e);
+        hv[j] = ld4c(p.h_prev, ((uint32_t)cj * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
+                     (size_t)p.N * p.Bp, 11);
+      }
+#pragma unroll
+      for (int j = 0; j < I; ++j) {
+        const bool use = ln.ok && kb + j * P + ln.slot < kend;
+        acc = fma4(wj[j], use ? hv[j] : f4(0.f), acc);
       }
     }
+    if (nsi != si) {  // this batch closed segment si
+      acc = sum_slots<L>(acc, ln.sub);
+      if (d.w & kInfoPieceBit) {
+        if (ln.slot == 0) red[wave][ln.sub] = acc;
+      } else {
+        fwd_epilogue(p, ln, d.x, acc, eo);
+      }
+      acc = f4(0.f);
+      eo = en;
+    }
+    si = nsi;
+    d = nd;
+    kb = nkb;
+    kend = nkend;
+    c = cn;
+    w = wn;
   }
-  acc = sum_slots<L>(acc, sub);
-  if (split) {
-    if (slot == 0) red[wave][sub] = acc;
+  consume(pf);
+  if (first_info & kInfoGroupBit) {
+    // combine the pieces of this workgroup's split rows (fixed order)
     __syncthreads();
-    if (wave != 0) return;
-    acc = red[0][sub];
-#pragma unroll
-    for (int q = 1; q < kWaves; ++q) acc = add4(acc, red[q][sub]);
-  }
-  if (slot != 0 || !lane_ok) return;
-  // elementwise: drive, bias, tanh, leaky mix
-  const size_t off = (size_t)row * p.Bp + col;
-  const float4 hp = *reinterpret_cast<const float4*>(p.h_prev + off);
-  const float lam = p.leak[row], bi = p.bias[row];
-  float d[4] = {0.f, 0.f, 0.f, 0.f};
-  const int ks = p.input_slot[row];
-  if (ks >= 0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (col + q < p.B) d[q] = p.drives_t[(size_t)ks * p.B + col + q];
-  }
-  float4 a;
-  a.x = acc.x + d[0] + bi;
-  a.y = acc.y + d[1] + bi;
-  a.z = acc.z + d[2] + bi;
-  a.w = acc.w + d[3] + bi;
-  const float4 pr = tanh4(a);
-  const float om = 1.0f - lam;
-  float4 h;
-  h.x = om * hp.x + lam * pr.x;
-  h.y = om * hp.y + lam * pr.y;
-  h.z = om * hp.z + lam * pr.z;
-  h.w = om * hp.w + lam * pr.w;
-  *reinterpret_cast<float4*>(p.h_next + off) = h;
-  *reinterpret_cast<float4*>(p.a_next + off) = a;
-  if (p.out_t) {
-    const float hv[4] = {h.x, h.y, h.z, h.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (col + q < p.B) p.out_t[(size_t)(col + q) * p.N + row] = hv[q];
+    const int4 d0 = seg_at(segs, p.K, 0);
+    if (d0.x >= 0 && (d0.w & kInfoPieceBit) && (d0.w & 0xFF) == wave) {
+      const int np = (d0.w >> 8) & 0xFF;
+      float4 a = red[wave][ln.sub];
+      for (int q = 1; q < np; ++q) a = add4(a, red[wave + q][ln.sub]);
+      fwd_epilogue(p, ln, d0.x, a, fwd_epi_load(p, ln, d0.x));
+    }
   }
 }
 
 struct BwdArgs {
-  const int2* items;
-  const int32_t* rows;
-  const int32_t* t_row_ptr;
+  const int4* segs;       // schedule of the transposed CSR: K segments per wave
+  int K;
   const int32_t* t_col_idx;
   const float* v_csc;
   float* gv_csc;          // [chunks][E] transposed-CSR order, one row per column chunk
@@ -256,138 +444,176 @@ struct BwdArgs {
   float* gstate0;         // [B][N], written when s-1 == 0
   int first_k1;           // 1: overwrite gleak/gbias instead of accumulating
   int first_gv;           // 1: overwrite gv_csc instead of accumulating
-  int N, B, Bp, E;
+  int N, B, Bp, E, n_in;
 };
 
+// Row operands of the backward epilogue (this lane's column).
+struct BwdEpi {
+  float lam, gold, gin, ak, qk;
+  int ks;
+};
+
+__device__ __forceinline__ BwdEpi bwd_epi_load(const BwdArgs& p, const Lanes& ln, int row) {
+  BwdEpi e{0.f, 0.f, 0.f, 0.f, 0.f, -1};
+  if (row < 0 || !ln.eok) return e;
+  const int c = ln.ecol;
+  const size_t off = (size_t)row * p.Bp + c;
+  [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
+  e.lam = CK_AT(p.leak, row, p.N, 1);
+  if (p.ga_in != nullptr) e.gold = CK_AT(p.gh, off, NBp, 12);
+  if (c < p.B) {
+    if (p.G_t) e.gin = CK_AT(p.G_t, (size_t)c * p.N + row, (size_t)p.B * p.N, 13);
+    if (p.a_k1 != nullptr) {
+      e.ak = CK_AT(p.a_k1, off, NBp, 14);
+      e.qk = CK_AT(p.h_k1, off, NBp, 15);
+      e.ks = CK_AT(p.input_slot, row, p.N, 3);
+    }
+  }
+  return e;
+}
+
+// g^(s-1) = (1 - leak) g^(s) + (W^T ga^(s))[row] (+ G entering at s-1), then the
+// elementwise pass of microstep s-1 (leak/bias row reductions, drive gradient),
+// or the initial-state gradient when s-1 == 0.
 template <int L>
-__global__ __launch_bounds__(kThreads) void bwd_step(BwdArgs p) {
+__device__ __forceinline__ void bwd_epilogue(const BwdArgs& p, const Lanes& ln, int row,
+                                             float4 acc, const BwdEpi& e) {
+  const int c = ln.ecol;
+  const size_t off = (size_t)row * p.Bp + (ln.eok ? c : 0);
+  const bool real_col = ln.eok && c < p.B;
+  float g = pick4(acc, ln.slot);
+  if (p.ga_in != nullptr) g = fmaf(1.0f - e.lam, e.gold, g);
+  if (p.G_t && real_col) g += e.gin;
+  if (p.a_k1 == nullptr) {
+    if (real_col) CK_AT(p.gstate0, (size_t)c * p.N + row, (size_t)p.B * p.N, 16) = g;
+    return;
+  }
+  float lsum = 0.f, bsum = 0.f;
+  if (ln.eok) {
+    float ga = 0.f;
+    if (real_col) {
+      lsum = g * (tanhf(e.ak) - e.qk);
+      ga = g * e.lam * sech2f(e.ak);
+      bsum = ga;
+      if (e.ks >= 0) CK_AT(p.gdrives_t, (size_t)e.ks * p.B + c, (size_t)p.n_in * p.B, 17) += ga;
+    } else {
+      g = 0.f;
+    }
+    CK_AT(p.gh, off, (size_t)p.N * p.Bp, 18) = g;
+    CK_AT(p.ga_out, off, (size_t)p.N * p.Bp, 19) = ga;
+  }
+  lsum = epilogue_sum<L>(lsum, ln.slot);
+  bsum = epilogue_sum<L>(bsum, ln.slot);
+  if (ln.lane == 0) {
+    float& gl = CK_AT(p.gleak + (size_t)blockIdx.y * p.N, row, p.N, 20);
+    float& gb = CK_AT(p.gbias + (size_t)blockIdx.y * p.N, row, p.N, 20);
+    gl = p.first_k1 ? lsum : gl + lsum;
+    gb = p.first_k1 ? bsum : gb + bsum;
+  }
+}
+
+template <int L>
+__global__ __launch_bounds__(kThreads) CK_BWD_ATTR void bwd_step(BwdArgs p) {
   using G = Geom<L>;
   constexpr int P = G::P, I = G::I, EB = G::EB;
   __shared__ float4 red[kWaves][16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = lane / L, sub = lane % L;
-  const int col = blockIdx.y * kChunkCols + sub * 4;
-  const bool lane_ok = slot < P && col < p.Bp;
-  const int2 it = p.items[blockIdx.x];
-  const bool split = it.y < 0;
-  if (!split && wave >= it.y) return;
-  const int row = p.rows[it.x + (split ? 0 : wave)];
+  const Lanes ln = lanes<L>(p.Bp);
+  const int wave = __builtin_amdgcn_readfirstlane(ln.wave);
+  const int colc = ln.ok ? ln.col : 0;
+  const int4* segs = p.segs + ((size_t)blockIdx.x * kWaves + wave) * p.K;
+  const bool edges = p.ga_in != nullptr;
+  const float pf = edges ? prefetch_plane(p.ga_in, (uint32_t)p.N * (uint32_t)p.Bp * 4u) : 0.f;
+  float* gv = p.gv_csc + (size_t)blockIdx.y * p.E;
+  // this lane keeps the edge term of edge sub * P + slot of each batch
+  const int emine = ln.sub * P + ln.slot;
+  const bool keeps = ln.slot < P && ln.sub < I;
+  int si = 0;
+  int4 d = seg_at(segs, p.K, 0);
+  const int first_info = d.w;
+  BwdEpi eo = bwd_epi_load(p, ln, (d.w & kInfoPieceBit) ? -1 : d.x);
+  int kb = d.y, kend = edges ? d.z : d.y;
+  int c = 0;
+  float w = 0.f, gold = 0.f;
+  float4 hj = f4(0.f);
+  if (d.x >= 0 && kb < kend) {
+    csr_batch(p.t_col_idx, p.v_csc, kb, kend, ln.lane, p.E, c, w);
+    if (!p.first_gv) gold = CK_AT(gv, min(kb + emine, kend - 1), p.E, 21);
+    hj = ld4c(p.h_sm1, ((uint32_t)d.x * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
+              (size_t)p.N * p.Bp, 23);
+  }
   float4 acc = f4(0.f);
-  if (p.ga_in != nullptr) {
-    int kbeg = p.t_row_ptr[row], kend = p.t_row_ptr[row + 1];
-    if (split) {
-      const int n = kend - kbeg, per = (n + kWaves - 1) / kWaves;
-      kbeg = min(kend, kbeg + wave * per);
-      kend = min(kend, kbeg + per);
+  while (d.x >= 0) {
+    int nsi = si, nkb = kb + EB, nkend = kend;
+    int4 nd = d;
+    if (nkb >= kend) {
+      nsi = si + 1;
+      nd = seg_at(segs, p.K, nsi);
+      nkb = nd.y;
+      nkend = edges ? nd.z : nd.y;
     }
-    const float4 hj = lane_ok ? *reinterpret_cast<const float4*>(p.h_sm1 + (size_t)row * p.Bp + col)
-                              : f4(0.f);
-    for (int kb = kbeg; kb < kend; kb += EB) {
-      const int nb = min(EB, kend - kb);
-      int c = 0;
-      float w = 0.f;
-      if (lane < nb) {
-        c = p.t_col_idx[kb + lane];
-        w = p.v_csc[kb + lane];
-      }
-      float mine = 0.f;  // edge-gradient term kept by this lane: edge kb + sub*P + slot
+    int cn = 0;
+    float wn = 0.f, goldn = 0.f;
+    float4 hjn = hj;
+    if (nd.x >= 0 && nkb < nkend) {
+      csr_batch(p.t_col_idx, p.v_csc, nkb, nkend, ln.lane, p.E, cn, wn);
+      if (!p.first_gv) goldn = CK_AT(gv, min(nkb + emine, nkend - 1), p.E, 21);
+      if (nsi != si)
+        hjn = ld4c(p.h_sm1, ((uint32_t)nd.x * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
+                   (size_t)p.N * p.Bp, 23);
+    }
+    BwdEpi en = eo;
+    if (nsi != si) en = bwd_epi_load(p, ln, (nd.w & kInfoPieceBit) ? -1 : nd.x);
+    if (kb < kend) {
+      float4 gav[I];
+      float wj[I];
 #pragma unroll
       for (int j = 0; j < I; ++j) {
-        const int e = j * P + slot;
+        const int e = j * P + ln.slot;
         const int cj = __shfl(c, e);
-        const float wj = __shfl(w, e);
-        float part = 0.f;
-        if (lane_ok && e < nb) {
-          const float4 gv = *reinterpret_cast<const float4*>(p.ga_in + (size_t)cj * p.Bp + col);
-          acc = fma4(wj, gv, acc);
-          part = dot4(gv, hj);
-        }
-        const float tot = sum_in_slot<L>(part, slot);
-        if (sub == j) mine = tot;
+        wj[j] = __shfl(w, e);
+        gav[j] = ld4c(p.ga_in, ((uint32_t)cj * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
+                      (size_t)p.N * p.Bp, 24);
       }
-      if (slot < P && sub < I) {
-        const int e = sub * P + slot;
-        if (e < nb) {
-          float* dst = p.gv_csc + (size_t)blockIdx.y * p.E + kb + e;
-          *dst = p.first_gv ? mine : *dst + mine;
-        }
+      float mine = 0.f;
+#pragma unroll
+      for (int j = 0; j < I; ++j) {
+        const bool use = ln.ok && kb + j * P + ln.slot < kend;
+        const float4 g4 = use ? gav[j] : f4(0.f);
+        acc = fma4(wj[j], g4, acc);
+        const float tot = slot_sum<L>(dot4(g4, hj), ln.slot);
+        if (ln.sub == j) mine = tot;
       }
+      if (keeps && kb + emine < kend) CK_AT(gv, kb + emine, p.E, 22) = gold + mine;
     }
-    acc = sum_slots<L>(acc, sub);
-    if (split) {
-      if (slot == 0) red[wave][sub] = acc;
-      __syncthreads();
-      if (wave != 0) return;
-      acc = red[0][sub];
-#pragma unroll
-      for (int q = 1; q < kWaves; ++q) acc = add4(acc, red[q][sub]);
-    }
-  } else if (split && wave != 0) {
-    return;
-  }
-  if (slot != 0) return;
-  // g^(s-1)[row, cols] = (1 - leak) g^(s) + W^T ga^(s) (+ G entering at s-1)
-  const size_t off = (size_t)row * p.Bp + col;
-  const float lam = p.leak[row];
-  float4 g = acc;
-  if (p.ga_in != nullptr && lane_ok) {
-    const float4 go = *reinterpret_cast<const float4*>(p.gh + off);
-    const float om = 1.0f - lam;
-    g.x = fmaf(om, go.x, acc.x);
-    g.y = fmaf(om, go.y, acc.y);
-    g.z = fmaf(om, go.z, acc.z);
-    g.w = fmaf(om, go.w, acc.w);
-  }
-  float gg[4] = {g.x, g.y, g.z, g.w};
-  if (p.G_t) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (lane_ok && col + q < p.B) gg[q] += p.G_t[(size_t)(col + q) * p.N + row];
-  }
-  if (p.a_k1 == nullptr) {  // s - 1 == 0: gradient of the initial state
-    if (lane_ok) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (col + q < p.B) p.gstate0[(size_t)(col + q) * p.N + row] = gg[q];
-    }
-    return;
-  }
-  // elementwise pass of microstep s-1 on this node
-  float lsum = 0.f, bsum = 0.f;
-  float ga[4] = {0.f, 0.f, 0.f, 0.f};
-  if (lane_ok) {
-    const float4 a4 = *reinterpret_cast<const float4*>(p.a_k1 + off);
-    const float4 q4 = *reinterpret_cast<const float4*>(p.h_k1 + off);
-    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-    const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (col + q < p.B) {
-        const float pr = tanhf(av[q]);
-        lsum += gg[q] * (pr - qv[q]);
-        ga[q] = gg[q] * lam * sech2f(av[q]);
-        bsum += ga[q];
+    if (nsi != si) {
+      acc = sum_slots<L>(acc, ln.sub);
+      if (d.w & kInfoPieceBit) {
+        if (ln.slot == 0) red[wave][ln.sub] = acc;
       } else {
-        gg[q] = 0.f;
+        bwd_epilogue<L>(p, ln, d.x, acc, eo);
       }
+      acc = f4(0.f);
+      eo = en;
     }
-    *reinterpret_cast<float4*>(p.gh + off) = make_float4(gg[0], gg[1], gg[2], gg[3]);
-    *reinterpret_cast<float4*>(p.ga_out + off) = make_float4(ga[0], ga[1], ga[2], ga[3]);
-    const int ks = p.input_slot[row];
-    if (ks >= 0) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (col + q < p.B) p.gdrives_t[(size_t)ks * p.B + col + q] += ga[q];
-    }
+    si = nsi;
+    d = nd;
+    kb = nkb;
+    kend = nkend;
+    c = cn;
+    w = wn;
+    gold = goldn;
+    hj = hjn;
   }
-  // per-node leak and bias reductions over the batch (the lanes of slot 0)
-  lsum = sum_in_slot<L>(lsum, 0);
-  bsum = sum_in_slot<L>(bsum, 0);
-  if (sub == 0) {
-    float* gl = p.gleak + (size_t)blockIdx.y * p.N + row;
-    float* gb = p.gbias + (size_t)blockIdx.y * p.N + row;
-    *gl = p.first_k1 ? lsum : *gl + lsum;
-    *gb = p.first_k1 ? bsum : *gb + bsum;
+  consume(pf);
+  if (first_info & kInfoGroupBit) {
+    __syncthreads();
+    const int4 d0 = seg_at(segs, p.K, 0);
+    if (d0.x >= 0 && (d0.w & kInfoPieceBit) && (d0.w & 0xFF) == wave) {
+      const int np = (d0.w >> 8) & 0xFF;
+      float4 a = red[wave][ln.sub];
+      for (int q = 1; q < np; ++q) a = add4(a, red[wave + q][ln.sub]);
+      bwd_epilogue<L>(p, ln, d0.x, a, bwd_epi_load(p, ln, d0.x));
+    }
   }
 }
 
@@ -481,7 +707,7 @@ ck_status make_dims(const ck_graph* g, int64_t T, int64_t B, int64_t M, Dims* d)
     return CK_ERR_BAD_SIZE;
   }
   const int64_t Bp = (B + 3) / 4 * 4;
-  if (B >= (1LL << 30) || (g->N * Bp) >= (1LL << 31) || T * M >= (1LL << 31) ||
+  if (B >= (1LL << 30) || (g->N * Bp) >= (1LL << 30) || T * M >= (1LL << 31) ||
       T * B * g->N >= (1LL << 62) / 8) {
     set_error("sizes overflow 32-bit indexing: N=%lld B=%lld T=%lld M=%lld", (long long)g->N,
               (long long)B, (long long)T, (long long)M);
@@ -550,11 +776,10 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
   to_node_major<<<grid1((int64_t)d.plane), 256, 0, stream>>>(state0, (int)d.N, (int)d.B,
                                                              (int)d.Bp, h0);
   const FwdFn kern = KT::fwd[d.L - 1];
-  const dim3 grid(g->fwd.num_items, d.chunks);
+  const dim3 grid(g->fwd.num_wgs, d.chunks);
   FwdArgs a{};
-  a.items = g->fwd.items;
-  a.rows = g->fwd.rows;
-  a.row_ptr = g->row_ptr;
+  a.segs = g->fwd.segs;
+  a.K = g->fwd.K;
   a.col_idx = g->col_idx;
   a.v_csr = v_csr;
   a.leak = leak;
@@ -563,6 +788,8 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
   a.N = (int)d.N;
   a.B = (int)d.B;
   a.Bp = (int)d.Bp;
+  a.E = (int)d.E;
+  a.n_in = (int)d.n_in;
   for (int64_t s = 1; s <= d.S; ++s) {
     const int64_t t = (s - 1) / d.M;
     a.drives_t = d.n_in > 0 ? drives + (size_t)t * d.n_in * d.B : nullptr;
@@ -575,6 +802,21 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
     if (rc != CK_OK) return rc;
   }
   CK_HIP_TRY(hipGetLastError());
+#ifdef CK_CHECKED
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  CK_HIP_TRY(hipStreamIsCapturing(stream, &cap));
+  if (cap == hipStreamCaptureStatusNone) {
+    CK_HIP_TRY(hipStreamSynchronize(stream));
+    unsigned flag = 0;
+    CK_HIP_TRY(hipMemcpyFromSymbol(&flag, HIP_SYMBOL(g_ck_err), sizeof(unsigned)));
+    if (flag) {
+      const unsigned zero = 0;
+      (void)hipMemcpyToSymbol(HIP_SYMBOL(g_ck_err), &zero, sizeof(unsigned));
+      set_error("bounds check failed in %s: site mask 0x%x", "forward", flag);
+      return CK_ERR_HIP;
+    }
+  }
+#endif
   return CK_OK;
 }
 
@@ -619,11 +861,10 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
   if (d.n_in > 0)
     zero_f32<<<grid1(d.T * d.n_in * d.B), 256, 0, stream>>>(grad_drives, d.T * d.n_in * d.B);
   const BwdFn kern = KT::bwd[d.L - 1];
-  const dim3 grid(g->bwd.num_items, d.chunks);
+  const dim3 grid(g->bwd.num_wgs, d.chunks);
   BwdArgs a{};
-  a.items = g->bwd.items;
-  a.rows = g->bwd.rows;
-  a.t_row_ptr = g->t_row_ptr;
+  a.segs = g->bwd.segs;
+  a.K = g->bwd.K;
   a.t_col_idx = g->t_col_idx;
   a.v_csc = v_csc;
   a.gv_csc = gv_csc;
@@ -638,6 +879,7 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
   a.B = (int)d.B;
   a.Bp = (int)d.Bp;
   a.E = (int)d.E;
+  a.n_in = (int)d.n_in;
   // Launch "s" covers the edge pass of microstep s and the elementwise pass of
   // microstep s-1; launch S+1 has no edge pass and seeds g^(S) = G[T-1].
   for (int64_t s = d.S + 1; s >= 1; --s) {
@@ -671,6 +913,21 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
     scatter_sum_f32<<<grid1(d.E), 256, 0, stream>>>(gv_csc, d.chunks, g->t_perm, d.E,
                                                     grad_edge_values);
   CK_HIP_TRY(hipGetLastError());
+#ifdef CK_CHECKED
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  CK_HIP_TRY(hipStreamIsCapturing(stream, &cap));
+  if (cap == hipStreamCaptureStatusNone) {
+    CK_HIP_TRY(hipStreamSynchronize(stream));
+    unsigned flag = 0;
+    CK_HIP_TRY(hipMemcpyFromSymbol(&flag, HIP_SYMBOL(g_ck_err), sizeof(unsigned)));
+    if (flag) {
+      const unsigned zero = 0;
+      (void)hipMemcpyToSymbol(HIP_SYMBOL(g_ck_err), &zero, sizeof(unsigned));
+      set_error("bounds check failed in %s: site mask 0x%x", "backward", flag);
+      return CK_ERR_HIP;
+    }
+  }
+#endif
   return CK_OK;
 }
 
@@ -684,6 +941,8 @@ extern "C" ck_status ck_profile_collect(double* fwd_ms, int64_t* fwd_launches, d
                                         int64_t* bwd_launches) {
   clear_error();
   ck_status rc = CK_OK;
+  // the events carry no fence of their own: wait for all recorded work first
+  if (!g_profile.fwd.empty() || !g_profile.bwd.empty()) CK_HIP_TRY(hipDeviceSynchronize());
   auto drain = [&](std::vector<std::pair<hipEvent_t, hipEvent_t>>& log, double* ms,
                    int64_t* n) {
     double total = 0.0;

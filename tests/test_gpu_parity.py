@@ -255,3 +255,48 @@ def test_workspace_too_small_is_rejected():
         sgr.recurrence_forward(g, to_dev(w.edge_values), to_dev(w.leak), to_dev(w.bias),
                                to_dev(w.drives), to_dev(w.state0), w.microsteps, workspace=small)
     assert ei.value.status == 6
+
+
+def test_hip_graph_replay_matches_eager():
+    """Forward+backward captured into a HIP graph (torch.cuda.CUDAGraph on the
+    library's stream) and replayed several times, with eager work and
+    synchronisation between replays: every replay equals the eager result."""
+    w = synthetic.make("edge_cases", T=4)
+    log("HIP graph replay vs eager: edge-cases workload, T=4")
+    g = make_graph(w)
+    ev, lk, bs, dr, st, G = (to_dev(x) for x in (w.edge_values, w.leak, w.bias, w.drives,
+                                                  w.state0, w.grad_out))
+    sb, wb = sgr.recurrence_sizes(g, w.T, w.B, w.microsteps)
+    out = torch.empty((w.T, w.B, w.num_nodes), dtype=torch.float32, device="cuda")
+    saved = torch.empty(sb, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(wb, dtype=torch.uint8, device="cuda")
+    f = dict(dtype=torch.float32, device="cuda")
+    grads = {"g_edge_values": torch.empty(w.num_edges, **f), "g_leak": torch.empty(w.num_nodes, **f),
+             "g_bias": torch.empty(w.num_nodes, **f), "g_drives": torch.empty(tuple(w.drives.shape), **f),
+             "g_state0": torch.empty(tuple(w.state0.shape), **f)}
+
+    def step():
+        sgr.recurrence_forward(g, ev, lk, bs, dr, st, w.microsteps, out=out, saved=saved, workspace=ws)
+        sgr.recurrence_backward(g, ev, lk, st, w.microsteps, saved, G, workspace=ws, grads=grads)
+
+    step()
+    torch.cuda.synchronize()
+    eager = {"out": out.cpu().numpy().copy(), **{k: v.cpu().numpy().copy() for k, v in grads.items()}}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg):
+        step()
+    for r in range(4):
+        out.fill_(7.0)
+        for v in grads.values():
+            v.fill_(-3.0)
+        torch.cuda.synchronize()
+        cg.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy(), eager["out"], err_msg=f"replay {r} out")
+        for k, v in grads.items():
+            np.testing.assert_array_equal(v.cpu().numpy(), eager[k], err_msg=f"replay {r} {k}")
