@@ -32,20 +32,27 @@ constexpr int kWgsPerCu = CK_WGS_PER_CU;
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X.
 constexpr int kXcds = 8;
 
-// Row schedule of one orientation of the graph.  Wave v (= workgroup * kWaves
-// + wave index) walks its segments segs[v * K .. v * K + K) in order until a
-// segment with row < 0.  Segment = {row, kbeg, kend, info}: the edges
-// [kbeg, kend) of the row's compressed list.
+// Row schedule of one orientation of the graph, as edge batches.  Wave v
+// (= workgroup * kWaves + wave index) walks batches[v * KB .. v * KB + KB) in
+// order until an entry with row < 0.  Entry = {row, kbeg, count, info}: edges
+// [kbeg, kbeg + count) (count <= kBatchEdges) of the row's compressed list.
+// A row is one or more consecutive batches of one wave ("segment"), or pieces
+// on several waves of one workgroup (split row).
 //   info bits 0..7: for a piece of a split row, the wave (inside the
 //   workgroup) that combines the pieces; bits 8..15: number of pieces;
 //   bit 16: the workgroup holds split rows (all its waves synchronise once at
-//   the end); bit 17: this segment is a piece (always a wave's first segment).
+//   the end); bit 17: this batch belongs to a piece (always a wave's first
+//   segment); bit 18: first batch of its segment; bit 19: last batch of its
+//   segment (the row, or the piece, is complete after it).
+constexpr int kBatchEdges = 64;
 constexpr int kInfoGroupBit = 1 << 16;
 constexpr int kInfoPieceBit = 1 << 17;
+constexpr int kInfoFirstBit = 1 << 18;
+constexpr int kInfoLastBit = 1 << 19;
 struct Schedule {
-  int4* segs = nullptr;  // [num_wgs * kWaves * K]
+  int4* batches = nullptr;  // [num_wgs * kWaves * KB]
   int num_wgs = 0;
-  int K = 0;             // segments per wave (padded with row = -1)
+  int KB = 0;               // batch entries per wave (padded with row = -1)
 };
 
 }  // namespace ckhip

@@ -353,27 +353,49 @@ ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, int num_cus
       K = std::max(K, waves[v].size());
     }
   }
+  // segments -> batches of at most kBatchEdges edges
+  auto batches_of = [](const std::vector<Seg>& lst, std::vector<int4>& outb) {
+    for (const Seg& sg : lst) {
+      const int n = sg.ke - sg.kb;
+      const int nb = std::max(1, (n + kBatchEdges - 1) / kBatchEdges);
+      for (int b = 0; b < nb; ++b) {
+        const int kb = sg.kb + b * kBatchEdges;
+        const int cnt = std::min(kBatchEdges, sg.ke - kb);
+        int info = sg.info;
+        if (b == 0) info |= kInfoFirstBit;
+        if (b == nb - 1) info |= kInfoLastBit;
+        outb.push_back(make_int4(sg.row, kb, std::max(cnt, 0), info));
+      }
+    }
+  };
+  std::vector<std::vector<std::vector<int4>>> bl(kXcds, std::vector<std::vector<int4>>(waves_x));
+  size_t KB = 1;
+  for (int x = 0; x < kXcds; ++x)
+    for (int v = 0; v < waves_x; ++v) {
+      batches_of(lists[x][v], bl[x][v]);
+      KB = std::max(KB, bl[x][v].size());
+    }
+  (void)K;
   const int num_wgs = wg_x * kXcds;
-  std::vector<int4> segs((size_t)num_wgs * kWaves * K, make_int4(-1, 0, 0, 0));
+  std::vector<int4> tab((size_t)num_wgs * kWaves * KB, make_int4(-1, 0, 0, 0));
   for (int x = 0; x < kXcds; ++x)
     for (int v = 0; v < waves_x; ++v) {
       const int wgl = v / kWaves, wv = v % kWaves;
-      const size_t gv = ((size_t)(wgl * kXcds + x) * kWaves + wv) * K;
-      const auto& lst = lists[x][v];
-      for (size_t k = 0; k < lst.size(); ++k)
-        segs[gv + k] = make_int4(lst[k].row, lst[k].kb, lst[k].ke, lst[k].info);
+      const size_t gv = ((size_t)(wgl * kXcds + x) * kWaves + wv) * KB;
+      const auto& lst = bl[x][v];
+      std::copy(lst.begin(), lst.end(), tab.begin() + gv);
       // an empty wave of a workgroup with split rows must still reach its barrier
       if (lst.empty()) {
         bool grp = false;
         for (int q = 0; q < kWaves; ++q)
           for (auto& sg : lists[x][wgl * kWaves + q]) grp |= (sg.info & kInfoGroupBit) != 0;
-        if (grp) segs[gv] = make_int4(-1, 0, 0, kInfoGroupBit);
+        if (grp) tab[gv] = make_int4(-1, 0, 0, kInfoGroupBit);
       }
     }
   out->num_wgs = num_wgs;
-  out->K = (int)K;
-  CK_HIP_TRY(hipMalloc(&out->segs, segs.size() * sizeof(int4)));
-  CK_HIP_TRY(hipMemcpy(out->segs, segs.data(), segs.size() * sizeof(int4), hipMemcpyHostToDevice));
+  out->KB = (int)KB;
+  CK_HIP_TRY(hipMalloc(&out->batches, tab.size() * sizeof(int4)));
+  CK_HIP_TRY(hipMemcpy(out->batches, tab.data(), tab.size() * sizeof(int4), hipMemcpyHostToDevice));
   return CK_OK;
 }
 
@@ -381,8 +403,8 @@ void free_graph_arrays(ck_graph* g) {
   int32_t* arrs[] = {g->row_ptr, g->col_idx, g->perm, g->t_row_ptr, g->t_col_idx, g->t_perm,
                      g->input_slot};
   for (int32_t* p : arrs) (void)hipFree(p);
-  (void)hipFree(g->fwd.segs);
-  (void)hipFree(g->bwd.segs);
+  (void)hipFree(g->fwd.batches);
+  (void)hipFree(g->bwd.batches);
 }
 
 }  // namespace

@@ -75,7 +75,9 @@ constexpr int kChunkCols = 64;  // columns per grid-y chunk when Bp > 64
 #if CK_BWD_OCC > 0
 #define CK_BWD_ATTR __attribute__((amdgpu_waves_per_eu(CK_BWD_OCC)))
 #else
-#define CK_BWD_ATTR
+// two 8-wave workgroups per CU (at most 128 VGPRs) for power-of-two row widths
+// up to 32 columns; the schedule is sized for that
+#define CK_BWD_ATTR __attribute__((amdgpu_waves_per_eu((L <= 8 && is_pow2(L)) ? 4 : 1)))
 #endif
 
 __device__ __forceinline__ float4 f4(float x) { return make_float4(x, x, x, x); }
@@ -276,24 +278,35 @@ __device__ __forceinline__ float prefetch_plane(const float* plane, uint32_t byt
 
 __device__ __forceinline__ void consume(float x) { asm volatile("" ::"v"(x)); }
 
-// Edge indices and values of one batch (lane k: edge kb + k, clamped to the
-// row; lanes past the end get value 0).
-__device__ __forceinline__ void csr_batch(const int32_t* __restrict__ idx,
-                                          const float* __restrict__ val, int kb, int kend,
-                                          int lane, int E, int& c, float& w) {
-  const int e = kb + lane;
-  const int ec = min(e, kend - 1);
-  c = CK_AT(idx, ec, E, 8);
-  w = e < kend ? CK_AT(val, ec, E, 9) : 0.f;
+// A wave walks its schedule in groups of kGroup batch entries: the group's
+// entries arrive as one vector load (lane q holds entry q), then the edge
+// indices (and, backward, the old edge gradients) of all its batches are
+// requested at once, so one memory round trip covers up to kGroup * 64 edges
+// before the gathers start.
+constexpr int kGroup = 8;
+
+__device__ __forceinline__ int4 lane_entry(const int4& v, int q) {
+  return make_int4(__builtin_amdgcn_readlane(v.x, q), __builtin_amdgcn_readlane(v.y, q),
+                   __builtin_amdgcn_readlane(v.z, q), __builtin_amdgcn_readlane(v.w, q));
 }
 
-__device__ __forceinline__ int4 seg_at(const int4* __restrict__ segs, int K, int k) {
-  return k < K ? CK_AT(segs, k, K, 10) : make_int4(-1, 0, 0, 0);
+// Edge indices and values of one batch entry d: lane k holds edge d.y + k
+// (clamped into the batch; lanes past its end get value 0).
+__device__ __forceinline__ void batch_edges(const int4& d, const int32_t* __restrict__ idx,
+                                            const float* __restrict__ val, int lane, int E,
+                                            int& c, float& w) {
+  c = 0;
+  w = 0.f;
+  if (d.x >= 0 && d.z > 0) {
+    const int e = d.y + min(lane, d.z - 1);
+    c = CK_AT(idx, e, E, 8);
+    w = lane < d.z ? CK_AT(val, e, E, 9) : 0.f;
+  }
 }
 
 struct FwdArgs {
-  const int4* segs;       // schedule: K segments per wave
-  int K;
+  const int4* batches;    // schedule: KB batch entries per wave
+  int KB;
   const int32_t* col_idx;
   const float* v_csr;
   const float* leak;
@@ -343,76 +356,66 @@ template <int L>
 __global__ __launch_bounds__(kThreads) CK_FWD_ATTR void fwd_step(FwdArgs p) {
   using G = Geom<L>;
   constexpr int P = G::P, I = G::I, EB = G::EB;
+  constexpr int NSUB = (kBatchEdges + EB - 1) / EB;  // gather rounds per batch entry
   __shared__ float4 red[kWaves][16];
   const Lanes ln = lanes<L>(p.Bp);
   const int wave = __builtin_amdgcn_readfirstlane(ln.wave);
   const int colc = ln.ok ? ln.col : 0;  // a valid address for lanes outside the loop
-  const int4* segs = p.segs + ((size_t)blockIdx.x * kWaves + wave) * p.K;
+  const int4* bt = p.batches + ((size_t)blockIdx.x * kWaves + wave) * p.KB;
   const float pf = prefetch_plane(p.h_prev, (uint32_t)p.N * (uint32_t)p.Bp * 4u);
-  int si = 0;
-  int4 d = seg_at(segs, p.K, 0);
-  const int first_info = d.w;
-  FwdEpi eo = fwd_epi_load(p, ln, (d.w & kInfoPieceBit) ? -1 : d.x);
-  int kb = d.y, kend = d.z;
-  int c = 0;
-  float w = 0.f;
-  if (d.x >= 0 && kb < kend) csr_batch(p.col_idx, p.v_csr, kb, kend, ln.lane, p.E, c, w);
+  const int4 idle = make_int4(-1, 0, 0, 0);
+  const int first_info = p.KB > 0 ? CK_AT(bt, 0, p.KB, 10).w : 0;
   float4 acc = f4(0.f);
-  while (d.x >= 0) {
-    // the batch after this one: rest of this row, or the next segment
-    int nsi = si, nkb = kb + EB, nkend = kend;
-    int4 nd = d;
-    if (nkb >= kend) {
-      nsi = si + 1;
-      nd = seg_at(segs, p.K, nsi);
-      nkb = nd.y;
-      nkend = nd.z;
-    }
-    int cn = 0;
-    float wn = 0.f;
-    if (nd.x >= 0 && nkb < nkend)
-      csr_batch(p.col_idx, p.v_csr, nkb, nkend, ln.lane, p.E, cn, wn);
-    FwdEpi en = eo;
-    if (nsi != si) en = fwd_epi_load(p, ln, (nd.w & kInfoPieceBit) ? -1 : nd.x);
-    if (kb < kend) {
-      float4 hv[I];
-      float wj[I];
+  FwdEpi eo{0.f, 0.f, 0.f, 0.f};
+  for (int g0 = 0; g0 < p.KB; g0 += kGroup) {
+    const int4 ent = (ln.lane < kGroup && g0 + ln.lane < p.KB) ? CK_AT(bt, g0 + ln.lane, p.KB, 10)
+                                                              : idle;
+    if (__builtin_amdgcn_readlane(ent.x, 0) < 0) break;
+    int cb[kGroup];
+    float wb[kGroup];
 #pragma unroll
-      for (int j = 0; j < I; ++j) {
-        const int e = j * P + ln.slot;
-        const int cj = __shfl(c, e);
-        wj[j] = __shfl(w, e);
-        hv[j] = ld4c(p.h_prev, ((uint32_t)cj * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
-                     (size_t)p.N * p.Bp, 11);
-      }
+    for (int q = 0; q < kGroup; ++q)
+      batch_edges(lane_entry(ent, q), p.col_idx, p.v_csr, ln.lane, p.E, cb[q], wb[q]);
 #pragma unroll
-      for (int j = 0; j < I; ++j) {
-        const bool use = ln.ok && kb + j * P + ln.slot < kend;
-        acc = fma4(wj[j], use ? hv[j] : f4(0.f), acc);
+    for (int q = 0; q < kGroup; ++q) {
+      const int4 d = lane_entry(ent, q);
+      if (d.x < 0) break;  // end of this wave's list (uniform)
+      if (d.w & kInfoFirstBit) eo = fwd_epi_load(p, ln, (d.w & kInfoPieceBit) ? -1 : d.x);
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) {
+        if (sb * EB >= d.z) break;  // no edges left in this batch (uniform)
+        float4 hv[I];
+        float wj[I];
+#pragma unroll
+        for (int j = 0; j < I; ++j) {
+          const int e = sb * EB + j * P + ln.slot;
+          const int cj = __shfl(cb[q], e);
+          wj[j] = __shfl(wb[q], e);
+          hv[j] = ld4c(p.h_prev, ((uint32_t)cj * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
+                       (size_t)p.N * p.Bp, 11);
+        }
+#pragma unroll
+        for (int j = 0; j < I; ++j) {
+          const bool use = ln.ok && sb * EB + j * P + ln.slot < d.z;
+          acc = fma4(wj[j], use ? hv[j] : f4(0.f), acc);
+        }
+      }
+      if (d.w & kInfoLastBit) {  // the row (or piece) is complete
+        acc = sum_slots<L>(acc, ln.sub);
+        if (d.w & kInfoPieceBit) {
+          if (ln.slot == 0) red[wave][ln.sub] = acc;
+        } else {
+          fwd_epilogue(p, ln, d.x, acc, eo);
+        }
+        acc = f4(0.f);
       }
     }
-    if (nsi != si) {  // this batch closed segment si
-      acc = sum_slots<L>(acc, ln.sub);
-      if (d.w & kInfoPieceBit) {
-        if (ln.slot == 0) red[wave][ln.sub] = acc;
-      } else {
-        fwd_epilogue(p, ln, d.x, acc, eo);
-      }
-      acc = f4(0.f);
-      eo = en;
-    }
-    si = nsi;
-    d = nd;
-    kb = nkb;
-    kend = nkend;
-    c = cn;
-    w = wn;
   }
   consume(pf);
   if (first_info & kInfoGroupBit) {
     // combine the pieces of this workgroup's split rows (fixed order)
     __syncthreads();
-    const int4 d0 = seg_at(segs, p.K, 0);
+    const int4 d0 = CK_AT(bt, 0, p.KB, 10);
     if (d0.x >= 0 && (d0.w & kInfoPieceBit) && (d0.w & 0xFF) == wave) {
       const int np = (d0.w >> 8) & 0xFF;
       float4 a = red[wave][ln.sub];
@@ -423,8 +426,8 @@ __global__ __launch_bounds__(kThreads) CK_FWD_ATTR void fwd_step(FwdArgs p) {
 }
 
 struct BwdArgs {
-  const int4* segs;       // schedule of the transposed CSR: K segments per wave
-  int K;
+  const int4* batches;    // schedule of the transposed CSR: KB batch entries per wave
+  int KB;
   const int32_t* t_col_idx;
   const float* v_csc;
   float* gv_csc;          // [chunks][E] transposed-CSR order, one row per column chunk
@@ -516,98 +519,94 @@ template <int L>
 __global__ __launch_bounds__(kThreads) CK_BWD_ATTR void bwd_step(BwdArgs p) {
   using G = Geom<L>;
   constexpr int P = G::P, I = G::I, EB = G::EB;
+  constexpr int NSUB = (kBatchEdges + EB - 1) / EB;
   __shared__ float4 red[kWaves][16];
   const Lanes ln = lanes<L>(p.Bp);
   const int wave = __builtin_amdgcn_readfirstlane(ln.wave);
   const int colc = ln.ok ? ln.col : 0;
-  const int4* segs = p.segs + ((size_t)blockIdx.x * kWaves + wave) * p.K;
+  const int4* bt = p.batches + ((size_t)blockIdx.x * kWaves + wave) * p.KB;
+  // the seeding launch (no ga_in) has no edge pass: every batch counts as empty
   const bool edges = p.ga_in != nullptr;
   const float pf = edges ? prefetch_plane(p.ga_in, (uint32_t)p.N * (uint32_t)p.Bp * 4u) : 0.f;
   float* gv = p.gv_csc + (size_t)blockIdx.y * p.E;
-  // this lane keeps the edge term of edge sub * P + slot of each batch
-  const int emine = ln.sub * P + ln.slot;
+  // in gather round (sb, j) slot q handles batch edge sb*EB + j*P + q; the
+  // edge term of round (sb, j = sub) is kept by lane (q, sub)
   const bool keeps = ln.slot < P && ln.sub < I;
-  int si = 0;
-  int4 d = seg_at(segs, p.K, 0);
-  const int first_info = d.w;
-  BwdEpi eo = bwd_epi_load(p, ln, (d.w & kInfoPieceBit) ? -1 : d.x);
-  int kb = d.y, kend = edges ? d.z : d.y;
-  int c = 0;
-  float w = 0.f, gold = 0.f;
-  float4 hj = f4(0.f);
-  if (d.x >= 0 && kb < kend) {
-    csr_batch(p.t_col_idx, p.v_csc, kb, kend, ln.lane, p.E, c, w);
-    if (!p.first_gv) gold = CK_AT(gv, min(kb + emine, kend - 1), p.E, 21);
-    hj = ld4c(p.h_sm1, ((uint32_t)d.x * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
-              (size_t)p.N * p.Bp, 23);
-  }
+  const int4 idle = make_int4(-1, 0, 0, 0);
+  const int first_info = p.KB > 0 ? CK_AT(bt, 0, p.KB, 10).w : 0;
   float4 acc = f4(0.f);
-  while (d.x >= 0) {
-    int nsi = si, nkb = kb + EB, nkend = kend;
-    int4 nd = d;
-    if (nkb >= kend) {
-      nsi = si + 1;
-      nd = seg_at(segs, p.K, nsi);
-      nkb = nd.y;
-      nkend = edges ? nd.z : nd.y;
-    }
-    int cn = 0;
-    float wn = 0.f, goldn = 0.f;
-    float4 hjn = hj;
-    if (nd.x >= 0 && nkb < nkend) {
-      csr_batch(p.t_col_idx, p.v_csc, nkb, nkend, ln.lane, p.E, cn, wn);
-      if (!p.first_gv) goldn = CK_AT(gv, min(nkb + emine, nkend - 1), p.E, 21);
-      if (nsi != si)
-        hjn = ld4c(p.h_sm1, ((uint32_t)nd.x * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
-                   (size_t)p.N * p.Bp, 23);
-    }
-    BwdEpi en = eo;
-    if (nsi != si) en = bwd_epi_load(p, ln, (nd.w & kInfoPieceBit) ? -1 : nd.x);
-    if (kb < kend) {
-      float4 gav[I];
-      float wj[I];
+  float4 hj = f4(0.f);
+  BwdEpi eo{0.f, 0.f, 0.f, 0.f, 0.f, -1};
+  for (int g0 = 0; g0 < p.KB; g0 += kGroup) {
+    int4 ent = (ln.lane < kGroup && g0 + ln.lane < p.KB) ? CK_AT(bt, g0 + ln.lane, p.KB, 10) : idle;
+    if (!edges) ent.z = 0;
+    if (__builtin_amdgcn_readlane(ent.x, 0) < 0) break;
+    int cb[kGroup];
+    float wb[kGroup], gb_old[kGroup][NSUB];
 #pragma unroll
-      for (int j = 0; j < I; ++j) {
-        const int e = j * P + ln.slot;
-        const int cj = __shfl(c, e);
-        wj[j] = __shfl(w, e);
-        gav[j] = ld4c(p.ga_in, ((uint32_t)cj * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
-                      (size_t)p.N * p.Bp, 24);
-      }
-      float mine = 0.f;
+    for (int q = 0; q < kGroup; ++q) {
+      const int4 d = lane_entry(ent, q);
+      batch_edges(d, p.t_col_idx, p.v_csc, ln.lane, p.E, cb[q], wb[q]);
 #pragma unroll
-      for (int j = 0; j < I; ++j) {
-        const bool use = ln.ok && kb + j * P + ln.slot < kend;
-        const float4 g4 = use ? gav[j] : f4(0.f);
-        acc = fma4(wj[j], g4, acc);
-        const float tot = slot_sum<L>(dot4(g4, hj), ln.slot);
-        if (ln.sub == j) mine = tot;
+      for (int sb = 0; sb < NSUB; ++sb) {
+        const int e = sb * EB + ln.sub * P + ln.slot;
+        gb_old[q][sb] = (d.x >= 0 && d.z > 0 && !p.first_gv)
+                            ? CK_AT(gv, d.y + min(e, d.z - 1), p.E, 21)
+                            : 0.f;
       }
-      if (keeps && kb + emine < kend) CK_AT(gv, kb + emine, p.E, 22) = gold + mine;
     }
-    if (nsi != si) {
-      acc = sum_slots<L>(acc, ln.sub);
-      if (d.w & kInfoPieceBit) {
-        if (ln.slot == 0) red[wave][ln.sub] = acc;
-      } else {
-        bwd_epilogue<L>(p, ln, d.x, acc, eo);
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      const int4 d = lane_entry(ent, q);
+      if (d.x < 0) break;  // end of this wave's list (uniform)
+      if (d.w & kInfoFirstBit) {
+        // the row's own h^(s-1) (edge dot products) and epilogue operands,
+        // requested before this batch's gathers so they arrive with them
+        if (d.z > 0)
+          hj = ld4c(p.h_sm1, ((uint32_t)d.x * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
+                    (size_t)p.N * p.Bp, 23);
+        eo = bwd_epi_load(p, ln, (d.w & kInfoPieceBit) ? -1 : d.x);
       }
-      acc = f4(0.f);
-      eo = en;
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) {
+        if (sb * EB >= d.z) break;  // no edges left in this batch (uniform)
+        float4 gav[I];
+        float wj[I];
+#pragma unroll
+        for (int j = 0; j < I; ++j) {
+          const int e = sb * EB + j * P + ln.slot;
+          const int cj = __shfl(cb[q], e);
+          wj[j] = __shfl(wb[q], e);
+          gav[j] = ld4c(p.ga_in, ((uint32_t)cj * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
+                        (size_t)p.N * p.Bp, 24);
+        }
+        float mine = 0.f;
+#pragma unroll
+        for (int j = 0; j < I; ++j) {
+          const bool use = ln.ok && sb * EB + j * P + ln.slot < d.z;
+          const float4 g4 = use ? gav[j] : f4(0.f);
+          acc = fma4(wj[j], g4, acc);
+          const float tot = slot_sum<L>(dot4(g4, hj), ln.slot);
+          if (ln.sub == j) mine = tot;
+        }
+        const int e = sb * EB + ln.sub * P + ln.slot;
+        if (keeps && e < d.z) CK_AT(gv, d.y + e, p.E, 22) = gb_old[q][sb] + mine;
+      }
+      if (d.w & kInfoLastBit) {
+        acc = sum_slots<L>(acc, ln.sub);
+        if (d.w & kInfoPieceBit) {
+          if (ln.slot == 0) red[wave][ln.sub] = acc;
+        } else {
+          bwd_epilogue<L>(p, ln, d.x, acc, eo);
+        }
+        acc = f4(0.f);
+      }
     }
-    si = nsi;
-    d = nd;
-    kb = nkb;
-    kend = nkend;
-    c = cn;
-    w = wn;
-    gold = goldn;
-    hj = hjn;
   }
   consume(pf);
   if (first_info & kInfoGroupBit) {
     __syncthreads();
-    const int4 d0 = seg_at(segs, p.K, 0);
+    const int4 d0 = CK_AT(bt, 0, p.KB, 10);
     if (d0.x >= 0 && (d0.w & kInfoPieceBit) && (d0.w & 0xFF) == wave) {
       const int np = (d0.w >> 8) & 0xFF;
       float4 a = red[wave][ln.sub];
@@ -778,8 +777,8 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
   const FwdFn kern = KT::fwd[d.L - 1];
   const dim3 grid(g->fwd.num_wgs, d.chunks);
   FwdArgs a{};
-  a.segs = g->fwd.segs;
-  a.K = g->fwd.K;
+  a.batches = g->fwd.batches;
+  a.KB = g->fwd.KB;
   a.col_idx = g->col_idx;
   a.v_csr = v_csr;
   a.leak = leak;
@@ -863,8 +862,8 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
   const BwdFn kern = KT::bwd[d.L - 1];
   const dim3 grid(g->bwd.num_wgs, d.chunks);
   BwdArgs a{};
-  a.segs = g->bwd.segs;
-  a.K = g->bwd.K;
+  a.batches = g->bwd.batches;
+  a.KB = g->bwd.KB;
   a.t_col_idx = g->t_col_idx;
   a.v_csc = v_csc;
   a.gv_csc = gv_csc;
