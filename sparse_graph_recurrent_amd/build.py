@@ -24,7 +24,7 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # keep the compiler from emitting packed-fp32 instructions

@@ -1,6 +1,6 @@
 // graph_build.hip -- ck_graph_create and friends: validation, CSR / transposed
-// CSR construction with a stable LSD radix sort, input-slot map and the
-// degree-balanced, XCD-aware row schedules.
+// CSR construction with a stable LSD radix sort, input-slot map and the upload
+// of the row schedules (planned in schedule.cpp).
 //
 // The graph is given as caller-ordered src/dst lists (connectome-kernels
 // README, "Use"); parameters stay in that order and the internal permutation is
@@ -10,7 +10,6 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
-#include <queue>
 #include <vector>
 
 #include "ck_internal.h"
@@ -267,135 +266,18 @@ ck_status build_compressed(const int64_t* major, const int64_t* minor, int64_t E
   return CK_OK;
 }
 
-// Degree-balanced, XCD-aware schedule (host side, from the row pointers).
-// The grid is sized for one resident round (kWgsPerCu workgroups per CU) and
-// every wave walks a list of row segments.  Rows are cut into kXcds
-// contiguous ranges of about equal cost (edges plus a per-row constant);
-// workgroup g runs on XCD g % kXcds and takes XCD-local workgroup g / kXcds.
-// Inside an XCD, rows above twice the per-wave share become pieces on consecutive
-// waves of one workgroup (combined through LDS at the end of the kernel),
-// then the remaining rows go heaviest first to the least-loaded wave.
-ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, int num_cus,
+// Upload the planned schedule of one orientation for `waves`-wave workgroups.
+ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, int num_cus, int waves,
                          Schedule* out) {
-  constexpr int64_t kRowCost = 16;
-  constexpr int64_t kMinWaveCost = 96;
-  std::vector<int64_t> deg(N);
-  int64_t total = 0;
-  for (int64_t i = 0; i < N; ++i) {
-    deg[i] = ptr[i + 1] - ptr[i];
-    total += deg[i] + kRowCost;
-  }
-  std::vector<int64_t> cut(kXcds + 1, N);
-  cut[0] = 0;
-  {
-    int64_t acc = 0;
-    int x = 1;
-    for (int64_t i = 0; i < N && x < kXcds; ++i) {
-      acc += deg[i] + kRowCost;
-      while (x < kXcds && acc * kXcds >= total * x) cut[x++] = i + 1;
-    }
-  }
-  // workgroups per XCD: one resident round, fewer for small graphs
-  const int64_t cap = std::max<int64_t>(1, (int64_t)num_cus / kXcds * kWgsPerCu);
-  const int64_t want = (total / kXcds + kMinWaveCost * kWaves - 1) / (kMinWaveCost * kWaves);
-  const int wg_x = (int)std::max<int64_t>(1, std::min(cap, want));
-  const int waves_x = wg_x * kWaves;
-  struct Seg {
-    int32_t row, kb, ke, info;
-  };
-  std::vector<std::vector<std::vector<Seg>>> lists(kXcds);
-  size_t K = 1;
-  for (int x = 0; x < kXcds; ++x) {
-    auto& waves = lists[x];
-    waves.assign(waves_x, {});
-    std::vector<int64_t> load(waves_x, 0);
-    std::vector<bool> wg_group(wg_x, false);
-    int64_t cost_x = 0;
-    for (int64_t i = cut[x]; i < cut[x + 1]; ++i) cost_x += deg[i] + kRowCost;
-    const int64_t share = std::max<int64_t>(kSplitEdges, cost_x / waves_x);
-    std::vector<int32_t> r;
-    for (int64_t i = cut[x]; i < cut[x + 1]; ++i) r.push_back((int32_t)i);
-    std::stable_sort(r.begin(), r.end(), [&](int32_t a, int32_t b) { return deg[a] > deg[b]; });
-    // split rows: pieces on consecutive, still piece-free waves of one workgroup
-    size_t j = 0;
-    int wg = 0, used = 0;
-    for (; j < r.size() && deg[r[j]] > 2 * share; ++j) {
-      const int64_t d = deg[r[j]];
-      const int np = (int)std::min<int64_t>(kWaves, (d + share - 1) / share);
-      if (used + np > kWaves) {
-        ++wg;
-        used = 0;
-      }
-      if (wg >= wg_x) break;  // no room left: the rest are whole rows
-      const int lead = used;
-      for (int q = 0; q < np; ++q) {
-        const int v = wg * kWaves + used++;
-        const int32_t kb = (int32_t)(ptr[r[j]] + d * q / np);
-        const int32_t ke = (int32_t)(ptr[r[j]] + d * (q + 1) / np);
-        waves[v].push_back({r[j], kb, ke, lead | (np << 8) | kInfoPieceBit});
-        load[v] += ke - kb + kRowCost;
-      }
-      wg_group[wg] = true;
-    }
-    // remaining rows: heaviest first to the least-loaded wave
-    using Entry = std::pair<int64_t, int>;
-    std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap;
-    for (int v = 0; v < waves_x; ++v) heap.push({load[v], v});
-    for (; j < r.size(); ++j) {
-      auto [l, v] = heap.top();
-      heap.pop();
-      waves[v].push_back({r[j], ptr[r[j]], ptr[r[j] + 1], 0});
-      heap.push({l + deg[r[j]] + kRowCost, v});
-    }
-    for (int v = 0; v < waves_x; ++v) {
-      if (wg_group[v / kWaves])
-        for (auto& sg : waves[v]) sg.info |= kInfoGroupBit;
-      K = std::max(K, waves[v].size());
-    }
-  }
-  // segments -> batches of at most kBatchEdges edges
-  auto batches_of = [](const std::vector<Seg>& lst, std::vector<int4>& outb) {
-    for (const Seg& sg : lst) {
-      const int n = sg.ke - sg.kb;
-      const int nb = std::max(1, (n + kBatchEdges - 1) / kBatchEdges);
-      for (int b = 0; b < nb; ++b) {
-        const int kb = sg.kb + b * kBatchEdges;
-        const int cnt = std::min(kBatchEdges, sg.ke - kb);
-        int info = sg.info;
-        if (b == 0) info |= kInfoFirstBit;
-        if (b == nb - 1) info |= kInfoLastBit;
-        outb.push_back(make_int4(sg.row, kb, std::max(cnt, 0), info));
-      }
-    }
-  };
-  std::vector<std::vector<std::vector<int4>>> bl(kXcds, std::vector<std::vector<int4>>(waves_x));
-  size_t KB = 1;
-  for (int x = 0; x < kXcds; ++x)
-    for (int v = 0; v < waves_x; ++v) {
-      batches_of(lists[x][v], bl[x][v]);
-      KB = std::max(KB, bl[x][v].size());
-    }
-  (void)K;
-  const int num_wgs = wg_x * kXcds;
-  std::vector<int4> tab((size_t)num_wgs * kWaves * KB, make_int4(-1, 0, 0, 0));
-  for (int x = 0; x < kXcds; ++x)
-    for (int v = 0; v < waves_x; ++v) {
-      const int wgl = v / kWaves, wv = v % kWaves;
-      const size_t gv = ((size_t)(wgl * kXcds + x) * kWaves + wv) * KB;
-      const auto& lst = bl[x][v];
-      std::copy(lst.begin(), lst.end(), tab.begin() + gv);
-      // an empty wave of a workgroup with split rows must still reach its barrier
-      if (lst.empty()) {
-        bool grp = false;
-        for (int q = 0; q < kWaves; ++q)
-          for (auto& sg : lists[x][wgl * kWaves + q]) grp |= (sg.info & kInfoGroupBit) != 0;
-        if (grp) tab[gv] = make_int4(-1, 0, 0, kInfoGroupBit);
-      }
-    }
-  out->num_wgs = num_wgs;
-  out->KB = (int)KB;
-  CK_HIP_TRY(hipMalloc(&out->batches, tab.size() * sizeof(int4)));
-  CK_HIP_TRY(hipMemcpy(out->batches, tab.data(), tab.size() * sizeof(int4), hipMemcpyHostToDevice));
+  static_assert(sizeof(BatchEntry) == sizeof(int4), "batch entries are read as int4");
+  SchedulePlan plan;
+  plan_schedule(ptr.data(), N, num_cus, waves, &plan);
+  out->num_wgs = plan.num_wgs;
+  out->waves = plan.waves;
+  out->KB = plan.KB;
+  const size_t bytes = plan.table.size() * sizeof(BatchEntry);
+  CK_HIP_TRY(hipMalloc(&out->batches, bytes));
+  CK_HIP_TRY(hipMemcpy(out->batches, plan.table.data(), bytes, hipMemcpyHostToDevice));
   return CK_OK;
 }
 
@@ -403,8 +285,10 @@ void free_graph_arrays(ck_graph* g) {
   int32_t* arrs[] = {g->row_ptr, g->col_idx, g->perm, g->t_row_ptr, g->t_col_idx, g->t_perm,
                      g->input_slot};
   for (int32_t* p : arrs) (void)hipFree(p);
-  (void)hipFree(g->fwd.batches);
-  (void)hipFree(g->bwd.batches);
+  for (int k = 0; k < 2; ++k) {
+    (void)hipFree(g->fwd[k].batches);
+    (void)hipFree(g->bwd[k].batches);
+  }
 }
 
 }  // namespace
@@ -507,10 +391,13 @@ extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int
     if (hipGetDeviceProperties(&prop, g->device) == hipSuccess && prop.multiProcessorCount > 0)
       num_cus = prop.multiProcessorCount;
   }
-  rc = build_schedule(hptr, N, num_cus, &g->fwd);
-  if (rc != CK_OK) return fail(rc);
-  rc = build_schedule(htptr, N, num_cus, &g->bwd);
-  if (rc != CK_OK) return fail(rc);
+  for (int k = 0; k < 2; ++k) {
+    const int waves = k == 0 ? 8 : 16;
+    rc = build_schedule(hptr, N, num_cus, waves, &g->fwd[k]);
+    if (rc != CK_OK) return fail(rc);
+    rc = build_schedule(htptr, N, num_cus, waves, &g->bwd[k]);
+    if (rc != CK_OK) return fail(rc);
+  }
   (void)hipFree(flags);
   (void)hipFree(seen);
   g->magic = kGraphMagic;

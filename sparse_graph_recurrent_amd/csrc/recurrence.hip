@@ -59,26 +59,6 @@ ck_status timed_launch(std::vector<std::pair<hipEvent_t, hipEvent_t>>& log, hipS
 }
 
 constexpr int kChunkCols = 64;  // columns per grid-y chunk when Bp > 64
-// Occupancy targets (waves per SIMD) that bound the register budget of the
-// two per-microstep kernels; 0 leaves the choice to the compiler.
-#ifndef CK_FWD_OCC
-#define CK_FWD_OCC 0
-#endif
-#ifndef CK_BWD_OCC
-#define CK_BWD_OCC 0
-#endif
-#if CK_FWD_OCC > 0
-#define CK_FWD_ATTR __attribute__((amdgpu_waves_per_eu(CK_FWD_OCC)))
-#else
-#define CK_FWD_ATTR
-#endif
-#if CK_BWD_OCC > 0
-#define CK_BWD_ATTR __attribute__((amdgpu_waves_per_eu(CK_BWD_OCC)))
-#else
-// two 8-wave workgroups per CU (at most 128 VGPRs) for power-of-two row widths
-// up to 32 columns; the schedule is sized for that
-#define CK_BWD_ATTR __attribute__((amdgpu_waves_per_eu((L <= 8 && is_pow2(L)) ? 4 : 1)))
-#endif
 
 __device__ __forceinline__ float4 f4(float x) { return make_float4(x, x, x, x); }
 __device__ __forceinline__ float4 fma4(float w, float4 h, float4 acc) {
@@ -255,28 +235,31 @@ __device__ __forceinline__ Lanes lanes(int Bp) {
   return r;
 }
 
-// Pull a whole state plane into this XCD's L2 at kernel start: the plane was
-// written by every XCD in the previous launch, so each XCD would otherwise
-// first-touch every gathered row from the memory side.  Workgroup w lives on
-// XCD w % kXcds; the workgroups of one XCD share the plane between them.
-// Returns a value that must be consumed (keeps the loads alive).
-constexpr uint32_t kPrefetchMaxBytes = 2u << 20;
-__device__ __forceinline__ float prefetch_plane(const float* plane, uint32_t bytes) {
-  float keep = 0.f;
-  if (bytes > kPrefetchMaxBytes || blockIdx.y != 0) return keep;
-  const uint32_t per_xcd = gridDim.x / kXcds;
-  if (per_xcd == 0) return keep;
-  const uint32_t slice = blockIdx.x / kXcds;
-  const uint32_t chunk = ((bytes / per_xcd) + 255u) & ~255u;
-  const uint32_t b0 = slice * chunk;
-  const uint32_t b1 = min(bytes, b0 + chunk);
-  // one dword per 128-byte line is enough to fill the line
-  for (uint32_t b = b0 + threadIdx.x * 128u; b < b1; b += kThreads * 128u)
-    keep += CK_AT(plane, b / 4u, bytes / 4u, 25);
-  return keep;
-}
 
-__device__ __forceinline__ void consume(float x) { asm volatile("" ::"v"(x)); }
+// LDS slot of a piece and the slot range of a split row (from the last
+// piece's info word); the checked build reports numbers outside [0, 2W).
+template <int W>
+__device__ __forceinline__ int piece_slot(int info) {
+  const int q = info & kInfoSlotMask;
+#ifdef CK_CHECKED
+  if (q >= 2 * W) {
+    atomicOr(&g_ck_err, 1u << 26);
+    return 0;
+  }
+#endif
+  return q;
+}
+template <int W>
+__device__ __forceinline__ void piece_range(int info, int& q0, int& q1) {
+  q1 = piece_slot<W>(info);
+  q0 = q1 - ((info >> kInfoCountShift) & kInfoSlotMask) + 1;
+#ifdef CK_CHECKED
+  if (q0 < 0) {
+    atomicOr(&g_ck_err, 1u << 26);
+    q0 = q1;
+  }
+#endif
+}
 
 // A wave walks its schedule in groups of kGroup batch entries: the group's
 // entries arrive as one vector load (lane q holds entry q), then the edge
@@ -353,16 +336,16 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& p, const Lanes& ln, 
 }
 
 template <int L>
-__global__ __launch_bounds__(kThreads) CK_FWD_ATTR void fwd_step(FwdArgs p) {
+__global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
   using G = Geom<L>;
+  constexpr int W = waves_for_lanes(L);
   constexpr int P = G::P, I = G::I, EB = G::EB;
   constexpr int NSUB = (kBatchEdges + EB - 1) / EB;  // gather rounds per batch entry
-  __shared__ float4 red[kWaves][16];
+  __shared__ float4 red[2 * W][16];  // partial sums of pieces, by piece number
   const Lanes ln = lanes<L>(p.Bp);
   const int wave = __builtin_amdgcn_readfirstlane(ln.wave);
   const int colc = ln.ok ? ln.col : 0;  // a valid address for lanes outside the loop
-  const int4* bt = p.batches + ((size_t)blockIdx.x * kWaves + wave) * p.KB;
-  const float pf = prefetch_plane(p.h_prev, (uint32_t)p.N * (uint32_t)p.Bp * 4u);
+  const int4* bt = p.batches + ((size_t)blockIdx.x * W + wave) * p.KB;
   const int4 idle = make_int4(-1, 0, 0, 0);
   const int first_info = p.KB > 0 ? CK_AT(bt, 0, p.KB, 10).w : 0;
   float4 acc = f4(0.f);
@@ -380,7 +363,7 @@ __global__ __launch_bounds__(kThreads) CK_FWD_ATTR void fwd_step(FwdArgs p) {
     for (int q = 0; q < kGroup; ++q) {
       const int4 d = lane_entry(ent, q);
       if (d.x < 0) break;  // end of this wave's list (uniform)
-      if (d.w & kInfoFirstBit) eo = fwd_epi_load(p, ln, (d.w & kInfoPieceBit) ? -1 : d.x);
+      if ((d.w & kInfoFirstBit) && !(d.w & kInfoPieceBit)) eo = fwd_epi_load(p, ln, d.x);
 #pragma unroll
       for (int sb = 0; sb < NSUB; ++sb) {
         if (sb * EB >= d.z) break;  // no edges left in this batch (uniform)
@@ -403,7 +386,7 @@ __global__ __launch_bounds__(kThreads) CK_FWD_ATTR void fwd_step(FwdArgs p) {
       if (d.w & kInfoLastBit) {  // the row (or piece) is complete
         acc = sum_slots<L>(acc, ln.sub);
         if (d.w & kInfoPieceBit) {
-          if (ln.slot == 0) red[wave][ln.sub] = acc;
+          if (ln.slot == 0) red[piece_slot<W>(d.w)][ln.sub] = acc;
         } else {
           fwd_epilogue(p, ln, d.x, acc, eo);
         }
@@ -411,16 +394,20 @@ __global__ __launch_bounds__(kThreads) CK_FWD_ATTR void fwd_step(FwdArgs p) {
       }
     }
   }
-  consume(pf);
   if (first_info & kInfoGroupBit) {
     // combine the pieces of this workgroup's split rows (fixed order)
-    __syncthreads();
+    // the wave holding a split row's last piece (its first segment) adds
+    // the row's pieces in piece order; its operand loads overlap the barrier
     const int4 d0 = CK_AT(bt, 0, p.KB, 10);
-    if (d0.x >= 0 && (d0.w & kInfoPieceBit) && (d0.w & 0xFF) == wave) {
-      const int np = (d0.w >> 8) & 0xFF;
-      float4 a = red[wave][ln.sub];
-      for (int q = 1; q < np; ++q) a = add4(a, red[wave + q][ln.sub]);
-      fwd_epilogue(p, ln, d0.x, a, fwd_epi_load(p, ln, d0.x));
+    const bool combine = d0.x >= 0 && (d0.w & kInfoCombineBit);
+    const FwdEpi ce = fwd_epi_load(p, ln, combine ? d0.x : -1);
+    __syncthreads();
+    if (combine) {
+      int q0, q1;
+      piece_range<W>(d0.w, q0, q1);
+      float4 a = red[q0][ln.sub];
+      for (int q = q0 + 1; q <= q1; ++q) a = add4(a, red[q][ln.sub]);
+      fwd_epilogue(p, ln, d0.x, a, ce);
     }
   }
 }
@@ -516,18 +503,18 @@ __device__ __forceinline__ void bwd_epilogue(const BwdArgs& p, const Lanes& ln, 
 }
 
 template <int L>
-__global__ __launch_bounds__(kThreads) CK_BWD_ATTR void bwd_step(BwdArgs p) {
+__global__ __launch_bounds__(waves_for_lanes(L) * 64) void bwd_step(BwdArgs p) {
   using G = Geom<L>;
+  constexpr int W = waves_for_lanes(L);
   constexpr int P = G::P, I = G::I, EB = G::EB;
   constexpr int NSUB = (kBatchEdges + EB - 1) / EB;
-  __shared__ float4 red[kWaves][16];
+  __shared__ float4 red[2 * W][16];  // partial sums of pieces, by piece number
   const Lanes ln = lanes<L>(p.Bp);
   const int wave = __builtin_amdgcn_readfirstlane(ln.wave);
   const int colc = ln.ok ? ln.col : 0;
-  const int4* bt = p.batches + ((size_t)blockIdx.x * kWaves + wave) * p.KB;
+  const int4* bt = p.batches + ((size_t)blockIdx.x * W + wave) * p.KB;
   // the seeding launch (no ga_in) has no edge pass: every batch counts as empty
   const bool edges = p.ga_in != nullptr;
-  const float pf = edges ? prefetch_plane(p.ga_in, (uint32_t)p.N * (uint32_t)p.Bp * 4u) : 0.f;
   float* gv = p.gv_csc + (size_t)blockIdx.y * p.E;
   // in gather round (sb, j) slot q handles batch edge sb*EB + j*P + q; the
   // edge term of round (sb, j = sub) is kept by lane (q, sub)
@@ -565,7 +552,7 @@ __global__ __launch_bounds__(kThreads) CK_BWD_ATTR void bwd_step(BwdArgs p) {
         if (d.z > 0)
           hj = ld4c(p.h_sm1, ((uint32_t)d.x * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
                     (size_t)p.N * p.Bp, 23);
-        eo = bwd_epi_load(p, ln, (d.w & kInfoPieceBit) ? -1 : d.x);
+        if (!(d.w & kInfoPieceBit)) eo = bwd_epi_load(p, ln, d.x);
       }
 #pragma unroll
       for (int sb = 0; sb < NSUB; ++sb) {
@@ -595,7 +582,7 @@ __global__ __launch_bounds__(kThreads) CK_BWD_ATTR void bwd_step(BwdArgs p) {
       if (d.w & kInfoLastBit) {
         acc = sum_slots<L>(acc, ln.sub);
         if (d.w & kInfoPieceBit) {
-          if (ln.slot == 0) red[wave][ln.sub] = acc;
+          if (ln.slot == 0) red[piece_slot<W>(d.w)][ln.sub] = acc;
         } else {
           bwd_epilogue<L>(p, ln, d.x, acc, eo);
         }
@@ -603,15 +590,19 @@ __global__ __launch_bounds__(kThreads) CK_BWD_ATTR void bwd_step(BwdArgs p) {
       }
     }
   }
-  consume(pf);
   if (first_info & kInfoGroupBit) {
-    __syncthreads();
+    // the wave holding a split row's last piece (its first segment) adds
+    // the row's pieces in piece order; its operand loads overlap the barrier
     const int4 d0 = CK_AT(bt, 0, p.KB, 10);
-    if (d0.x >= 0 && (d0.w & kInfoPieceBit) && (d0.w & 0xFF) == wave) {
-      const int np = (d0.w >> 8) & 0xFF;
-      float4 a = red[wave][ln.sub];
-      for (int q = 1; q < np; ++q) a = add4(a, red[wave + q][ln.sub]);
-      bwd_epilogue<L>(p, ln, d0.x, a, bwd_epi_load(p, ln, d0.x));
+    const bool combine = d0.x >= 0 && (d0.w & kInfoCombineBit);
+    const BwdEpi ce = bwd_epi_load(p, ln, combine ? d0.x : -1);
+    __syncthreads();
+    if (combine) {
+      int q0, q1;
+      piece_range<W>(d0.w, q0, q1);
+      float4 a = red[q0][ln.sub];
+      for (int q = q0 + 1; q <= q1; ++q) a = add4(a, red[q][ln.sub]);
+      bwd_epilogue<L>(p, ln, d0.x, a, ce);
     }
   }
 }
@@ -775,10 +766,11 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
   to_node_major<<<grid1((int64_t)d.plane), 256, 0, stream>>>(state0, (int)d.N, (int)d.B,
                                                              (int)d.Bp, h0);
   const FwdFn kern = KT::fwd[d.L - 1];
-  const dim3 grid(g->fwd.num_wgs, d.chunks);
+  const Schedule& sc = g->fwd[waves_for_lanes(d.L) == 16 ? 1 : 0];
+  const dim3 grid(sc.num_wgs, d.chunks), block(sc.waves * 64);
   FwdArgs a{};
-  a.batches = g->fwd.batches;
-  a.KB = g->fwd.KB;
+  a.batches = sc.batches;
+  a.KB = sc.KB;
   a.col_idx = g->col_idx;
   a.v_csr = v_csr;
   a.leak = leak;
@@ -797,7 +789,7 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
     a.a_next = aplanes + (size_t)(s - 1) * d.plane;
     a.out_t = (s % d.M == 0) ? out + (size_t)t * d.B * d.N : nullptr;
     rc = timed_launch(g_profile.fwd, stream,
-                      [&] { hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, a); });
+                      [&] { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); });
     if (rc != CK_OK) return rc;
   }
   CK_HIP_TRY(hipGetLastError());
@@ -860,10 +852,11 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
   if (d.n_in > 0)
     zero_f32<<<grid1(d.T * d.n_in * d.B), 256, 0, stream>>>(grad_drives, d.T * d.n_in * d.B);
   const BwdFn kern = KT::bwd[d.L - 1];
-  const dim3 grid(g->bwd.num_wgs, d.chunks);
+  const Schedule& sc = g->bwd[waves_for_lanes(d.L) == 16 ? 1 : 0];
+  const dim3 grid(sc.num_wgs, d.chunks), block(sc.waves * 64);
   BwdArgs a{};
-  a.batches = g->bwd.batches;
-  a.KB = g->bwd.KB;
+  a.batches = sc.batches;
+  a.KB = sc.KB;
   a.t_col_idx = g->t_col_idx;
   a.v_csc = v_csc;
   a.gv_csc = gv_csc;
@@ -901,7 +894,7 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
       a.gdrives_t = nullptr;
     }
     rc = timed_launch(g_profile.bwd, stream,
-                      [&] { hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, a); });
+                      [&] { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); });
     if (rc != CK_OK) return rc;
   }
   if (d.chunks > 1) {

@@ -1,0 +1,157 @@
+// schedule.cpp -- host-side planning of the per-wave batch lists (see
+// schedule.h); called by ck_graph_create for each orientation and width.
+#include "schedule.h"
+
+#include <algorithm>
+
+namespace ckhip {
+
+// Degree-balanced, XCD-aware schedule (host side, from the row pointers) for
+// workgroups of `waves` waves.  The unit of work is a batch: at most
+// kBatchEdges edges of one row, one gather round of a wave at B = 32; a row
+// without edges takes one empty batch (its epilogue still runs).
+//  1. Rows are cut into kXcds contiguous ranges of about equal batch count;
+//     workgroup g runs on XCD g % kXcds as that XCD's workgroup g / kXcds.
+//  2. Inside an XCD the rows are cut into at most wg_x contiguous workgroup
+//     ranges whose largest batch count is as small as possible (bisection on
+//     that bound, with greedy packing as the test).
+//  3. A workgroup's batches, in row order, are dealt to its waves as
+//     contiguous runs whose lengths differ by at most one.  A row whose batches
+//     land on several waves is split into pieces (one segment per wave), and
+//     its last piece's wave adds the pieces up after the workgroup barrier.
+void plan_schedule(const int32_t* ptr, int64_t N, int num_cus, int waves, SchedulePlan* out) {
+  constexpr int64_t kMinWaveBatches = 2;  // small graphs: fewer, fuller workgroups
+  std::vector<int64_t> nb(N);
+  int64_t total = 0;
+  for (int64_t i = 0; i < N; ++i) {
+    const int64_t d = ptr[i + 1] - ptr[i];
+    nb[i] = std::max<int64_t>(1, (d + kBatchEdges - 1) / kBatchEdges);
+    total += nb[i];
+  }
+  std::vector<int64_t> cut(kXcds + 1, N);
+  cut[0] = 0;
+  {
+    int64_t acc = 0;
+    int x = 1;
+    for (int64_t i = 0; i < N && x < kXcds; ++i) {
+      acc += nb[i];
+      while (x < kXcds && acc * kXcds >= total * x) cut[x++] = i + 1;
+    }
+  }
+  const int64_t cap = std::max<int64_t>(1, (int64_t)num_cus / kXcds * (kWavesPerCu / waves));
+  const int64_t per_x = (total + kXcds - 1) / kXcds;
+  const int wg_x = (int)std::min<int64_t>(
+      cap, std::max<int64_t>(1, (per_x + kMinWaveBatches * waves - 1) / (kMinWaveBatches * waves)));
+  // lists[(wgl * kXcds + x) * waves + wave]: batch entries of one wave
+  std::vector<std::vector<BatchEntry>> lists((size_t)wg_x * kXcds * waves);
+  for (int x = 0; x < kXcds; ++x) {
+    const int64_t r0 = cut[x], r1 = cut[x + 1];
+    if (r0 >= r1) continue;
+    // number of workgroup ranges greedy packing needs under bound lim
+    auto pack = [&](int64_t lim, std::vector<int64_t>* bounds) {
+      int64_t groups = 1, sum = 0;
+      if (bounds) bounds->assign(1, r0);
+      for (int64_t i = r0; i < r1; ++i) {
+        if (sum > 0 && sum + nb[i] > lim) {
+          ++groups;
+          sum = 0;
+          if (bounds) bounds->push_back(i);
+        }
+        sum += nb[i];
+      }
+      if (bounds) bounds->push_back(r1);
+      return groups;
+    };
+    int64_t sum = 0, big = 0;
+    for (int64_t i = r0; i < r1; ++i) {
+      sum += nb[i];
+      big = std::max(big, nb[i]);
+    }
+    int64_t lo = std::max(big, (sum + wg_x - 1) / wg_x), hi = std::max(lo, sum);
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (pack(mid, nullptr) <= wg_x)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    std::vector<int64_t> bounds;
+    pack(lo, &bounds);
+    for (size_t k = 0; k + 1 < bounds.size(); ++k) {
+      std::vector<BatchEntry> bl;  // this workgroup's batches in row order
+      for (int64_t i = bounds[k]; i < bounds[k + 1]; ++i)
+        for (int64_t j = 0; j < nb[i]; ++j) {
+          const int32_t kb = (int32_t)(ptr[i] + j * kBatchEdges);
+          const int32_t cnt = std::max(0, std::min<int32_t>(kBatchEdges, ptr[i + 1] - kb));
+          bl.push_back({(int32_t)i, kb, cnt, 0});
+        }
+      const size_t n = bl.size();
+      std::vector<size_t> wb(waves + 1);
+      for (int w = 0; w <= waves; ++w) wb[w] = n * (size_t)w / (size_t)waves;
+      int pieces = 0;
+      for (int w = 0; w < waves; ++w) {
+        const size_t b0 = wb[w], b1 = wb[w + 1];
+        if (b0 == b1) continue;
+        for (size_t b = b0; b < b1; ++b) {
+          if (b == b0 || bl[b - 1].row != bl[b].row) bl[b].info |= kInfoFirstBit;
+          if (b + 1 == b1 || bl[b + 1].row != bl[b].row) bl[b].info |= kInfoLastBit;
+        }
+        // the first segment continues a row of the previous wave, the last
+        // segment continues into the next wave: those segments are pieces
+        size_t f1 = b0;
+        while (f1 < b1 && bl[f1].row == bl[b0].row) ++f1;
+        size_t l0 = b1;
+        while (l0 > b0 && bl[l0 - 1].row == bl[b1 - 1].row) --l0;
+        const bool piece_first = b0 > 0 && bl[b0 - 1].row == bl[b0].row;
+        const bool piece_last = b1 < n && bl[b1].row == bl[b1 - 1].row;
+        auto mark = [&](size_t e0, size_t e1) {
+          for (size_t b = e0; b < e1; ++b) bl[b].info |= kInfoPieceBit | pieces;
+          ++pieces;
+        };
+        if (piece_first) mark(b0, f1);
+        if (piece_last && !(piece_first && l0 == b0)) mark(l0, b1);
+      }
+      // the last piece of each split row (highest number among the row's
+      // consecutive piece numbers) carries the row's piece count
+      if (pieces > 0) {
+        std::vector<int> row_of(pieces, -1);
+        std::vector<size_t> at(pieces, 0);
+        for (size_t b = 0; b < n; ++b)
+          if ((bl[b].info & kInfoPieceBit) && (bl[b].info & kInfoFirstBit)) {
+            const int q = bl[b].info & kInfoSlotMask;
+            row_of[q] = bl[b].row;
+            at[q] = b;
+          }
+        for (int q = 0; q < pieces; ++q) {
+          const bool last_of_row = q + 1 == pieces || row_of[q + 1] != row_of[q];
+          if (!last_of_row) continue;
+          int q0 = q;
+          while (q0 > 0 && row_of[q0 - 1] == row_of[q]) --q0;
+          const int np = q - q0 + 1;
+          for (size_t b = at[q]; b < n && bl[b].row == row_of[q] && (bl[b].info & kInfoPieceBit) &&
+                                 (bl[b].info & kInfoSlotMask) == q;
+               ++b)
+            bl[b].info |= kInfoCombineBit | (np << kInfoCountShift);
+        }
+        for (auto& e : bl) e.info |= kInfoGroupBit;
+      }
+      for (int w = 0; w < waves; ++w) {
+        auto& lst = lists[((size_t)k * kXcds + x) * waves + w];
+        lst.assign(bl.begin() + wb[w], bl.begin() + wb[w + 1]);
+        // an empty wave of a workgroup with pieces must still reach its barrier
+        if (lst.empty() && pieces > 0) lst.push_back({-1, 0, 0, kInfoGroupBit});
+      }
+    }
+  }
+  size_t KB = 1;
+  for (const auto& l : lists) KB = std::max(KB, l.size());
+  const int num_wgs = wg_x * kXcds;
+  out->table.assign((size_t)num_wgs * waves * KB, BatchEntry{-1, 0, 0, 0});
+  for (size_t v = 0; v < lists.size(); ++v)
+    std::copy(lists[v].begin(), lists[v].end(), out->table.begin() + v * KB);
+  out->num_wgs = num_wgs;
+  out->waves = waves;
+  out->KB = (int)KB;
+}
+
+}  // namespace ckhip

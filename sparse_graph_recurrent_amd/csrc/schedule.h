@@ -1,0 +1,74 @@
+// schedule.h -- the row schedule of one orientation of the graph: which
+// edge batches each wave of the per-microstep kernels walks.  Plain C++ (no
+// HIP calls), so that the CPU tests can build and check it on its own.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#ifdef __HIPCC__
+#define CK_HOST_DEVICE __host__ __device__
+#else
+#define CK_HOST_DEVICE
+#endif
+
+namespace ckhip {
+
+// Workgroup shapes of the per-microstep kernels.  A kernel whose row width
+// (L lanes of float4 per row) keeps it within 128 VGPRs runs 16-wave
+// workgroups, one per CU; the others run 8-wave workgroups, two per CU when
+// their registers allow.  Either way the schedule is sized for 16 resident
+// waves per CU, i.e. one round of workgroups.
+constexpr int kWavesPerCu = 16;
+CK_HOST_DEVICE constexpr int waves_for_lanes(int L) {
+  return (L <= 8 && (L & (L - 1)) == 0) ? 16 : 8;
+}
+constexpr int kMaxWaves = 16;
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X.
+constexpr int kXcds = 8;
+
+// Row schedule of one orientation of the graph for one workgroup width W, as
+// edge batches.  Wave v (= workgroup * W + wave index) walks
+// batches[v * KB .. v * KB + KB) in order until an entry with row < 0.
+// Entry = {row, kbeg, count, info}: edges [kbeg, kbeg + count) (count <=
+// kBatchEdges) of the row's compressed list.  Consecutive batches of one row on
+// one wave form a segment; a row whose batches fall on several waves (always
+// of one workgroup) is split into pieces, one segment per wave.  A piece is a
+// wave's first or last segment, so a workgroup holds at most 2 W pieces; they
+// are numbered in row order, so the pieces of one row have consecutive
+// numbers, and the last piece of a row is the first segment of its wave.
+//   info bits 0..5: piece number (LDS slot of the piece's partial sum);
+//   bits 6..11: on the last piece of a row, the row's number of pieces;
+//   bit 12: last piece of its row (its wave sums the row's pieces, in piece
+//   order, after the workgroup barrier and runs the row's epilogue);
+//   bit 16: the workgroup holds pieces (all its waves synchronise once at the
+//   end); bit 17: this batch belongs to a piece; bit 18: first batch of its
+//   segment; bit 19: last batch of its segment.
+constexpr int kBatchEdges = 64;
+constexpr int kInfoSlotMask = 63;
+constexpr int kInfoCountShift = 6;
+constexpr int kInfoCombineBit = 1 << 12;
+constexpr int kInfoGroupBit = 1 << 16;
+constexpr int kInfoPieceBit = 1 << 17;
+constexpr int kInfoFirstBit = 1 << 18;
+constexpr int kInfoLastBit = 1 << 19;
+// One batch entry; the same 16-byte layout as the int4 the kernels read.
+struct BatchEntry {
+  int32_t row, kbeg, count, info;
+};
+
+// The table of one schedule: wave v (= workgroup * waves + wave index) owns
+// entries [v * KB, v * KB + KB), padded with row = -1.
+struct SchedulePlan {
+  std::vector<BatchEntry> table;
+  int num_wgs = 0;
+  int waves = 0;
+  int KB = 0;
+};
+
+// Plan the schedule of a compressed row structure ptr[0..N] (row i holds edges
+// [ptr[i], ptr[i+1])) for workgroups of `waves` waves on `num_cus` compute
+// units.
+void plan_schedule(const int32_t* ptr, int64_t N, int num_cus, int waves, SchedulePlan* out);
+
+}  // namespace ckhip
