@@ -14,6 +14,9 @@ namespace ckhip {
 
 struct Schedule {
   int4* batches = nullptr;  // [num_wgs * waves * KB]
+  int32_t* pcol = nullptr;  // [slots] column of edge k of entry t at t * kBatchEdges + k, or -1
+  int32_t* pperm = nullptr; // [slots] caller index of that edge, or -1
+  int64_t slots = 0;        // num_wgs * waves * KB * kBatchEdges
   int num_wgs = 0;
   int waves = 0;            // waves per workgroup
   int KB = 0;               // batch entries per wave (padded with row = -1)

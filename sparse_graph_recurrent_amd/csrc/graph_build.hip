@@ -266,18 +266,47 @@ ck_status build_compressed(const int64_t* major, const int64_t* minor, int64_t E
   return CK_OK;
 }
 
-// Upload the planned schedule of one orientation for `waves`-wave workgroups.
-ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, int num_cus, int waves,
+// Padded edge slots of one schedule: slot t * kBatchEdges + k holds edge k of
+// batch entry t (its column index and caller index), or -1 past the batch's
+// end, so a wave finds the edges of its j-th batch at a fixed offset.
+__global__ void pad_edges(const int4* __restrict__ table, int64_t slots,
+                          const int32_t* __restrict__ col, const int32_t* __restrict__ perm,
+                          int32_t* __restrict__ pcol, int32_t* __restrict__ pperm) {
+  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= slots) return;
+  const int4 t = table[s / kBatchEdges];
+  const int k = (int)(s % kBatchEdges);
+  const bool live = t.x >= 0 && k < t.z;
+  pcol[s] = live ? col[t.y + k] : -1;
+  pperm[s] = live ? perm[t.y + k] : -1;
+}
+
+// Plan and upload the schedule of one orientation (row pointers ptr, edge
+// columns col and caller indices perm in compressed order) for `waves`-wave
+// workgroups, with its padded edge slots.
+ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, const int32_t* col,
+                         const int32_t* perm, int num_cus, int waves, hipStream_t stream,
                          Schedule* out) {
   static_assert(sizeof(BatchEntry) == sizeof(int4), "batch entries are read as int4");
   SchedulePlan plan;
   plan_schedule(ptr.data(), N, num_cus, waves, &plan);
+  const int64_t slots = (int64_t)plan.table.size() * kBatchEdges;
+  if (slots > kInt32Limit) {
+    set_error("padded edge slots (%lld) overflow 32-bit indexing", (long long)slots);
+    return CK_ERR_TOO_LARGE;
+  }
   out->num_wgs = plan.num_wgs;
   out->waves = plan.waves;
   out->KB = plan.KB;
+  out->slots = slots;
   const size_t bytes = plan.table.size() * sizeof(BatchEntry);
   CK_HIP_TRY(hipMalloc(&out->batches, bytes));
   CK_HIP_TRY(hipMemcpy(out->batches, plan.table.data(), bytes, hipMemcpyHostToDevice));
+  CK_HIP_TRY(hipMalloc(&out->pcol, slots * sizeof(int32_t)));
+  CK_HIP_TRY(hipMalloc(&out->pperm, slots * sizeof(int32_t)));
+  pad_edges<<<grid_for(slots, 256), 256, 0, stream>>>(out->batches, slots, col, perm, out->pcol,
+                                                       out->pperm);
+  CK_HIP_TRY(hipGetLastError());
   return CK_OK;
 }
 
@@ -285,10 +314,12 @@ void free_graph_arrays(ck_graph* g) {
   int32_t* arrs[] = {g->row_ptr, g->col_idx, g->perm, g->t_row_ptr, g->t_col_idx, g->t_perm,
                      g->input_slot};
   for (int32_t* p : arrs) (void)hipFree(p);
-  for (int k = 0; k < 2; ++k) {
-    (void)hipFree(g->fwd[k].batches);
-    (void)hipFree(g->bwd[k].batches);
-  }
+  for (int k = 0; k < 2; ++k)
+    for (Schedule* sc : {&g->fwd[k], &g->bwd[k]}) {
+      (void)hipFree(sc->batches);
+      (void)hipFree(sc->pcol);
+      (void)hipFree(sc->pperm);
+    }
 }
 
 }  // namespace
@@ -393,11 +424,12 @@ extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int
   }
   for (int k = 0; k < 2; ++k) {
     const int waves = k == 0 ? 8 : 16;
-    rc = build_schedule(hptr, N, num_cus, waves, &g->fwd[k]);
+    rc = build_schedule(hptr, N, g->col_idx, g->perm, num_cus, waves, stream, &g->fwd[k]);
     if (rc != CK_OK) return fail(rc);
-    rc = build_schedule(htptr, N, num_cus, waves, &g->bwd[k]);
+    rc = build_schedule(htptr, N, g->t_col_idx, g->t_perm, num_cus, waves, stream, &g->bwd[k]);
     if (rc != CK_OK) return fail(rc);
   }
+  CK_GB_TRY(hipStreamSynchronize(stream));
   (void)hipFree(flags);
   (void)hipFree(seen);
   g->magic = kGraphMagic;

@@ -206,6 +206,48 @@ __device__ __forceinline__ float4 ld4c(const float* base, uint32_t byte_off, siz
 }
 #endif
 
+// Row gathers go through a buffer resource over one [N][Bp] plane.  A lane
+// with nothing to gather (padded edge slot, idle lane) passes kNoRow, an
+// offset past any plane (planes are below 2^32 - 16 bytes): the hardware
+// range check returns zero for it without a memory access, so no branch is
+// needed around the load.  (Third descriptor word: the gfx9 family's raw
+// 32-bit buffer format.)
+constexpr uint32_t kNoRow = 0xFFFFFFF0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const float* plane, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(plane), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ float4 gather4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t bytes,
+                                          int site) {
+#ifdef CK_CHECKED
+  if (off != kNoRow && ((size_t)off + 16 > bytes || (off & 15u))) {
+    atomicOr(&g_ck_err, 1u << site);
+    return g_ck_dummy[0];
+  }
+#else
+  (void)bytes;
+  (void)site;
+#endif
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Load of a value that is the same for every lane (a per-row parameter) from
+// an array no kernel of the recurrence writes: through the constant address
+// space, so it takes the scalar path and no vector memory instruction.
+template <typename T>
+__device__ __forceinline__ T ld_row(const T* base, size_t i, size_t n, int site) {
+#ifdef CK_CHECKED
+  if (base == nullptr || i >= n) {
+    atomicOr(&g_ck_err, 1u << site);
+    return T(0);
+  }
+#else
+  (void)n;
+  (void)site;
+#endif
+  return ((const __attribute__((address_space(4))) T*)base)[i];
+}
+
 __device__ __forceinline__ float pick4(float4 v, int q) {
   return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
 }
@@ -261,37 +303,54 @@ __device__ __forceinline__ void piece_range(int info, int& q0, int& q1) {
 #endif
 }
 
-// A wave walks its schedule in groups of kGroup batch entries: the group's
-// entries arrive as one vector load (lane q holds entry q), then the edge
-// indices (and, backward, the old edge gradients) of all its batches are
-// requested at once, so one memory round trip covers up to kGroup * 64 edges
-// before the gathers start.
-constexpr int kGroup = 8;
+// A wave walks its schedule in groups of G batch entries.  The group's
+// entries (lane q holds entry q) and the padded edge slots of its batches
+// (lane k holds edge k of each batch) sit at offsets fixed by the wave's
+// index, so both are requested together at the start of the group.  The
+// gathers then run as a ring: a unit is one gather round of a batch (I loads
+// per lane), TU units are in flight, and units are consumed in order, each
+// freed ring slot being refilled with the unit TU places ahead.  The row
+// operands of a batch's epilogue are requested with its first unit.
+template <int L, int G>
+struct Pipe {
+  static constexpr int I = Geom<L>::I;
+  static constexpr int NSUB = (kBatchEdges + Geom<L>::EB - 1) / Geom<L>::EB;  // units per batch
+  static constexpr int NU = G * NSUB;                                          // units per group
+  // units in flight: about 32 VGPRs of gathered float4 rows per lane (more
+  // in flight measured no faster at B = 32: the gathers are bound by the
+  // vector memory pipeline's throughput, not by its latency)
+  static constexpr int TU = (8 / I) < 1 ? 1 : ((8 / I) > NU ? NU : 8 / I);
+  // batch entries whose operands are in flight with the ring
+  static constexpr int TE = (TU - 1) / NSUB + 1;
+};
+constexpr int kFwdGroup = 8;
+constexpr int kBwdGroup = 4;
 
 __device__ __forceinline__ int4 lane_entry(const int4& v, int q) {
   return make_int4(__builtin_amdgcn_readlane(v.x, q), __builtin_amdgcn_readlane(v.y, q),
                    __builtin_amdgcn_readlane(v.z, q), __builtin_amdgcn_readlane(v.w, q));
 }
 
-// Edge indices and values of one batch entry d: lane k holds edge d.y + k
-// (clamped into the batch; lanes past its end get value 0).
-__device__ __forceinline__ void batch_edges(const int4& d, const int32_t* __restrict__ idx,
-                                            const float* __restrict__ val, int lane, int E,
-                                            int& c, float& w) {
-  c = 0;
-  w = 0.f;
-  if (d.x >= 0 && d.z > 0) {
-    const int e = d.y + min(lane, d.z - 1);
-    c = CK_AT(idx, e, E, 8);
-    w = lane < d.z ? CK_AT(val, e, E, 9) : 0.f;
-  }
+// The value a lane shuffle brought from batch edge e, or `none` past the
+// batch's 64 edges.  The shuffle itself must run on every lane (a permute
+// reads nothing useful from a lane that is switched off), so it is done
+// unconditionally and only its result is selected.
+template <typename T>
+__device__ __forceinline__ T lane_or(T shuffled, int e, T none) {
+  return e < kBatchEdges ? shuffled : none;
+}
+
+// Number of entries in use in a group (they form a prefix of lanes 0..G-1).
+template <int G>
+__device__ __forceinline__ int group_entries(const int4& ent, int lane) {
+  return __popcll(__ballot(lane < G && ent.x >= 0));
 }
 
 struct FwdArgs {
   const int4* batches;    // schedule: KB batch entries per wave
+  const int2* pedge;      // [slots] padded edge slots: {source node or -1, bits of the value}
+  int64_t slots;
   int KB;
-  const int32_t* col_idx;
-  const float* v_csr;
   const float* leak;
   const float* bias;
   const int32_t* input_slot;
@@ -300,7 +359,7 @@ struct FwdArgs {
   float* h_next;          // [N][Bp]
   float* a_next;          // [N][Bp]
   float* out_t;           // [B][N] or nullptr when s is not the last microstep of a step
-  int N, B, Bp, E, n_in;
+  int N, B, Bp, n_in;
 };
 
 // Row operands of the forward epilogue (this lane's column).
@@ -310,12 +369,14 @@ struct FwdEpi {
 
 __device__ __forceinline__ FwdEpi fwd_epi_load(const FwdArgs& p, const Lanes& ln, int row) {
   FwdEpi e{0.f, 0.f, 0.f, 0.f};
-  if (row < 0 || !ln.eok) return e;
+  if (row < 0) return e;
+  // per-row values first (the same for every lane)
+  e.lam = ld_row(p.leak, row, p.N, 1);
+  e.bi = ld_row(p.bias, row, p.N, 2);
+  const int ks = ld_row(p.input_slot, row, p.N, 3);
+  if (!ln.eok) return e;
   [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
   e.hp = CK_AT(p.h_prev, (size_t)row * p.Bp + ln.ecol, NBp, 0);
-  e.lam = CK_AT(p.leak, row, p.N, 1);
-  e.bi = CK_AT(p.bias, row, p.N, 2);
-  const int ks = CK_AT(p.input_slot, row, p.N, 3);
   if (ks >= 0 && ln.ecol < p.B)
     e.dv = CK_AT(p.drives_t, (size_t)ks * p.B + ln.ecol, (size_t)p.n_in * p.B, 4);
   return e;
@@ -337,67 +398,99 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& p, const Lanes& ln, 
 
 template <int L>
 __global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
-  using G = Geom<L>;
+  using Gm = Geom<L>;
+  using Pp = Pipe<L, kFwdGroup>;
   constexpr int W = waves_for_lanes(L);
-  constexpr int P = G::P, I = G::I, EB = G::EB;
-  constexpr int NSUB = (kBatchEdges + EB - 1) / EB;  // gather rounds per batch entry
+  constexpr int P = Gm::P, I = Gm::I, EB = Gm::EB;
+  constexpr int NSUB = Pp::NSUB, NU = Pp::NU, TU = Pp::TU, TE = Pp::TE;
   __shared__ float4 red[2 * W][16];  // partial sums of pieces, by piece number
   const Lanes ln = lanes<L>(p.Bp);
   const int wave = __builtin_amdgcn_readfirstlane(ln.wave);
-  const int colc = ln.ok ? ln.col : 0;  // a valid address for lanes outside the loop
-  const int4* bt = p.batches + ((size_t)blockIdx.x * W + wave) * p.KB;
+  const uint32_t colb = (uint32_t)(ln.ok ? ln.col : 0) * 4u;  // this lane's columns, in bytes
+  const uint32_t rowb = (uint32_t)p.Bp * 4u;                   // bytes per state row
+  [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
+  const size_t wv = (size_t)blockIdx.x * W + wave;
+  const int4* bt = p.batches + wv * p.KB;
+  const size_t slot0 = wv * p.KB * kBatchEdges;
   const int4 idle = make_int4(-1, 0, 0, 0);
   const int first_info = p.KB > 0 ? CK_AT(bt, 0, p.KB, 10).w : 0;
+  const uint32_t pbytes = (uint32_t)NBp * 4u;
+  const __amdgpu_buffer_rsrc_t hsrc = plane_rsrc(p.h_prev, pbytes);
   float4 acc = f4(0.f);
   FwdEpi eo{0.f, 0.f, 0.f, 0.f};
-  for (int g0 = 0; g0 < p.KB; g0 += kGroup) {
-    const int4 ent = (ln.lane < kGroup && g0 + ln.lane < p.KB) ? CK_AT(bt, g0 + ln.lane, p.KB, 10)
-                                                              : idle;
-    if (__builtin_amdgcn_readlane(ent.x, 0) < 0) break;
-    int cb[kGroup];
-    float wb[kGroup];
+  for (int g0 = 0; g0 < p.KB; g0 += kFwdGroup) {
+    const int4 ent = (ln.lane < kFwdGroup && g0 + ln.lane < p.KB)
+                         ? CK_AT(bt, g0 + ln.lane, p.KB, 10) : idle;
+    int cb[kFwdGroup];
+    float wb[kFwdGroup];
 #pragma unroll
-    for (int q = 0; q < kGroup; ++q)
-      batch_edges(lane_entry(ent, q), p.col_idx, p.v_csr, ln.lane, p.E, cb[q], wb[q]);
+    for (int q = 0; q < kFwdGroup; ++q) {
+      cb[q] = -1;
+      wb[q] = 0.f;
+      if (g0 + q < p.KB) {
+        const int2 pe = CK_AT(p.pedge, slot0 + (size_t)(g0 + q) * kBatchEdges + ln.lane, p.slots, 8);
+        cb[q] = pe.x;
+        wb[q] = __int_as_float(pe.y);
+      }
+    }
+    const int nq = group_entries<kFwdGroup>(ent, ln.lane);
+    if (nq == 0) break;
+    int4 dq[kFwdGroup];  // the entries as wave-uniform values
 #pragma unroll
-    for (int q = 0; q < kGroup; ++q) {
-      const int4 d = lane_entry(ent, q);
-      if (d.x < 0) break;  // end of this wave's list (uniform)
-      if ((d.w & kInfoFirstBit) && !(d.w & kInfoPieceBit)) eo = fwd_epi_load(p, ln, d.x);
+    for (int q = 0; q < kFwdGroup; ++q) dq[q] = lane_entry(ent, q);
+    float4 hv[TU][I];
+    FwdEpi er[TE];
 #pragma unroll
-      for (int sb = 0; sb < NSUB; ++sb) {
-        if (sb * EB >= d.z) break;  // no edges left in this batch (uniform)
-        float4 hv[I];
-        float wj[I];
+    for (int u = 0; u < NU + TU; ++u) {
+      if (u >= TU) {  // consume unit u - TU
+        const int uc = u - TU, q = uc / NSUB, sb = uc % NSUB;
+        if (q < nq) {
+          const int4 d = dq[q];
+          if (sb == 0 && (d.w & kInfoFirstBit) && !(d.w & kInfoPieceBit)) eo = er[q % TE];
+          if (sb * EB < d.z) {
 #pragma unroll
-        for (int j = 0; j < I; ++j) {
-          const int e = sb * EB + j * P + ln.slot;
-          const int cj = __shfl(cb[q], e);
-          wj[j] = __shfl(wb[q], e);
-          hv[j] = ld4c(p.h_prev, ((uint32_t)cj * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
-                       (size_t)p.N * p.Bp, 11);
-        }
-#pragma unroll
-        for (int j = 0; j < I; ++j) {
-          const bool use = ln.ok && sb * EB + j * P + ln.slot < d.z;
-          acc = fma4(wj[j], use ? hv[j] : f4(0.f), acc);
+            for (int j = 0; j < I; ++j) {
+              if (sb * EB + j * P >= d.z) break;  // past the batch's last edge (uniform)
+              const int e = sb * EB + j * P + ln.slot;
+              const float wj = lane_or(__shfl(wb[q], e & 63), e, 0.f);
+              acc = fma4(wj, hv[uc % TU][j], acc);
+            }
+          }
+          if (sb == NSUB - 1 && (d.w & kInfoLastBit)) {  // the row (or piece) is complete
+            acc = sum_slots<L>(acc, ln.sub);
+            if (d.w & kInfoPieceBit) {
+              if (ln.slot == 0) red[piece_slot<W>(d.w)][ln.sub] = acc;
+            } else {
+              fwd_epilogue(p, ln, d.x, acc, eo);
+            }
+            acc = f4(0.f);
+          }
         }
       }
-      if (d.w & kInfoLastBit) {  // the row (or piece) is complete
-        acc = sum_slots<L>(acc, ln.sub);
-        if (d.w & kInfoPieceBit) {
-          if (ln.slot == 0) red[piece_slot<W>(d.w)][ln.sub] = acc;
-        } else {
-          fwd_epilogue(p, ln, d.x, acc, eo);
+      if (u < NU) {  // issue unit u into the slot just freed
+        const int q = u / NSUB, sb = u % NSUB;
+        if (q < nq) {
+          const int4 d = dq[q];
+          if (sb * EB < d.z) {
+#pragma unroll
+            for (int j = 0; j < I; ++j) {
+              if (sb * EB + j * P >= d.z) break;  // past the batch's last edge (uniform)
+              const int e = sb * EB + j * P + ln.slot;
+              const int cj = lane_or(__shfl(cb[q], e & 63), e, -1);
+              hv[u % TU][j] = gather4(hsrc, (cj >= 0 && ln.ok) ? (uint32_t)cj * rowb + colb : kNoRow,
+                                      pbytes, 11);
+            }
+          }
+          if (sb == 0)
+            er[q % TE] = fwd_epi_load(
+                p, ln, ((d.w & kInfoFirstBit) && !(d.w & kInfoPieceBit)) ? d.x : -1);
         }
-        acc = f4(0.f);
       }
     }
   }
   if (first_info & kInfoGroupBit) {
-    // combine the pieces of this workgroup's split rows (fixed order)
-    // the wave holding a split row's last piece (its first segment) adds
-    // the row's pieces in piece order; its operand loads overlap the barrier
+    // the wave holding a split row's last piece (its first segment) adds the
+    // row's pieces in piece order; its operand loads overlap the barrier
     const int4 d0 = CK_AT(bt, 0, p.KB, 10);
     const bool combine = d0.x >= 0 && (d0.w & kInfoCombineBit);
     const FwdEpi ce = fwd_epi_load(p, ln, combine ? d0.x : -1);
@@ -414,10 +507,10 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
 
 struct BwdArgs {
   const int4* batches;    // schedule of the transposed CSR: KB batch entries per wave
+  const int2* pedge;      // [slots] padded edge slots: {destination node or -1, bits of the value}
+  float* gv;              // [chunks][slots] edge gradient per slot, one row per column chunk
+  int64_t slots;
   int KB;
-  const int32_t* t_col_idx;
-  const float* v_csc;
-  float* gv_csc;          // [chunks][E] transposed-CSR order, one row per column chunk
   const float* leak;
   const int32_t* input_slot;
   const float* ga_in;     // ga^(s) [N][Bp] (gathered); nullptr: no edge pass (init)
@@ -433,30 +526,42 @@ struct BwdArgs {
   float* gbias;           // [chunks][N]
   float* gstate0;         // [B][N], written when s-1 == 0
   int first_k1;           // 1: overwrite gleak/gbias instead of accumulating
-  int first_gv;           // 1: overwrite gv_csc instead of accumulating
-  int N, B, Bp, E, n_in;
+  int first_gv;           // 1: overwrite gv instead of accumulating
+  int N, B, Bp, n_in;
 };
 
-// Row operands of the backward epilogue (this lane's column).
+// Row operands of the backward epilogue (this lane's column), including the
+// old values of the three sums it accumulates into.
 struct BwdEpi {
-  float lam, gold, gin, ak, qk;
+  float lam, gold, gin, ak, qk, gdo, glo, gbo;
   int ks;
 };
 
 __device__ __forceinline__ BwdEpi bwd_epi_load(const BwdArgs& p, const Lanes& ln, int row) {
-  BwdEpi e{0.f, 0.f, 0.f, 0.f, 0.f, -1};
-  if (row < 0 || !ln.eok) return e;
+  BwdEpi e{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, -1};
+  if (row < 0) return e;
+  // per-row values first (the same for every lane)
+  e.lam = ld_row(p.leak, row, p.N, 1);
+  if (p.a_k1 != nullptr) {
+    e.ks = ld_row(p.input_slot, row, p.N, 3);
+    // the two row sums this launch adds to (written below by lane 0 only)
+    if (!p.first_k1 && ln.lane == 0) {
+      e.glo = CK_AT(p.gleak + (size_t)blockIdx.y * p.N, row, p.N, 20);
+      e.gbo = CK_AT(p.gbias + (size_t)blockIdx.y * p.N, row, p.N, 20);
+    }
+  }
+  if (!ln.eok) return e;
   const int c = ln.ecol;
   const size_t off = (size_t)row * p.Bp + c;
   [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
-  e.lam = CK_AT(p.leak, row, p.N, 1);
   if (p.ga_in != nullptr) e.gold = CK_AT(p.gh, off, NBp, 12);
   if (c < p.B) {
     if (p.G_t) e.gin = CK_AT(p.G_t, (size_t)c * p.N + row, (size_t)p.B * p.N, 13);
     if (p.a_k1 != nullptr) {
       e.ak = CK_AT(p.a_k1, off, NBp, 14);
       e.qk = CK_AT(p.h_k1, off, NBp, 15);
-      e.ks = CK_AT(p.input_slot, row, p.N, 3);
+      if (e.ks >= 0)
+        e.gdo = CK_AT(p.gdrives_t, (size_t)e.ks * p.B + c, (size_t)p.n_in * p.B, 17);
     }
   }
   return e;
@@ -485,7 +590,8 @@ __device__ __forceinline__ void bwd_epilogue(const BwdArgs& p, const Lanes& ln, 
       lsum = g * (tanhf(e.ak) - e.qk);
       ga = g * e.lam * sech2f(e.ak);
       bsum = ga;
-      if (e.ks >= 0) CK_AT(p.gdrives_t, (size_t)e.ks * p.B + c, (size_t)p.n_in * p.B, 17) += ga;
+      if (e.ks >= 0)
+        CK_AT(p.gdrives_t, (size_t)e.ks * p.B + c, (size_t)p.n_in * p.B, 17) = e.gdo + ga;
     } else {
       g = 0.f;
     }
@@ -495,104 +601,130 @@ __device__ __forceinline__ void bwd_epilogue(const BwdArgs& p, const Lanes& ln, 
   lsum = epilogue_sum<L>(lsum, ln.slot);
   bsum = epilogue_sum<L>(bsum, ln.slot);
   if (ln.lane == 0) {
-    float& gl = CK_AT(p.gleak + (size_t)blockIdx.y * p.N, row, p.N, 20);
-    float& gb = CK_AT(p.gbias + (size_t)blockIdx.y * p.N, row, p.N, 20);
-    gl = p.first_k1 ? lsum : gl + lsum;
-    gb = p.first_k1 ? bsum : gb + bsum;
+    CK_AT(p.gleak + (size_t)blockIdx.y * p.N, row, p.N, 20) = p.first_k1 ? lsum : e.glo + lsum;
+    CK_AT(p.gbias + (size_t)blockIdx.y * p.N, row, p.N, 20) = p.first_k1 ? bsum : e.gbo + bsum;
   }
 }
 
 template <int L>
 __global__ __launch_bounds__(waves_for_lanes(L) * 64) void bwd_step(BwdArgs p) {
-  using G = Geom<L>;
+  using Gm = Geom<L>;
+  using Pp = Pipe<L, kBwdGroup>;
   constexpr int W = waves_for_lanes(L);
-  constexpr int P = G::P, I = G::I, EB = G::EB;
-  constexpr int NSUB = (kBatchEdges + EB - 1) / EB;
+  constexpr int P = Gm::P, I = Gm::I, EB = Gm::EB;
+  constexpr int NSUB = Pp::NSUB, NU = Pp::NU, TU = Pp::TU, TE = Pp::TE;
   __shared__ float4 red[2 * W][16];  // partial sums of pieces, by piece number
   const Lanes ln = lanes<L>(p.Bp);
   const int wave = __builtin_amdgcn_readfirstlane(ln.wave);
-  const int colc = ln.ok ? ln.col : 0;
-  const int4* bt = p.batches + ((size_t)blockIdx.x * W + wave) * p.KB;
+  const uint32_t colb = (uint32_t)(ln.ok ? ln.col : 0) * 4u;
+  const uint32_t rowb = (uint32_t)p.Bp * 4u;
+  [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
+  const size_t wv = (size_t)blockIdx.x * W + wave;
+  const int4* bt = p.batches + wv * p.KB;
+  const size_t slot0 = wv * p.KB * kBatchEdges;
   // the seeding launch (no ga_in) has no edge pass: every batch counts as empty
   const bool edges = p.ga_in != nullptr;
-  float* gv = p.gv_csc + (size_t)blockIdx.y * p.E;
+  float* gv = p.gv + (size_t)blockIdx.y * p.slots;
   // in gather round (sb, j) slot q handles batch edge sb*EB + j*P + q; the
   // edge term of round (sb, j = sub) is kept by lane (q, sub)
   const bool keeps = ln.slot < P && ln.sub < I;
   const int4 idle = make_int4(-1, 0, 0, 0);
   const int first_info = p.KB > 0 ? CK_AT(bt, 0, p.KB, 10).w : 0;
+  const uint32_t pbytes = (uint32_t)NBp * 4u;
+  const __amdgpu_buffer_rsrc_t gsrc = plane_rsrc(p.ga_in, pbytes);
   float4 acc = f4(0.f);
   float4 hj = f4(0.f);
-  BwdEpi eo{0.f, 0.f, 0.f, 0.f, 0.f, -1};
-  for (int g0 = 0; g0 < p.KB; g0 += kGroup) {
-    int4 ent = (ln.lane < kGroup && g0 + ln.lane < p.KB) ? CK_AT(bt, g0 + ln.lane, p.KB, 10) : idle;
-    if (!edges) ent.z = 0;
-    if (__builtin_amdgcn_readlane(ent.x, 0) < 0) break;
-    int cb[kGroup];
-    float wb[kGroup], gb_old[kGroup][NSUB];
+  BwdEpi eo{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, -1};
+  for (int g0 = 0; g0 < p.KB; g0 += kBwdGroup) {
+    const int4 ent = (ln.lane < kBwdGroup && g0 + ln.lane < p.KB)
+                         ? CK_AT(bt, g0 + ln.lane, p.KB, 10) : idle;
+    int cb[kBwdGroup];
+    float wb[kBwdGroup];
 #pragma unroll
-    for (int q = 0; q < kGroup; ++q) {
-      const int4 d = lane_entry(ent, q);
-      batch_edges(d, p.t_col_idx, p.v_csc, ln.lane, p.E, cb[q], wb[q]);
-#pragma unroll
-      for (int sb = 0; sb < NSUB; ++sb) {
-        const int e = sb * EB + ln.sub * P + ln.slot;
-        gb_old[q][sb] = (d.x >= 0 && d.z > 0 && !p.first_gv)
-                            ? CK_AT(gv, d.y + min(e, d.z - 1), p.E, 21)
-                            : 0.f;
+    for (int q = 0; q < kBwdGroup; ++q) {
+      cb[q] = -1;
+      wb[q] = 0.f;
+      if (edges && g0 + q < p.KB) {
+        const int2 pe = CK_AT(p.pedge, slot0 + (size_t)(g0 + q) * kBatchEdges + ln.lane, p.slots, 8);
+        cb[q] = pe.x;
+        wb[q] = __int_as_float(pe.y);
       }
     }
+    const int nq = group_entries<kBwdGroup>(ent, ln.lane);
+    if (nq == 0) break;
+    int4 dq[kBwdGroup];  // the entries as wave-uniform values
 #pragma unroll
-    for (int q = 0; q < kGroup; ++q) {
-      const int4 d = lane_entry(ent, q);
-      if (d.x < 0) break;  // end of this wave's list (uniform)
-      if (d.w & kInfoFirstBit) {
-        // the row's own h^(s-1) (edge dot products) and epilogue operands,
-        // requested before this batch's gathers so they arrive with them
-        if (d.z > 0)
-          hj = ld4c(p.h_sm1, ((uint32_t)d.x * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
-                    (size_t)p.N * p.Bp, 23);
-        if (!(d.w & kInfoPieceBit)) eo = bwd_epi_load(p, ln, d.x);
+    for (int q = 0; q < kBwdGroup; ++q) dq[q] = lane_entry(ent, q);
+    float4 gav[TU][I];
+    float gold[TU];
+    float4 hr[TE];
+#pragma unroll
+    for (int u = 0; u < NU + TU; ++u) {
+      if (u >= TU) {  // consume unit u - TU
+        const int uc = u - TU, q = uc / NSUB, sb = uc % NSUB;
+        if (q < nq) {
+          const int4 d = dq[q];
+          const int cnt = edges ? d.z : 0;
+          if (sb == 0 && (d.w & kInfoFirstBit)) {
+            hj = hr[q % TE];
+            // requested here, they arrive while the row's gathers are consumed
+            if (!(d.w & kInfoPieceBit)) eo = bwd_epi_load(p, ln, d.x);
+          }
+          if (sb * EB < cnt) {
+            float mine = 0.f;
+#pragma unroll
+            for (int j = 0; j < I; ++j) {
+              if (sb * EB + j * P >= cnt) break;  // past the batch's last edge (uniform)
+              const int e = sb * EB + j * P + ln.slot;
+              const float wj = lane_or(__shfl(wb[q], e & 63), e, 0.f);
+              const float4 g4 = gav[uc % TU][j];
+              acc = fma4(wj, g4, acc);
+              const float tot = slot_sum<L>(dot4(g4, hj), ln.slot);
+              if (ln.sub == j) mine = tot;
+            }
+            const int ek = sb * EB + ln.sub * P + ln.slot;
+            if (keeps && ek < cnt)
+              CK_AT(gv, slot0 + (size_t)(g0 + q) * kBatchEdges + ek, p.slots, 22) =
+                  gold[uc % TU] + mine;
+          }
+          if (sb == NSUB - 1 && (d.w & kInfoLastBit)) {
+            acc = sum_slots<L>(acc, ln.sub);
+            if (d.w & kInfoPieceBit) {
+              if (ln.slot == 0) red[piece_slot<W>(d.w)][ln.sub] = acc;
+            } else {
+              bwd_epilogue<L>(p, ln, d.x, acc, eo);
+            }
+            acc = f4(0.f);
+          }
+        }
       }
+      if (u < NU) {  // issue unit u into the slot just freed
+        const int q = u / NSUB, sb = u % NSUB;
+        if (q < nq) {
+          const int4 d = dq[q];
+          const int cnt = edges ? d.z : 0;
+          if (sb * EB < cnt) {
 #pragma unroll
-      for (int sb = 0; sb < NSUB; ++sb) {
-        if (sb * EB >= d.z) break;  // no edges left in this batch (uniform)
-        float4 gav[I];
-        float wj[I];
-#pragma unroll
-        for (int j = 0; j < I; ++j) {
-          const int e = sb * EB + j * P + ln.slot;
-          const int cj = __shfl(cb[q], e);
-          wj[j] = __shfl(wb[q], e);
-          gav[j] = ld4c(p.ga_in, ((uint32_t)cj * (uint32_t)p.Bp + (uint32_t)colc) * 4u,
-                        (size_t)p.N * p.Bp, 24);
+            for (int j = 0; j < I; ++j) {
+              if (sb * EB + j * P >= cnt) break;  // past the batch's last edge (uniform)
+              const int e = sb * EB + j * P + ln.slot;
+              const int cj = lane_or(__shfl(cb[q], e & 63), e, -1);
+              gav[u % TU][j] = gather4(gsrc, (cj >= 0 && ln.ok) ? (uint32_t)cj * rowb + colb : kNoRow,
+                                       pbytes, 24);
+            }
+            const int ek = sb * EB + ln.sub * P + ln.slot;
+            gold[u % TU] = (keeps && ek < cnt && !p.first_gv)
+                               ? CK_AT(gv, slot0 + (size_t)(g0 + q) * kBatchEdges + ek, p.slots, 21)
+                               : 0.f;
+          }
+          if (sb == 0)  // the row's own h^(s-1), for the edge dot products
+            hr[q % TE] = ((d.w & kInfoFirstBit) && cnt > 0)
+                             ? ld4c(p.h_sm1, (uint32_t)d.x * rowb + colb, NBp, 23) : f4(0.f);
         }
-        float mine = 0.f;
-#pragma unroll
-        for (int j = 0; j < I; ++j) {
-          const bool use = ln.ok && sb * EB + j * P + ln.slot < d.z;
-          const float4 g4 = use ? gav[j] : f4(0.f);
-          acc = fma4(wj[j], g4, acc);
-          const float tot = slot_sum<L>(dot4(g4, hj), ln.slot);
-          if (ln.sub == j) mine = tot;
-        }
-        const int e = sb * EB + ln.sub * P + ln.slot;
-        if (keeps && e < d.z) CK_AT(gv, d.y + e, p.E, 22) = gb_old[q][sb] + mine;
-      }
-      if (d.w & kInfoLastBit) {
-        acc = sum_slots<L>(acc, ln.sub);
-        if (d.w & kInfoPieceBit) {
-          if (ln.slot == 0) red[piece_slot<W>(d.w)][ln.sub] = acc;
-        } else {
-          bwd_epilogue<L>(p, ln, d.x, acc, eo);
-        }
-        acc = f4(0.f);
       }
     }
   }
   if (first_info & kInfoGroupBit) {
-    // the wave holding a split row's last piece (its first segment) adds
-    // the row's pieces in piece order; its operand loads overlap the barrier
     const int4 d0 = CK_AT(bt, 0, p.KB, 10);
     const bool combine = d0.x >= 0 && (d0.w & kInfoCombineBit);
     const BwdEpi ce = bwd_epi_load(p, ln, combine ? d0.x : -1);
@@ -608,21 +740,28 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void bwd_step(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------- small kernels
-__global__ void gather_f32(const float* __restrict__ src, const int32_t* __restrict__ idx,
-                           int64_t n, float* __restrict__ dst) {
-  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k < n) dst[k] = src[idx[k]];
-}
 
-// dst[idx[k]] = sum over chunks c (ascending) of src[c][k]
+// dst[idx[k]] = sum over chunks c (ascending) of src[c][k], for idx[k] >= 0
 __global__ void scatter_sum_f32(const float* __restrict__ src, int chunks,
                                 const int32_t* __restrict__ idx, int64_t n,
                                 float* __restrict__ dst) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= n) return;
+  const int32_t i = idx[k];
+  if (i < 0) return;
   float s = src[k];
   for (int c = 1; c < chunks; ++c) s += src[(size_t)c * n + k];
-  dst[idx[k]] = s;
+  dst[i] = s;
+}
+
+// Padded edge slot k of a schedule: {its node (or -1), bits of its edge value
+// (0 for an empty slot)}, from the caller-ordered edge values.
+__global__ void pack_edges(const float* __restrict__ values, const int32_t* __restrict__ pcol,
+                           const int32_t* __restrict__ pperm, int64_t n, int2* __restrict__ out) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  const int32_t i = pperm[k];
+  out[k] = make_int2(pcol[k], i >= 0 ? __float_as_int(values[i]) : 0);
 }
 
 // [B][N] -> [N][Bp] with zero padding columns
@@ -666,6 +805,8 @@ using KT = Tables<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>;
 struct Dims {
   int64_t N, E, n_in, T, B, M, S, Bp;
   int L, chunks;
+  int wide;                // schedule index: 1 for 16-wave workgroups, 0 for 8-wave
+  int64_t slots_f, slots_b;  // padded edge slots of the forward / backward schedule
   size_t plane;  // floats per [N][Bp] plane
 };
 
@@ -678,8 +819,8 @@ struct WsLayout {
 WsLayout ws_layout(const Dims& d) {
   WsLayout w;
   size_t o = 0;
-  w.v = o;   o = align256(o + (size_t)std::max<int64_t>(d.E, 1) * 4);
-  w.gv = o;  o = align256(o + (size_t)d.chunks * std::max<int64_t>(d.E, 1) * 4);
+  w.v = o;   o = align256(o + (size_t)std::max<int64_t>({d.slots_f, d.slots_b, 1}) * 8);
+  w.gv = o;  o = align256(o + (size_t)d.chunks * std::max<int64_t>(d.slots_b, 1) * 4);
   w.h0 = o;  o = align256(o + d.plane * 4);
   w.gh = o;  o = align256(o + d.plane * 4);
   w.ga0 = o; o = align256(o + d.plane * 4);
@@ -713,6 +854,9 @@ ck_status make_dims(const ck_graph* g, int64_t T, int64_t B, int64_t M, Dims* d)
   d->Bp = Bp;
   d->L = Bp <= kChunkCols ? (int)(Bp / 4) : 16;
   d->chunks = (int)((Bp + kChunkCols - 1) / kChunkCols);
+  d->wide = waves_for_lanes(d->L) == 16 ? 1 : 0;
+  d->slots_f = g->fwd[d->wide].slots;
+  d->slots_b = g->bwd[d->wide].slots;
   d->plane = (size_t)g->N * Bp;
   return CK_OK;
 }
@@ -758,28 +902,28 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
     return CK_ERR_WORKSPACE;
   }
   char* wsb = static_cast<char*>(workspace);
-  float* v_csr = reinterpret_cast<float*>(wsb + ws.v);
+  int2* pedge = reinterpret_cast<int2*>(wsb + ws.v);
   float* h0 = reinterpret_cast<float*>(wsb + ws.h0);
   float* hplanes = static_cast<float*>(saved);
   float* aplanes = hplanes + (size_t)d.S * d.plane;
-  if (d.E > 0) gather_f32<<<grid1(d.E), 256, 0, stream>>>(edge_values, g->perm, d.E, v_csr);
+  const Schedule& sc = g->fwd[d.wide];
+  if (d.E > 0)
+    pack_edges<<<grid1(sc.slots), 256, 0, stream>>>(edge_values, sc.pcol, sc.pperm, sc.slots, pedge);
   to_node_major<<<grid1((int64_t)d.plane), 256, 0, stream>>>(state0, (int)d.N, (int)d.B,
                                                              (int)d.Bp, h0);
   const FwdFn kern = KT::fwd[d.L - 1];
-  const Schedule& sc = g->fwd[waves_for_lanes(d.L) == 16 ? 1 : 0];
   const dim3 grid(sc.num_wgs, d.chunks), block(sc.waves * 64);
   FwdArgs a{};
   a.batches = sc.batches;
   a.KB = sc.KB;
-  a.col_idx = g->col_idx;
-  a.v_csr = v_csr;
+  a.pedge = pedge;
+  a.slots = sc.slots;
   a.leak = leak;
   a.bias = bias;
   a.input_slot = g->input_slot;
   a.N = (int)d.N;
   a.B = (int)d.B;
   a.Bp = (int)d.Bp;
-  a.E = (int)d.E;
   a.n_in = (int)d.n_in;
   for (int64_t s = 1; s <= d.S; ++s) {
     const int64_t t = (s - 1) / d.M;
@@ -837,8 +981,8 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
     return CK_ERR_WORKSPACE;
   }
   char* wsb = static_cast<char*>(workspace);
-  float* v_csc = reinterpret_cast<float*>(wsb + ws.v);
-  float* gv_csc = reinterpret_cast<float*>(wsb + ws.gv);
+  int2* pedge = reinterpret_cast<int2*>(wsb + ws.v);
+  float* gv = reinterpret_cast<float*>(wsb + ws.gv);
   float* h0 = reinterpret_cast<float*>(wsb + ws.h0);
   float* gh = reinterpret_cast<float*>(wsb + ws.gh);
   float* gabuf[2] = {reinterpret_cast<float*>(wsb + ws.ga0), reinterpret_cast<float*>(wsb + ws.ga1)};
@@ -846,20 +990,21 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
   const float* aplanes = hplanes + (size_t)d.S * d.plane;
   auto hplane = [&](int64_t s) { return s == 0 ? h0 : hplanes + (size_t)(s - 1) * d.plane; };
   auto aplane = [&](int64_t s) { return aplanes + (size_t)(s - 1) * d.plane; };
-  if (d.E > 0) gather_f32<<<grid1(d.E), 256, 0, stream>>>(edge_values, g->t_perm, d.E, v_csc);
+  const Schedule& sc = g->bwd[d.wide];
+  if (d.E > 0)
+    pack_edges<<<grid1(sc.slots), 256, 0, stream>>>(edge_values, sc.pcol, sc.pperm, sc.slots, pedge);
   to_node_major<<<grid1((int64_t)d.plane), 256, 0, stream>>>(state0, (int)d.N, (int)d.B,
                                                              (int)d.Bp, h0);
   if (d.n_in > 0)
     zero_f32<<<grid1(d.T * d.n_in * d.B), 256, 0, stream>>>(grad_drives, d.T * d.n_in * d.B);
   const BwdFn kern = KT::bwd[d.L - 1];
-  const Schedule& sc = g->bwd[waves_for_lanes(d.L) == 16 ? 1 : 0];
   const dim3 grid(sc.num_wgs, d.chunks), block(sc.waves * 64);
   BwdArgs a{};
   a.batches = sc.batches;
   a.KB = sc.KB;
-  a.t_col_idx = g->t_col_idx;
-  a.v_csc = v_csc;
-  a.gv_csc = gv_csc;
+  a.pedge = pedge;
+  a.gv = gv;
+  a.slots = sc.slots;
   a.gh = gh;
   a.leak = leak;
   a.input_slot = g->input_slot;
@@ -870,7 +1015,6 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
   a.N = (int)d.N;
   a.B = (int)d.B;
   a.Bp = (int)d.Bp;
-  a.E = (int)d.E;
   a.n_in = (int)d.n_in;
   // Launch "s" covers the edge pass of microstep s and the elementwise pass of
   // microstep s-1; launch S+1 has no edge pass and seeds g^(S) = G[T-1].
@@ -902,8 +1046,8 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
     sum_chunks<<<grid1(d.N), 256, 0, stream>>>(a.gbias, d.chunks, d.N, grad_bias);
   }
   if (d.E > 0)
-    scatter_sum_f32<<<grid1(d.E), 256, 0, stream>>>(gv_csc, d.chunks, g->t_perm, d.E,
-                                                    grad_edge_values);
+    scatter_sum_f32<<<grid1(sc.slots), 256, 0, stream>>>(gv, d.chunks, sc.pperm, sc.slots,
+                                                         grad_edge_values);
   CK_HIP_TRY(hipGetLastError());
 #ifdef CK_CHECKED
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
