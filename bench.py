@@ -110,7 +110,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the recurrence would "
-              f"shard over the batch across GPUs, which this build does not implement.",
+              f"shard over the batch across GPUs, which is not implemented here.",
               file=sys.stderr)
         sys.exit(2)
 

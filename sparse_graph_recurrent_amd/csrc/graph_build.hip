@@ -281,12 +281,24 @@ __global__ void pad_edges(const int4* __restrict__ table, int64_t slots,
   pperm[s] = live ? perm[t.y + k] : -1;
 }
 
+// On the device the y field of a table entry carries the row's input slot
+// (the kernels find a batch's edges by position in the padded slots, so the
+// edge offset is no longer needed there): the row's drive can then be
+// requested as soon as the entry arrives.
+__global__ void entry_input_slots(int4* __restrict__ table, int64_t n,
+                                  const int32_t* __restrict__ input_slot) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  const int4 e = table[t];
+  if (e.x >= 0) table[t].y = input_slot[e.x];
+}
+
 // Plan and upload the schedule of one orientation (row pointers ptr, edge
 // columns col and caller indices perm in compressed order) for `waves`-wave
 // workgroups, with its padded edge slots.
 ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, const int32_t* col,
-                         const int32_t* perm, int num_cus, int waves, hipStream_t stream,
-                         Schedule* out) {
+                         const int32_t* perm, const int32_t* input_slot, int num_cus, int waves,
+                         hipStream_t stream, Schedule* out) {
   static_assert(sizeof(BatchEntry) == sizeof(int4), "batch entries are read as int4");
   SchedulePlan plan;
   plan_schedule(ptr.data(), N, num_cus, waves, &plan);
@@ -306,6 +318,8 @@ ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, const int32
   CK_HIP_TRY(hipMalloc(&out->pperm, slots * sizeof(int32_t)));
   pad_edges<<<grid_for(slots, 256), 256, 0, stream>>>(out->batches, slots, col, perm, out->pcol,
                                                        out->pperm);
+  const int64_t entries = (int64_t)plan.table.size();
+  entry_input_slots<<<grid_for(entries, 256), 256, 0, stream>>>(out->batches, entries, input_slot);
   CK_HIP_TRY(hipGetLastError());
   return CK_OK;
 }
@@ -424,9 +438,11 @@ extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int
   }
   for (int k = 0; k < 2; ++k) {
     const int waves = k == 0 ? 8 : 16;
-    rc = build_schedule(hptr, N, g->col_idx, g->perm, num_cus, waves, stream, &g->fwd[k]);
+    rc = build_schedule(hptr, N, g->col_idx, g->perm, g->input_slot, num_cus, waves, stream,
+                        &g->fwd[k]);
     if (rc != CK_OK) return fail(rc);
-    rc = build_schedule(htptr, N, g->t_col_idx, g->t_perm, num_cus, waves, stream, &g->bwd[k]);
+    rc = build_schedule(htptr, N, g->t_col_idx, g->t_perm, g->input_slot, num_cus, waves,
+                        stream, &g->bwd[k]);
     if (rc != CK_OK) return fail(rc);
   }
   CK_GB_TRY(hipStreamSynchronize(stream));

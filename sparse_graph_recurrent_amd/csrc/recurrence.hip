@@ -353,12 +353,10 @@ struct FwdArgs {
   int KB;
   const float* leak;
   const float* bias;
-  const int32_t* input_slot;
   const float* drives_t;  // [n_in][B] of the current input step (nullptr if n_in == 0)
   const float* h_prev;    // [N][Bp]
   float* h_next;          // [N][Bp]
   float* a_next;          // [N][Bp]
-  float* out_t;           // [B][N] or nullptr when s is not the last microstep of a step
   int N, B, Bp, n_in;
 };
 
@@ -367,13 +365,13 @@ struct FwdEpi {
   float hp, lam, bi, dv;
 };
 
-__device__ __forceinline__ FwdEpi fwd_epi_load(const FwdArgs& p, const Lanes& ln, int row) {
+// row: the node (or -1 for none); ks: its input slot from the schedule entry
+__device__ __forceinline__ FwdEpi fwd_epi_load(const FwdArgs& p, const Lanes& ln, int row, int ks) {
   FwdEpi e{0.f, 0.f, 0.f, 0.f};
   if (row < 0) return e;
   // per-row values first (the same for every lane)
   e.lam = ld_row(p.leak, row, p.N, 1);
   e.bi = ld_row(p.bias, row, p.N, 2);
-  const int ks = ld_row(p.input_slot, row, p.N, 3);
   if (!ln.eok) return e;
   [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
   e.hp = CK_AT(p.h_prev, (size_t)row * p.Bp + ln.ecol, NBp, 0);
@@ -393,7 +391,6 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& p, const Lanes& ln, 
   [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
   CK_AT(p.h_next, off, NBp, 5) = h;
   CK_AT(p.a_next, off, NBp, 6) = a;
-  if (p.out_t && c < p.B) CK_AT(p.out_t, (size_t)c * p.N + row, (size_t)p.B * p.N, 7) = h;
 }
 
 template <int L>
@@ -448,12 +445,25 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
           const int4 d = dq[q];
           if (sb == 0 && (d.w & kInfoFirstBit) && !(d.w & kInfoPieceBit)) eo = er[q % TE];
           if (sb * EB < d.z) {
+            // rounds past the batch's last edge hold zero rows and weights,
+            // so up to 8 rounds run without a branch and all weight shuffles
+            // go first (wider rows keep the register-lean per-round form)
+            if constexpr (I <= 8) {
+              float wj[I];
 #pragma unroll
-            for (int j = 0; j < I; ++j) {
-              if (sb * EB + j * P >= d.z) break;  // past the batch's last edge (uniform)
-              const int e = sb * EB + j * P + ln.slot;
-              const float wj = lane_or(__shfl(wb[q], e & 63), e, 0.f);
-              acc = fma4(wj, hv[uc % TU][j], acc);
+              for (int j = 0; j < I; ++j) {
+                const int e = sb * EB + j * P + ln.slot;
+                wj[j] = lane_or(__shfl(wb[q], e & 63), e, 0.f);
+              }
+#pragma unroll
+              for (int j = 0; j < I; ++j) acc = fma4(wj[j], hv[uc % TU][j], acc);
+            } else {
+#pragma unroll
+              for (int j = 0; j < I; ++j) {
+                if (sb * EB + j * P >= d.z) break;  // past the batch's last edge (uniform)
+                const int e = sb * EB + j * P + ln.slot;
+                acc = fma4(lane_or(__shfl(wb[q], e & 63), e, 0.f), hv[uc % TU][j], acc);
+              }
             }
           }
           if (sb == NSUB - 1 && (d.w & kInfoLastBit)) {  // the row (or piece) is complete
@@ -474,7 +484,10 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
           if (sb * EB < d.z) {
 #pragma unroll
             for (int j = 0; j < I; ++j) {
-              if (sb * EB + j * P >= d.z) break;  // past the batch's last edge (uniform)
+              if (sb * EB + j * P >= d.z) {  // past the batch's last edge (uniform): no load
+                hv[u % TU][j] = f4(0.f);
+                continue;
+              }
               const int e = sb * EB + j * P + ln.slot;
               const int cj = lane_or(__shfl(cb[q], e & 63), e, -1);
               hv[u % TU][j] = gather4(hsrc, (cj >= 0 && ln.ok) ? (uint32_t)cj * rowb + colb : kNoRow,
@@ -483,7 +496,7 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
           }
           if (sb == 0)
             er[q % TE] = fwd_epi_load(
-                p, ln, ((d.w & kInfoFirstBit) && !(d.w & kInfoPieceBit)) ? d.x : -1);
+                p, ln, ((d.w & kInfoFirstBit) && !(d.w & kInfoPieceBit)) ? d.x : -1, d.y);
         }
       }
     }
@@ -493,7 +506,7 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
     // row's pieces in piece order; its operand loads overlap the barrier
     const int4 d0 = CK_AT(bt, 0, p.KB, 10);
     const bool combine = d0.x >= 0 && (d0.w & kInfoCombineBit);
-    const FwdEpi ce = fwd_epi_load(p, ln, combine ? d0.x : -1);
+    const FwdEpi ce = fwd_epi_load(p, ln, combine ? d0.x : -1, d0.y);
     __syncthreads();
     if (combine) {
       int q0, q1;
@@ -512,7 +525,6 @@ struct BwdArgs {
   int64_t slots;
   int KB;
   const float* leak;
-  const int32_t* input_slot;
   const float* ga_in;     // ga^(s) [N][Bp] (gathered); nullptr: no edge pass (init)
   const float* h_sm1;     // h^(s-1) [N][Bp]
   float* gh;              // in: g^(s) (ignored when ga_in == nullptr), out: g^(s-1)
@@ -537,13 +549,14 @@ struct BwdEpi {
   int ks;
 };
 
-__device__ __forceinline__ BwdEpi bwd_epi_load(const BwdArgs& p, const Lanes& ln, int row) {
+// row: the node (or -1 for none); ks: its input slot from the schedule entry
+__device__ __forceinline__ BwdEpi bwd_epi_load(const BwdArgs& p, const Lanes& ln, int row, int ks) {
   BwdEpi e{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, -1};
   if (row < 0) return e;
   // per-row values first (the same for every lane)
   e.lam = ld_row(p.leak, row, p.N, 1);
   if (p.a_k1 != nullptr) {
-    e.ks = ld_row(p.input_slot, row, p.N, 3);
+    e.ks = ks;
     // the two row sums this launch adds to (written below by lane 0 only)
     if (!p.first_k1 && ln.lane == 0) {
       e.glo = CK_AT(p.gleak + (size_t)blockIdx.y * p.N, row, p.N, 20);
@@ -668,17 +681,19 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void bwd_step(BwdArgs p) {
           if (sb == 0 && (d.w & kInfoFirstBit)) {
             hj = hr[q % TE];
             // requested here, they arrive while the row's gathers are consumed
-            if (!(d.w & kInfoPieceBit)) eo = bwd_epi_load(p, ln, d.x);
+            if (!(d.w & kInfoPieceBit)) eo = bwd_epi_load(p, ln, d.x, d.y);
           }
           if (sb * EB < cnt) {
+            // one branch per round: the backward's rounds carry more arithmetic
+            // (the edge dot products), which a branch-free form would spend on
+            // rounds past the batch's end
             float mine = 0.f;
 #pragma unroll
             for (int j = 0; j < I; ++j) {
               if (sb * EB + j * P >= cnt) break;  // past the batch's last edge (uniform)
               const int e = sb * EB + j * P + ln.slot;
-              const float wj = lane_or(__shfl(wb[q], e & 63), e, 0.f);
               const float4 g4 = gav[uc % TU][j];
-              acc = fma4(wj, g4, acc);
+              acc = fma4(lane_or(__shfl(wb[q], e & 63), e, 0.f), g4, acc);
               const float tot = slot_sum<L>(dot4(g4, hj), ln.slot);
               if (ln.sub == j) mine = tot;
             }
@@ -727,7 +742,7 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void bwd_step(BwdArgs p) {
   if (first_info & kInfoGroupBit) {
     const int4 d0 = CK_AT(bt, 0, p.KB, 10);
     const bool combine = d0.x >= 0 && (d0.w & kInfoCombineBit);
-    const BwdEpi ce = bwd_epi_load(p, ln, combine ? d0.x : -1);
+    const BwdEpi ce = bwd_epi_load(p, ln, combine ? d0.x : -1, d0.y);
     __syncthreads();
     if (combine) {
       int q0, q1;
@@ -764,13 +779,66 @@ __global__ void pack_edges(const float* __restrict__ values, const int32_t* __re
   out[k] = make_int2(pcol[k], i >= 0 ? __float_as_int(values[i]) : 0);
 }
 
-// [B][N] -> [N][Bp] with zero padding columns
-__global__ void to_node_major(const float* __restrict__ x, int N, int B, int Bp,
-                              float* __restrict__ y) {
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)N * Bp) return;
-  const int i = (int)(t / Bp), b = (int)(t % Bp);
-  y[t] = b < B ? x[(size_t)b * N + i] : 0.0f;
+// Tiled transposes between the node-major state planes [N][Bp] and the
+// caller's batch-major [B][N] layout, 32 x 32 tiles through LDS so that both
+// the reads and the writes are coalesced.  Plane t of `planes` starts at
+// t * pstride floats; grid = (ceil(N / 32), <= ceil(cols / 32), <= T), the y
+// and z loops cover what the grid does not.
+constexpr int kTile = 32;
+
+// bm[t][b][n] = planes[t][n][b] for b < B
+__global__ __launch_bounds__(256) void planes_to_batch_major(const float* __restrict__ planes,
+                                                             size_t pstride, int64_t T, int N,
+                                                             int B, int Bp, float* __restrict__ bm) {
+  __shared__ float tile[kTile][kTile + 1];
+  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
+  const int n0 = blockIdx.x * kTile;
+  for (int64_t t = blockIdx.z; t < T; t += gridDim.z)
+    for (int b0 = blockIdx.y * kTile; b0 < B; b0 += gridDim.y * kTile) {
+      const float* src = planes + (size_t)t * pstride;
+      for (int i = ty; i < kTile; i += blockDim.x / kTile) {
+        const int n = n0 + i, b = b0 + tx;
+        tile[i][tx] = (n < N && b < B) ? src[(size_t)n * Bp + b] : 0.0f;
+      }
+      __syncthreads();
+      float* dst = bm + (size_t)t * B * N;
+      for (int i = ty; i < kTile; i += blockDim.x / kTile) {
+        const int b = b0 + i, n = n0 + tx;
+        if (b < B && n < N) dst[(size_t)b * N + n] = tile[tx][i];
+      }
+      __syncthreads();
+    }
+}
+
+// planes[t][n][b] = bm[t][b][n] for b < B, 0 for B <= b < Bp
+__global__ __launch_bounds__(256) void batch_major_to_planes(const float* __restrict__ bm,
+                                                             int64_t T, int N, int B, int Bp,
+                                                             size_t pstride,
+                                                             float* __restrict__ planes) {
+  __shared__ float tile[kTile][kTile + 1];
+  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
+  const int n0 = blockIdx.x * kTile;
+  for (int64_t t = blockIdx.z; t < T; t += gridDim.z)
+    for (int b0 = blockIdx.y * kTile; b0 < Bp; b0 += gridDim.y * kTile) {
+      const float* src = bm + (size_t)t * B * N;
+      for (int i = ty; i < kTile; i += blockDim.x / kTile) {
+        const int b = b0 + i, n = n0 + tx;
+        tile[i][tx] = (b < B && n < N) ? src[(size_t)b * N + n] : 0.0f;
+      }
+      __syncthreads();
+      float* dst = planes + (size_t)t * pstride;
+      for (int i = ty; i < kTile; i += blockDim.x / kTile) {
+        const int n = n0 + i, b = b0 + tx;
+        if (n < N && b < Bp) dst[(size_t)n * Bp + b] = tile[tx][i];
+      }
+      __syncthreads();
+    }
+}
+
+inline dim3 transpose_grid(int64_t N, int64_t cols, int64_t T) {
+  return dim3((unsigned)std::max<int64_t>(1, (N + kTile - 1) / kTile),
+              (unsigned)std::min<int64_t>((cols + kTile - 1) / kTile, 65535),
+              (unsigned)std::min<int64_t>(T, 65535));
 }
 
 // out[i] = sum over chunks c (ascending) of part[c][i]
@@ -909,8 +977,8 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
   const Schedule& sc = g->fwd[d.wide];
   if (d.E > 0)
     pack_edges<<<grid1(sc.slots), 256, 0, stream>>>(edge_values, sc.pcol, sc.pperm, sc.slots, pedge);
-  to_node_major<<<grid1((int64_t)d.plane), 256, 0, stream>>>(state0, (int)d.N, (int)d.B,
-                                                             (int)d.Bp, h0);
+  batch_major_to_planes<<<transpose_grid(d.N, d.Bp, 1), 256, 0, stream>>>(
+      state0, 1, (int)d.N, (int)d.B, (int)d.Bp, d.plane, h0);
   const FwdFn kern = KT::fwd[d.L - 1];
   const dim3 grid(sc.num_wgs, d.chunks), block(sc.waves * 64);
   FwdArgs a{};
@@ -920,7 +988,6 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
   a.slots = sc.slots;
   a.leak = leak;
   a.bias = bias;
-  a.input_slot = g->input_slot;
   a.N = (int)d.N;
   a.B = (int)d.B;
   a.Bp = (int)d.Bp;
@@ -931,11 +998,14 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
     a.h_prev = s == 1 ? h0 : hplanes + (size_t)(s - 2) * d.plane;
     a.h_next = hplanes + (size_t)(s - 1) * d.plane;
     a.a_next = aplanes + (size_t)(s - 1) * d.plane;
-    a.out_t = (s % d.M == 0) ? out + (size_t)t * d.B * d.N : nullptr;
     rc = timed_launch(g_profile.fwd, stream,
                       [&] { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); });
     if (rc != CK_OK) return rc;
   }
+  // out[t] = the state after the last microstep of step t, in [B][N]
+  planes_to_batch_major<<<transpose_grid(d.N, d.B, d.T), 256, 0, stream>>>(
+      hplanes + (size_t)(d.M - 1) * d.plane, (size_t)d.M * d.plane, d.T, (int)d.N, (int)d.B,
+      (int)d.Bp, out);
   CK_HIP_TRY(hipGetLastError());
 #ifdef CK_CHECKED
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -993,8 +1063,8 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
   const Schedule& sc = g->bwd[d.wide];
   if (d.E > 0)
     pack_edges<<<grid1(sc.slots), 256, 0, stream>>>(edge_values, sc.pcol, sc.pperm, sc.slots, pedge);
-  to_node_major<<<grid1((int64_t)d.plane), 256, 0, stream>>>(state0, (int)d.N, (int)d.B,
-                                                             (int)d.Bp, h0);
+  batch_major_to_planes<<<transpose_grid(d.N, d.Bp, 1), 256, 0, stream>>>(
+      state0, 1, (int)d.N, (int)d.B, (int)d.Bp, d.plane, h0);
   if (d.n_in > 0)
     zero_f32<<<grid1(d.T * d.n_in * d.B), 256, 0, stream>>>(grad_drives, d.T * d.n_in * d.B);
   const BwdFn kern = KT::bwd[d.L - 1];
@@ -1007,7 +1077,6 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
   a.slots = sc.slots;
   a.gh = gh;
   a.leak = leak;
-  a.input_slot = g->input_slot;
   float* part = reinterpret_cast<float*>(wsb + ws.part);
   a.gleak = d.chunks > 1 ? part : grad_leak;
   a.gbias = d.chunks > 1 ? part + (size_t)d.chunks * d.N : grad_bias;

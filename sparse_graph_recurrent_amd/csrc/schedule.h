@@ -31,7 +31,9 @@ constexpr int kXcds = 8;
 // edge batches.  Wave v (= workgroup * W + wave index) walks
 // batches[v * KB .. v * KB + KB) in order until an entry with row < 0.
 // Entry = {row, kbeg, count, info}: edges [kbeg, kbeg + count) (count <=
-// kBatchEdges) of the row's compressed list.  Consecutive batches of one row on
+// kBatchEdges) of the row's compressed list.  (The uploaded device table
+// replaces kbeg by the row's input slot, or -1, once the padded edge slots
+// are built from it.)  Consecutive batches of one row on
 // one wave form a segment; a row whose batches fall on several waves (always
 // of one workgroup) is split into pieces, one segment per wave.  A piece is a
 // wave's first or last segment, so a workgroup holds at most 2 W pieces; they
