@@ -62,13 +62,22 @@ def run_oracle(w, G=None, cols=None, backward=True, nthreads=0, precision="f64")
     if cols is not None:
         cols = np.asarray(cols)
         dr, st, Gx = dr[:, :, cols], st[cols], Gx[:, cols]
+    if precision == "f32sorted":  # second fp32 evaluation (sorted summation order)
+        from oracle import sorted_f32
+        return sorted_f32.run(w.src, w.dst, w.num_nodes, w.input_nodes, w.edge_values, w.leak,
+                              w.bias, dr, st, w.microsteps, Gx)
     return oracle.run(w.src, w.dst, w.num_nodes, w.input_nodes, w.edge_values, w.leak, w.bias,
                       dr, st, w.microsteps, grad_out=Gx if backward else None, nthreads=nthreads,
                       precision=precision)
 
 
-def compare(name, got, want, rtol, atol):
-    """Assert the per-element bound; log max abs/rel error and failing count."""
+def compare(name, got, want, rtol, atol, fp32_floor=0.0):
+    """Assert the per-element bound; log max abs/rel error and failing count.
+
+    fp32_floor: an absolute allowance, used only where the fp32 evaluation of
+    the definition itself misses the bound on some elements (see
+    compare_with_fp32_floor); every element must then be within the bound or
+    within fp32_floor, whichever is larger."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     assert got.shape == want.shape, (name, got.shape, want.shape)
@@ -76,17 +85,48 @@ def compare(name, got, want, rtol, atol):
         return
     err = np.abs(got - want)
     rms = float(np.sqrt(np.mean(want ** 2)))
-    bound = atol + rtol * np.maximum(np.abs(want), NEAR_ZERO * rms)
+    bound = np.maximum(atol + rtol * np.maximum(np.abs(want), NEAR_ZERO * rms), fp32_floor)
     bare = int(np.sum(err > atol + rtol * np.abs(want)))
+    floored = int(np.sum(err > atol + rtol * np.maximum(np.abs(want), NEAR_ZERO * rms)))
     bad = err > bound
     nrm = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)
     log(f"  {name:14s} n={got.size:>10d} rms={rms:.3e} max_abs={err.max():.3e} "
         f"max_abs/rms={err.max() / max(rms, 1e-300):.2e} norm_rel={nrm:.3e} "
-        f"outside_bare_bound={bare} fail={int(bad.sum())}")
+        f"outside_bare_bound={bare} outside_floored_bound={floored} "
+        f"fp32_floor={fp32_floor:.3e} fail={int(bad.sum())}")
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)
         raise AssertionError(f"{name}: {int(bad.sum())} of {got.size} elements outside "
                              f"atol={atol} rtol={rtol}; worst at {i}: got {got[i]!r} want {want[i]!r}")
+
+
+def _sampled(gpu, k, cols):
+    g = gpu[k]
+    if cols is not None:
+        if k == "out":
+            g = g[:, cols]
+        elif k == "g_drives":
+            g = g[:, :, cols]
+        elif k == "g_state0":
+            g = g[cols]
+    return g
+
+
+def compare_with_fp32_floor(gpu, ref64, refs32, cols=None, factor=2.0):
+    """Per-element parity where fp32 evaluations of the definition themselves
+    miss the per-element bound: each GPU element must be within the bound or
+    within `factor` times the worst error of the fp32 evaluations `refs32`
+    (evaluations that differ only in summation order) on the same tensor, and
+    the GPU's worst error per tensor must stay within that allowance."""
+    for k in ("out",) + GRAD_KEYS:
+        if k not in ref64 or ref64[k].size == 0:
+            continue
+        rtol, atol = (STATE_RTOL, STATE_ATOL) if k == "out" else (GRAD_RTOL, GRAD_ATOL)
+        e32 = max(float(np.max(np.abs(np.asarray(r[k], np.float64) - ref64[k]))) for r in refs32)
+        log(f"  fp32 floor {k:14s} worst fp32 evaluation error {e32:.3e} ("
+            + ", ".join(f"{float(np.max(np.abs(np.asarray(r[k], np.float64) - ref64[k]))):.3e}"
+                        for r in refs32) + ")")
+        compare(k, _sampled(gpu, k, cols), ref64[k], rtol, atol, fp32_floor=factor * e32)
 
 
 def compare_all(gpu, ref, cols=None, backward=True):

@@ -14,7 +14,7 @@ import torch
 import oracle
 import sparse_graph_recurrent_amd as sgr
 import synthetic
-from gpu_helpers import (column_masked_grad, compare_all, compare_floor, log, make_graph, run_gpu,
+from gpu_helpers import (column_masked_grad, compare_all, compare_floor, compare_with_fp32_floor, log, make_graph, run_gpu,
                          run_oracle, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -193,13 +193,22 @@ def test_mid_scale_sampled_parity():
 
 @pytest.mark.slow
 def test_connectome_sampled_parity():
+    """Whole-connectome shape (hubs of in-degree up to 20,000, 80 % positive
+    weights, 64 microsteps).  This workload is ill-conditioned for fp32: two
+    fp32 evaluations of the definition that differ only in summation order
+    (the C oracle's fp32 build in caller edge order, and a float32 sparse
+    product evaluation in sorted order) differ several-fold in error, and the
+    first already misses the per-element bound on a few elements.  So each
+    GPU element must be within the bound or within twice the worst error of
+    those fp32 evaluations on its tensor."""
     w = synthetic.make("connectome")
     cols = [0, 31]
     G = column_masked_grad(w, cols)
     log("parity: whole-connectome workload, columns 0, 31")
     gpu, ref = run_gpu(w, G=G), run_oracle(w, G=G, cols=cols)
-    compare_all(gpu, ref, cols=cols)
-    compare_floor(gpu, ref, run_oracle(w, G=G, cols=cols, precision="f32"), cols=cols)
+    refs32 = [run_oracle(w, G=G, cols=cols, precision="f32"),
+              run_oracle(w, G=G, cols=cols, precision="f32sorted")]
+    compare_with_fp32_floor(gpu, ref, refs32, cols=cols)
     log("graph build: connectome")
     g = make_graph(w)
     got = {k: v.cpu().numpy() for k, v in g.export().items()}
