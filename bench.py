@@ -51,7 +51,11 @@ def algorithmic_bytes(N, E, n_in, B, T, M):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "flygpt_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "sparse_graph_recurrent_amd", "csrc", "recurrence.hip")
+CSRC = os.path.join(ROOT, "sparse_graph_recurrent_amd", "csrc")
+
+
+def kernel_source(kernel: str) -> str:
+    return os.path.join(CSRC, "resident.hip" if kernel.startswith("res_") else "recurrence.hip")
 
 
 def measured_traffic(kernel: str):
@@ -61,7 +65,7 @@ def measured_traffic(kernel: str):
     try:
         with open(TRAFFIC_PROFILE) as f:
             text = f.read()
-        with open(KERNEL_SOURCE, "rb") as f:
+        with open(kernel_source(kernel), "rb") as f:
             digest = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
@@ -70,7 +74,7 @@ def measured_traffic(kernel: str):
         if ":" in line and line.strip().startswith("- "):
             k, v = line.strip()[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if fields.get("source_sha256") != digest:
+    if fields.get(f"{kernel}_source_sha256", fields.get("source_sha256")) != digest:
         return None
     v = fields.get(f"{kernel}_bytes_per_launch")
     return int(v) if v else None
@@ -138,6 +142,7 @@ def main():
     ev, lk, bs, dr, st, G = (dev(x) for x in (w.edge_values, w.leak, w.bias, w.drives, w.state0,
                                                w.grad_out))
     sb, wb = sgr.recurrence_sizes(graph, T, B, M)
+    path = sgr.recurrence_path(graph, B)
     out = torch.empty((T, B, N), dtype=torch.float32, device="cuda")
     saved = torch.empty(sb, dtype=torch.uint8, device="cuda")
     ws = torch.empty(wb, dtype=torch.uint8, device="cuda")
@@ -184,16 +189,18 @@ def main():
     prof = sgr.profile_collect()
     fwd_us = 1e3 * prof["fwd_ms"] / max(prof["fwd_launches"], 1)
     bwd_us = 1e3 * prof["bwd_ms"] / max(prof["bwd_launches"], 1)
+    fwd_n = prof["fwd_launches"] // args.steps
+    bwd_n = prof["bwd_launches"] // args.steps
 
     fwd_b, bwd_b, Q = algorithmic_bytes(N, E, n_in, B, T, M)
-    # the backward kernel dominates; its launch S+1 of each step has no edge
-    # pass, so the per-launch average is taken over all S+1 launches of
-    # S microsteps' worth of backward bytes
-    bwd_per_launch_b = bwd_b * S / (S + 1)
+    # a step's S microsteps of forward (backward) bytes are spread over its
+    # forward (backward) launches: S + 1 per-microstep backward launches (the
+    # first has no edge pass), or one resident launch per direction
+    resident = path == "resident"
     if prof["bwd_ms"] >= prof["fwd_ms"]:
-        name, per_b, us = "bwd_step", bwd_per_launch_b, bwd_us
+        name, per_b, us = ("res_bwd" if resident else "bwd_step"), bwd_b * S / bwd_n, bwd_us
     else:
-        name, per_b, us = "fwd_step", fwd_b, fwd_us
+        name, per_b, us = ("res_fwd" if resident else "fwd_step"), fwd_b * S / fwd_n, fwd_us
     achieved = per_b / (us * 1e-6) / 1e9
     visits = S * E * B
     res = {
@@ -214,8 +221,8 @@ def main():
                    "parallelism": "single GPU", "hip_graph": use_graph},
         "yardstick_GBps": Q / (ms * 1e-3) / 1e9,
         "yardstick_frac_of_hbm_peak": Q / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "kernels": {"fwd_step_us": fwd_us, "bwd_step_us": bwd_us,
-                    "fwd_launches_per_step": S, "bwd_launches_per_step": S + 1},
+        "kernels": {"path": path, "fwd_launch_us": fwd_us, "bwd_launch_us": bwd_us,
+                    "fwd_launches_per_step": fwd_n, "bwd_launches_per_step": bwd_n},
         "roofline": {"bound": "hbm", "kernel": name, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(name)},

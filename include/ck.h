@@ -73,6 +73,10 @@ typedef enum {
  * Internally: the CSR by destination (rows ordered by (src, caller index)),
  * the transposed CSR by source (rows ordered by (dst, caller index)), both
  * edge permutations, the input-slot map and the degree-balanced row schedules.
+ * When the device deals a launch's workgroups evenly over 8 XCDs, num_nodes
+ * is at most 9200 and the environment variable CK_RESIDENT is not "0" at
+ * creation, it also plans the XCD-resident kernels (see
+ * ck_recurrence_path), which run a whole forward or backward in one launch.
  * The caller's edge order is kept for edge values and their gradient: the
  * permutation is invisible outside.  Validation failures return
  * CK_ERR_BAD_SIZE, CK_ERR_TOO_LARGE, CK_ERR_NULL_ARG, CK_ERR_INDEX_RANGE or
@@ -106,15 +110,40 @@ ck_status ck_graph_export(ck_graph_t g, int32_t* row_ptr, int32_t* col_idx, int3
  *                    backward: the state and the pre-activation after every
  *                    microstep (connectome-kernels README, "Design notes"),
  *                    2 * T * M * N * Bp * 4 bytes with Bp = B rounded up to a
- *                    multiple of 4 (= 2*T*M*N*B*4 when B % 4 == 0).
+ *                    multiple of 4 (= 2*T*M*N*B*4 when B % 4 == 0); on the
+ *                    XCD-resident path N is first rounded up to a multiple of
+ *                    8.  Its layout is internal.
  *   workspace_bytes  scratch needed by either forward or backward.
  */
 ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int64_t microsteps,
                               size_t* saved_bytes, size_t* workspace_bytes);
 
 /*
+ * Which kernels a call with batch B runs on this graph: *resident = 1 for the
+ * XCD-resident kernels, 0 for the per-microstep kernels.
+ *
+ * Per-microstep kernels: one fused launch per microstep and direction, the
+ * rows of all batch columns spread over every compute unit.
+ * XCD-resident kernels (graphs planned for them at creation, B <= 32): one
+ * launch per call.  Batch column group c (4 columns) is computed by the
+ * compute units of XCD c alone, which keep its whole state plane in LDS and
+ * their share of the edges in registers, and exchange each microstep's new
+ * state through their shared L2 behind a barrier local to the XCD.  Such a
+ * launch holds one workgroup on every compute unit and its workgroups wait
+ * for one another, so it must not run concurrently with other kernels on the
+ * device.  A wait that does not end within about a second raises an internal
+ * error flag; the call's outputs (or all five gradients) are then NaN.  (The
+ * poll limit of those waits is read from CK_RESIDENT_SPIN_LIMIT at graph
+ * creation, default 1048576; a negative value fails every wait at once and
+ * exists to test that failure path.)
+ * Both paths compute the same sums; results agree to rounding.
+ */
+ck_status ck_recurrence_path(ck_graph_t g, int64_t B, int* resident);
+
+/*
  * Forward over the whole window (connectome-kernels README, introduction and
- * "Use"): one fused launch per microstep.
+ * "Use"): one fused launch per microstep, or one launch on the XCD-resident
+ * path (ck_recurrence_path).
  *
  *   edge_values  fp32[E]           caller edge order
  *   leak, bias   fp32[N]
@@ -155,9 +184,9 @@ ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_values, const f
 /*
  * Measurement hook (changes no result).  While enabled (process-wide),
  * forward and backward record a pair of HIP events on the caller's stream
- * around every launch of the per-microstep kernels: the fused forward
- * microstep kernel and the fused backward step kernel (timing-only events
- * without a system-scope fence).  ck_profile_collect synchronises the device,
+ * around every launch of the main kernels: the fused forward microstep and
+ * backward step kernels, or the XCD-resident forward and backward kernels
+ * (timing-only events without a system-scope fence).  ck_profile_collect synchronises the device,
  * returns the summed kernel durations in milliseconds and the launch counts
  * since the last collect, and releases the events.  Any output pointer may be NULL.  Not meant for concurrent use from
  * several threads.

@@ -37,7 +37,8 @@ STATUS_NAMES = {
 }
 
 EXPORTED = ("ck_graph_create", "ck_graph_destroy", "ck_graph_sizes", "ck_graph_export",
-            "ck_recurrence_sizes", "ck_recurrence_forward", "ck_recurrence_backward",
+            "ck_recurrence_sizes", "ck_recurrence_path", "ck_recurrence_forward",
+            "ck_recurrence_backward",
             "ck_profile_enable", "ck_profile_collect", "ck_status_string", "ck_last_error")
 
 
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.ck_graph_sizes.argtypes = [p, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.ck_graph_export.argtypes = [p] * 9
         L.ck_recurrence_sizes.argtypes = [p, i64, i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.ck_recurrence_path.argtypes = [p, i64, ctypes.POINTER(ctypes.c_int)]
         L.ck_recurrence_forward.argtypes = [p, p, p, p, p, p, i64, i64, i64, p, p, p, sz, p]
         L.ck_recurrence_backward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p, p, p, p, p, p, sz, p]
         L.ck_profile_enable.argtypes = [ctypes.c_int]
@@ -176,6 +178,15 @@ def recurrence_sizes(graph: SparseGraph, T: int, B: int, microsteps: int):
     _check(lib().ck_recurrence_sizes(graph.handle, int(T), int(B), int(microsteps),
                                      ctypes.byref(s), ctypes.byref(w)))
     return s.value, w.value
+
+
+def recurrence_path(graph: SparseGraph, B: int) -> str:
+    """Kernels a call with batch B runs on this graph: "resident" (one launch
+    per call, each XCD computing one group of 4 batch columns) or
+    "per_microstep" (one launch per microstep)."""
+    r = ctypes.c_int()
+    _check(lib().ck_recurrence_path(graph.handle, int(B), ctypes.byref(r)))
+    return "resident" if r.value else "per_microstep"
 
 
 def _byte_buffer(nbytes: int, device) -> torch.Tensor:

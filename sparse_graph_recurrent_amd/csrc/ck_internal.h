@@ -6,6 +6,8 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <utility>
+#include <vector>
 
 #include "ck.h"
 #include "schedule.h"
@@ -20,6 +22,37 @@ struct Schedule {
   int num_wgs = 0;
   int waves = 0;            // waves per workgroup
   int KB = 0;               // batch entries per wave (padded with row = -1)
+};
+
+// Largest node count of the XCD-resident kernels: one workgroup holds a
+// whole [N + 1] x 16-byte state plane plus kResLanes 16-byte partial sums in
+// the 160 KiB of LDS of a gfx950 compute unit.
+constexpr int64_t kResMaxN = 9200;
+// XCDs of an MI355X; a launch deals its workgroups round-robin over them.
+constexpr int kResXcds = 8;
+
+// Hardware id of the XCD (accelerator complex die) the calling wave runs on.
+__device__ __forceinline__ unsigned xcc_id() {
+  unsigned x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 15u;
+}
+
+// Device copy of a ResidentPlan (see schedule.h) with its padded edge slots:
+// slot (r, j, l) = ((r * D) + j) * kResLanes + l holds edge j of lane l's
+// piece on workgroup r (coalesced per j when the lanes load their pieces).
+struct Resident {
+  int D = 0;
+  int ranks = 0;
+  int32_t* rank_rows = nullptr;   // [ranks + 1]
+  int32_t* owner_pbeg = nullptr;  // [ranks][kResLanes + 1]
+  int32_t* piece_row = nullptr;   // [ranks][kResLanes], -1 for a lane without a piece
+  int32_t* pcol = nullptr;        // [slots] node at the other end of the edge, or N (an all-zero row)
+  int32_t* pperm = nullptr;       // [slots] caller index of the edge, or -1
+  int64_t slots = 0;              // ranks * D * kResLanes
+  int blk = 0;                    // block length of two-level row sums
+  bool two_level = false;         // some row has more than blk pieces
+  int32_t* piece_blk = nullptr;   // [ranks][kResLanes] pieces in the block the lane heads, or 0
 };
 
 }  // namespace ckhip
@@ -37,6 +70,16 @@ struct ck_graph {
   int32_t* input_slot; // [N] k if the node is input_nodes[k], else -1
   ckhip::Schedule fwd[2]; // rows of the CSR (in-degree), for 8- and 16-wave workgroups
   ckhip::Schedule bwd[2]; // rows of the transposed CSR (out-degree), likewise
+  // XCD-resident kernels (one launch per call): usable when res_ok is set at
+  // creation (the device has 8 XCDs of equal size, N fits the LDS-resident
+  // plane, both orientations have a plan, and CK_RESIDENT is not "0").
+  int res_ok;
+  // polls before a resident kernel's wait gives up (CK_RESIDENT_SPIN_LIMIT
+  // at creation, default 2^20 -- about a second; a negative value makes every
+  // wait give up at once, which tests use to exercise the failure path)
+  int res_spin_limit;
+  ckhip::Resident res_fwd;  // rows of the CSR
+  ckhip::Resident res_bwd;  // rows of the transposed CSR
 };
 
 namespace ckhip {
@@ -58,3 +101,62 @@ ck_status check_graph(const ck_graph* g);
       return ck_e_ == hipErrorOutOfMemory ? CK_ERR_NOMEM : CK_ERR_HIP;              \
     }                                                                               \
   } while (0)
+
+namespace ckhip {
+
+// Measurement hook state: HIP event pairs around the main kernel launches.
+struct Profile {
+  bool enabled = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> fwd, bwd;
+};
+extern Profile g_profile;
+
+// Launch `launch()` on `stream`, bracketed by events when profiling is on.
+template <typename F>
+ck_status timed_launch(std::vector<std::pair<hipEvent_t, hipEvent_t>>& log, hipStream_t stream,
+                       F&& launch) {
+  if (!g_profile.enabled) {
+    launch();
+    return CK_OK;
+  }
+  // timing-only events: no system-scope fence (cache writeback/invalidate)
+  // around the kernel they bracket
+  hipEvent_t a, b;
+  CK_HIP_TRY(hipEventCreateWithFlags(&a, hipEventDisableSystemFence));
+  CK_HIP_TRY(hipEventCreateWithFlags(&b, hipEventDisableSystemFence));
+  CK_HIP_TRY(hipEventRecord(a, stream));
+  launch();
+  CK_HIP_TRY(hipEventRecord(b, stream));
+  log.emplace_back(a, b);
+  return CK_OK;
+}
+
+}  // namespace ckhip
+
+namespace ckhip {
+
+// Sizes of one call of the XCD-resident kernels: G = ceil(B / 4) column
+// groups (at most kResXcds), Np = N rounded up to 8 rows (a group's plane
+// slice is a whole number of 128-byte lines).
+struct ResDims {
+  int64_t N, Np, B, G, n_in, T, M, S;
+};
+// Workspace of the resident path, byte offsets.
+struct ResWs {
+  size_t pedge, h0, ctl, ga, gv, gl, gb, total;
+};
+// Allows the resident kernels their LDS (once per graph creation).
+ck_status res_prepare();
+ResWs res_ws_layout(const ck_graph* g, const ResDims& d);
+size_t res_saved_bytes(const ResDims& d);
+ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_values,
+                      const float* leak, const float* bias, const float* drives,
+                      const float* state0, float* out, void* saved, void* workspace,
+                      hipStream_t stream);
+ck_status res_backward(const ck_graph* g, const ResDims& d, const float* edge_values,
+                       const float* leak, const float* state0, const void* saved,
+                       const float* grad_out, float* grad_edge_values, float* grad_leak,
+                       float* grad_bias, float* grad_drives, float* grad_state0, void* workspace,
+                       hipStream_t stream);
+
+}  // namespace ckhip

@@ -324,6 +324,104 @@ ck_status build_schedule(const std::vector<int32_t>& ptr, int64_t N, const int32
   return CK_OK;
 }
 
+// Records the XCD of each workgroup.
+__global__ void xcc_of_workgroups(int32_t* __restrict__ out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = (int32_t)xcc_id();
+}
+
+// Resident slot q = ((r * D) + j) * kResLanes + l: edge j of lane l's piece on
+// workgroup r, or an empty slot (node N, caller index -1).
+__global__ void pad_resident(const int32_t* __restrict__ kbeg, const int32_t* __restrict__ cnt,
+                             int D, int64_t slots, const int32_t* __restrict__ col,
+                             const int32_t* __restrict__ perm, int32_t N,
+                             int32_t* __restrict__ pcol, int32_t* __restrict__ pperm) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= slots) return;
+  const int64_t l = q % kResLanes, rj = q / kResLanes;
+  const int64_t r = rj / D, j = rj % D;
+  const int64_t lane = r * kResLanes + l;
+  if (j < cnt[lane]) {
+    const int32_t k = kbeg[lane] + (int32_t)j;
+    pcol[q] = col[k];
+    pperm[q] = perm[k];
+  } else {
+    pcol[q] = N;
+    pperm[q] = -1;
+  }
+}
+
+// True when a launch of num_cus workgroups puts num_cus / kResXcds of them on
+// each of kResXcds XCDs: the grouping the resident kernels rely on (they
+// check it again themselves).
+bool xcds_as_expected(int num_cus, hipStream_t stream) {
+  if (num_cus <= 0 || num_cus % kResXcds != 0) return false;
+  int32_t* d = nullptr;
+  if (hipMalloc(&d, num_cus * sizeof(int32_t)) != hipSuccess) return false;
+  std::vector<int32_t> h(num_cus, -1);
+  xcc_of_workgroups<<<num_cus, 64, 0, stream>>>(d);
+  bool ok = hipGetLastError() == hipSuccess &&
+            hipMemcpyAsync(h.data(), d, num_cus * sizeof(int32_t), hipMemcpyDeviceToHost,
+                           stream) == hipSuccess &&
+            hipStreamSynchronize(stream) == hipSuccess;
+  (void)hipFree(d);
+  std::vector<int> per(kResXcds, 0);
+  for (int b = 0; ok && b < num_cus; ++b) {
+    ok = h[b] >= 0 && h[b] < kResXcds;
+    if (ok) ++per[h[b]];
+  }
+  for (int x = 0; ok && x < kResXcds; ++x) ok = per[x] == num_cus / kResXcds;
+  return ok;
+}
+
+ck_status build_resident(const std::vector<int32_t>& ptr, int64_t N, const int32_t* col,
+                         const int32_t* perm, int ranks, int max_lens, hipStream_t stream,
+                         Resident* out, bool* planned) {
+  ResidentPlan plan;
+  *planned = plan_resident(ptr.data(), N, ranks, max_lens, &plan);
+  if (!*planned) return CK_OK;
+  out->D = plan.D;
+  out->ranks = plan.ranks;
+  out->slots = (int64_t)plan.ranks * plan.D * kResLanes;
+  auto upload = [&](int32_t** dst, const std::vector<int32_t>& src) -> hipError_t {
+    hipError_t e = hipMalloc(dst, src.size() * sizeof(int32_t));
+    if (e == hipSuccess)
+      e = hipMemcpy(*dst, src.data(), src.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    return e;
+  };
+  CK_HIP_TRY(upload(&out->rank_rows, plan.rank_rows));
+  CK_HIP_TRY(upload(&out->owner_pbeg, plan.owner_pbeg));
+  CK_HIP_TRY(upload(&out->piece_row, plan.piece_row));
+  CK_HIP_TRY(upload(&out->piece_blk, plan.piece_blk));
+  out->blk = plan.blk;
+  out->two_level = false;
+  for (int32_t v : plan.piece_blk) out->two_level = out->two_level || v > 0;
+  int32_t *kbeg = nullptr, *cnt = nullptr;
+  hipError_t e = upload(&kbeg, plan.piece_kbeg);
+  if (e == hipSuccess) e = upload(&cnt, plan.piece_cnt);
+  if (e == hipSuccess) e = hipMalloc(&out->pcol, out->slots * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMalloc(&out->pperm, out->slots * sizeof(int32_t));
+  if (e == hipSuccess) {
+    pad_resident<<<grid_for(out->slots, 256), 256, 0, stream>>>(
+        kbeg, cnt, plan.D, out->slots, col, perm, (int32_t)N, out->pcol, out->pperm);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  (void)hipFree(kbeg);
+  (void)hipFree(cnt);
+  CK_HIP_TRY(e);
+  return CK_OK;
+}
+
+void free_resident(Resident* r) {
+  (void)hipFree(r->rank_rows);
+  (void)hipFree(r->owner_pbeg);
+  (void)hipFree(r->piece_row);
+  (void)hipFree(r->piece_blk);
+  (void)hipFree(r->pcol);
+  (void)hipFree(r->pperm);
+  *r = Resident();
+}
+
 void free_graph_arrays(ck_graph* g) {
   int32_t* arrs[] = {g->row_ptr, g->col_idx, g->perm, g->t_row_ptr, g->t_col_idx, g->t_perm,
                      g->input_slot};
@@ -334,6 +432,8 @@ void free_graph_arrays(ck_graph* g) {
       (void)hipFree(sc->pcol);
       (void)hipFree(sc->pperm);
     }
+  free_resident(&g->res_fwd);
+  free_resident(&g->res_bwd);
 }
 
 }  // namespace
@@ -446,6 +546,30 @@ extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int
     if (rc != CK_OK) return fail(rc);
   }
   CK_GB_TRY(hipStreamSynchronize(stream));
+  // XCD-resident plans (optional: without them every call takes the
+  // per-microstep kernels)
+  {
+    const char* env = getenv("CK_RESIDENT");
+    const bool wanted = !(env && env[0] == '0' && env[1] == '\0');
+    const char* spin = getenv("CK_RESIDENT_SPIN_LIMIT");
+    g->res_spin_limit = spin && spin[0] ? atoi(spin) : (1 << 20);
+    if (wanted && N <= kResMaxN && xcds_as_expected(num_cus, stream)) {
+      const int ranks = num_cus / kResXcds;
+      bool pf = false, pb = false;
+      rc = build_resident(hptr, N, g->col_idx, g->perm, ranks, kResNumPieceLens, stream,
+                          &g->res_fwd, &pf);
+      if (rc != CK_OK) return fail(rc);
+      if (pf)
+        rc = build_resident(htptr, N, g->t_col_idx, g->t_perm, ranks, kResBwdPieceLens, stream,
+                            &g->res_bwd, &pb);
+      if (rc != CK_OK) return fail(rc);
+      g->res_ok = pf && pb && res_prepare() == CK_OK ? 1 : 0;
+      if (!g->res_ok) {
+        free_resident(&g->res_fwd);
+        free_resident(&g->res_bwd);
+      }
+    }
+  }
   (void)hipFree(flags);
   (void)hipFree(seen);
   g->magic = kGraphMagic;

@@ -27,67 +27,16 @@
 #include <vector>
 
 #include "ck_internal.h"
+#include "device_math.h"
 
 namespace ckhip {
-namespace {
 
-// Measurement hook state: HIP event pairs around per-microstep launches.
-struct Profile {
-  bool enabled = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> fwd, bwd;
-};
 Profile g_profile;
 
-// Launch `launch()` on `stream`, bracketed by events when profiling is on.
-template <typename F>
-ck_status timed_launch(std::vector<std::pair<hipEvent_t, hipEvent_t>>& log, hipStream_t stream,
-                       F&& launch) {
-  if (!g_profile.enabled) {
-    launch();
-    return CK_OK;
-  }
-  // timing-only events: no system-scope fence (cache writeback/invalidate)
-  // around the kernel they bracket
-  hipEvent_t a, b;
-  CK_HIP_TRY(hipEventCreateWithFlags(&a, hipEventDisableSystemFence));
-  CK_HIP_TRY(hipEventCreateWithFlags(&b, hipEventDisableSystemFence));
-  CK_HIP_TRY(hipEventRecord(a, stream));
-  launch();
-  CK_HIP_TRY(hipEventRecord(b, stream));
-  log.emplace_back(a, b);
-  return CK_OK;
-}
+namespace {
+
 
 constexpr int kChunkCols = 64;  // columns per grid-y chunk when Bp > 64
-
-__device__ __forceinline__ float4 f4(float x) { return make_float4(x, x, x, x); }
-__device__ __forceinline__ float4 fma4(float w, float4 h, float4 acc) {
-  acc.x = fmaf(w, h.x, acc.x);
-  acc.y = fmaf(w, h.y, acc.y);
-  acc.z = fmaf(w, h.z, acc.z);
-  acc.w = fmaf(w, h.w, acc.w);
-  return acc;
-}
-__device__ __forceinline__ float4 add4(float4 a, float4 b) {
-  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-}
-__device__ __forceinline__ float4 shfl4(float4 v, int src) {
-  return make_float4(__shfl(v.x, src), __shfl(v.y, src), __shfl(v.z, src), __shfl(v.w, src));
-}
-__device__ __forceinline__ float4 shfl_xor4(float4 v, int m) {
-  return make_float4(__shfl_xor(v.x, m), __shfl_xor(v.y, m), __shfl_xor(v.z, m),
-                     __shfl_xor(v.w, m));
-}
-__device__ __forceinline__ float dot4(float4 a, float4 b) {
-  return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-}
-// sech^2(a) = 4 e^{-2|a|} / (1 + e^{-2|a|})^2, from the pre-activation itself
-// (not 1 - tanh^2, which cancels badly once |a| is a few units).
-__device__ __forceinline__ float sech2f(float a) {
-  float e = expf(-2.0f * fabsf(a));
-  float d = 1.0f + e;
-  return 4.0f * e / (d * d);
-}
 
 constexpr bool is_pow2(int x) { return (x & (x - 1)) == 0; }
 
@@ -876,6 +825,8 @@ struct Dims {
   int wide;                // schedule index: 1 for 16-wave workgroups, 0 for 8-wave
   int64_t slots_f, slots_b;  // padded edge slots of the forward / backward schedule
   size_t plane;  // floats per [N][Bp] plane
+  bool resident;  // the call runs the XCD-resident kernels (one launch per call)
+  ResDims rd;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -926,6 +877,8 @@ ck_status make_dims(const ck_graph* g, int64_t T, int64_t B, int64_t M, Dims* d)
   d->slots_f = g->fwd[d->wide].slots;
   d->slots_b = g->bwd[d->wide].slots;
   d->plane = (size_t)g->N * Bp;
+  d->resident = g->res_ok != 0 && Bp <= 4 * kResXcds;
+  d->rd = ResDims{g->N, (g->N + 7) / 8 * 8, B, Bp / 4, g->n_in, T, M, T * M};
   return CK_OK;
 }
 
@@ -942,8 +895,24 @@ extern "C" ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int
   Dims d;
   rc = make_dims(g, T, B, microsteps, &d);
   if (rc != CK_OK) return rc;
-  if (saved_bytes) *saved_bytes = 2 * (size_t)d.S * d.plane * sizeof(float);
-  if (workspace_bytes) *workspace_bytes = ws_layout(d).total;
+  if (saved_bytes)
+    *saved_bytes = d.resident ? res_saved_bytes(d.rd) : 2 * (size_t)d.S * d.plane * sizeof(float);
+  if (workspace_bytes) *workspace_bytes = d.resident ? res_ws_layout(g, d.rd).total : ws_layout(d).total;
+  return CK_OK;
+}
+
+extern "C" ck_status ck_recurrence_path(ck_graph_t g, int64_t B, int* resident) {
+  clear_error();
+  ck_status rc = check_graph(g);
+  if (rc != CK_OK) return rc;
+  if (!resident) {
+    set_error("resident output pointer is NULL");
+    return CK_ERR_NULL_ARG;
+  }
+  Dims d;
+  rc = make_dims(g, 1, B, 1, &d);
+  if (rc != CK_OK) return rc;
+  *resident = d.resident ? 1 : 0;
   return CK_OK;
 }
 
@@ -963,6 +932,15 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
       !out || !saved || !workspace) {
     set_error("NULL pointer for a non-empty tensor in forward");
     return CK_ERR_NULL_ARG;
+  }
+  if (d.resident) {
+    const size_t need = res_ws_layout(g, d.rd).total;
+    if (workspace_bytes < need) {
+      set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+      return CK_ERR_WORKSPACE;
+    }
+    return res_forward(g, d.rd, edge_values, leak, bias, drives, state0, out, saved, workspace,
+                       stream);
   }
   const WsLayout ws = ws_layout(d);
   if (workspace_bytes < ws.total) {
@@ -1044,6 +1022,15 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
       !workspace) {
     set_error("NULL pointer for a non-empty tensor in backward");
     return CK_ERR_NULL_ARG;
+  }
+  if (d.resident) {
+    const size_t need = res_ws_layout(g, d.rd).total;
+    if (workspace_bytes < need) {
+      set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+      return CK_ERR_WORKSPACE;
+    }
+    return res_backward(g, d.rd, edge_values, leak, state0, saved, grad_out, grad_edge_values,
+                        grad_leak, grad_bias, grad_drives, grad_state0, workspace, stream);
   }
   const WsLayout ws = ws_layout(d);
   if (workspace_bytes < ws.total) {

@@ -154,4 +154,105 @@ void plan_schedule(const int32_t* ptr, int64_t N, int num_cus, int waves, Schedu
   out->KB = (int)KB;
 }
 
+
+// Resident plan (see schedule.h).  For a piece length D, row i has
+// p_i = ceil(d_i / D) pieces (none for an empty row, whose owner still runs
+// its epilogue).  The rows are cut greedily into contiguous ranges of at most
+// `cap` pieces and kResLanes rows; bisection finds the smallest cap that needs
+// at most `ranks` ranges.
+namespace {
+
+bool pack_ranges(const std::vector<int64_t>& pc, int ranks, int64_t cap, std::vector<int32_t>* cut) {
+  const int64_t N = (int64_t)pc.size();
+  if (cut) cut->assign(1, 0);
+  int used = 1;
+  int64_t pieces = 0, rows = 0;
+  for (int64_t i = 0; i < N; ++i) {
+    if (pc[i] > cap) return false;
+    if (pieces + pc[i] > cap || rows + 1 > kResLanes) {
+      if (++used > ranks) return false;
+      if (cut) cut->push_back((int32_t)i);
+      pieces = 0;
+      rows = 0;
+    }
+    pieces += pc[i];
+    ++rows;
+  }
+  if (cut) {
+    while ((int)cut->size() < ranks + 1) cut->push_back((int32_t)N);
+  }
+  return true;
+}
+
+}  // namespace
+
+bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_lens, ResidentPlan* out) {
+  if (ranks <= 0 || N <= 0) return false;
+  max_lens = std::min(max_lens, kResNumPieceLens);
+  int best_D = 0;
+  int64_t best_cap = 0, best_cost = -1;
+  std::vector<int64_t> pc(N);
+  for (int li = 0; li < max_lens; ++li) {
+    const int D = kResPieceLens[li];
+    int64_t lo = 0;
+    for (int64_t i = 0; i < N; ++i) {
+      pc[i] = (ptr[i + 1] - ptr[i] + D - 1) / D;
+      lo = std::max(lo, pc[i]);
+    }
+    if (!pack_ranges(pc, ranks, kResLanes, nullptr)) continue;
+    int64_t hi = kResLanes;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (pack_ranges(pc, ranks, mid, nullptr)) hi = mid;
+      else lo = mid + 1;
+    }
+    const int64_t cost = hi * (D + 4);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_cap = hi;
+      best_D = D;
+    }
+  }
+  if (best_cost < 0) return false;
+  const int D = best_D;
+  for (int64_t i = 0; i < N; ++i) pc[i] = (ptr[i + 1] - ptr[i] + D - 1) / D;
+  ResidentPlan& p = *out;
+  p = ResidentPlan();
+  p.D = D;
+  p.ranks = ranks;
+  pack_ranges(pc, ranks, best_cap, &p.rank_rows);
+  // block length: about the square root of the largest row's piece count, so
+  // that neither level of its sum is long
+  int64_t maxp = 1;
+  for (int64_t i = 0; i < N; ++i) maxp = std::max(maxp, pc[i]);
+  int blk = 8;
+  while (blk < 32 && (int64_t)blk * blk < maxp) ++blk;
+  p.blk = blk;
+  p.piece_blk.assign((size_t)ranks * kResLanes, 0);
+  p.owner_pbeg.assign((size_t)ranks * (kResLanes + 1), 0);
+  p.piece_row.assign((size_t)ranks * kResLanes, -1);
+  p.piece_kbeg.assign((size_t)ranks * kResLanes, 0);
+  p.piece_cnt.assign((size_t)ranks * kResLanes, 0);
+  for (int r = 0; r < ranks; ++r) {
+    const int32_t r0 = p.rank_rows[r], r1 = p.rank_rows[r + 1];
+    int32_t* pb = &p.owner_pbeg[(size_t)r * (kResLanes + 1)];
+    int lane = 0;
+    for (int32_t i = r0; i < r1; ++i) {
+      pb[i - r0] = lane;
+      if (pc[i] > blk)
+        for (int64_t h = 0; h < pc[i]; h += blk)
+          p.piece_blk[(size_t)r * kResLanes + lane + h] = (int32_t)std::min<int64_t>(blk, pc[i] - h);
+      for (int32_t k = ptr[i]; k < ptr[i + 1]; k += D, ++lane) {
+        const size_t q = (size_t)r * kResLanes + lane;
+        p.piece_row[q] = i;
+        p.piece_kbeg[q] = k;
+        p.piece_cnt[q] = std::min<int32_t>(D, ptr[i + 1] - k);
+      }
+    }
+    for (int o = r1 - r0; o <= kResLanes; ++o) pb[o] = lane;
+    p.max_pieces = std::max(p.max_pieces, lane);
+  }
+  return true;
+}
+
 }  // namespace ckhip

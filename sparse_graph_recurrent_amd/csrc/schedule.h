@@ -73,4 +73,49 @@ struct SchedulePlan {
 // units.
 void plan_schedule(const int32_t* ptr, int64_t N, int num_cus, int waves, SchedulePlan* out);
 
+// ---------------------------------------------------------------------------
+// Resident plan: the split of one orientation's rows over the `ranks`
+// workgroups of one XCD for the XCD-resident kernels, which run every
+// microstep of a call in one launch.  Each XCD computes all rows for its own
+// group of batch columns, so all XCDs share one plan.
+//
+// A row of degree d is cut into ceil(d / D) pieces of at most D consecutive
+// edges; each piece is held by one thread (lane) of a workgroup of kResLanes
+// threads, in registers, for the whole launch.  Rows are cut into contiguous
+// workgroup ranges; inside a range, the pieces of its rows take consecutive
+// lanes in row order, and the row's "owner" (the range's o-th row is owned by
+// lane o) adds its pieces' partial sums in lane order.  A row of more than
+// `blk` pieces is added in two levels: the lanes at its pieces 0, blk, 2 blk,
+// ... ("block heads") first add their block of at most blk partial sums in
+// place, then the owner adds the block sums.
+constexpr int kResLanes = 1024;
+// Piece lengths the kernels are built for.
+constexpr int kResPieceLens[] = {8, 12, 16, 20, 24};
+constexpr int kResNumPieceLens = 5;
+// The backward kernel also keeps D edge-gradient sums per lane; past D = 20
+// it no longer fits in 128 registers.
+constexpr int kResBwdPieceLens = 4;
+
+struct ResidentPlan {
+  int D = 0;                        // edges per piece
+  int ranks = 0;                    // workgroups per XCD
+  int max_pieces = 0;               // pieces on the busiest workgroup
+  std::vector<int32_t> rank_rows;   // [ranks + 1]: rows of workgroup r are [rank_rows[r], rank_rows[r+1])
+  std::vector<int32_t> owner_pbeg;  // [ranks][kResLanes + 1]: the pieces of the r-th range's row o
+                                    // are lanes [owner_pbeg[o], owner_pbeg[o+1]); constant past the range
+  std::vector<int32_t> piece_row;   // [ranks][kResLanes]: row of the lane's piece, or -1
+  std::vector<int32_t> piece_kbeg;  // [ranks][kResLanes]: first edge (compressed index) of the piece
+  std::vector<int32_t> piece_cnt;   // [ranks][kResLanes]: edges in the piece (0 if none)
+  int blk = 0;                      // block length of the two-level sums
+  std::vector<int32_t> piece_blk;   // [ranks][kResLanes]: pieces in the lane's block if it is
+                                    // a block head of a row of more than blk pieces, else 0
+};
+
+// Plan the pieces of ptr[0..N] for `ranks` workgroups, choosing the piece
+// length among kResPieceLens[0 .. max_lens) that minimises the busiest
+// workgroup's (pieces x (D + 4)), an estimate of its gather work plus the
+// owners' combining.  Returns false when no length fits (a range needs more
+// than kResLanes pieces or rows).
+bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_lens, ResidentPlan* out);
+
 }  // namespace ckhip

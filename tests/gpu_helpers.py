@@ -3,6 +3,8 @@ binding (which calls the C ABI), run the oracle on the same seeded inputs, and
 compare element by element with the stated tolerances."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -37,13 +39,37 @@ def to_dev(a, dtype=None):
     return t.cuda()
 
 
-def make_graph(w) -> sgr.SparseGraph:
-    return sgr.SparseGraph(to_dev(w.src), to_dev(w.dst), w.num_nodes, to_dev(w.input_nodes))
+PATHS = ("resident", "per_microstep")
 
 
-def run_gpu(w, G=None, graph=None, backward=True):
+def make_graph(w, path=None, env=None) -> sgr.SparseGraph:
+    """The workload's graph.  path: None for the library's choice, or
+    "resident" / "per_microstep" to pin the kernels (CK_RESIDENT at creation;
+    a requested resident path must be the one taken at the workload's B).
+    env: extra environment variables set while the graph is created."""
+    set_env = dict(env or {})
+    if path == "per_microstep":
+        set_env["CK_RESIDENT"] = "0"
+    elif path == "resident":
+        set_env["CK_RESIDENT"] = "1"
+    saved = {k: os.environ.get(k) for k in set_env}
+    os.environ.update(set_env)
+    try:
+        g = sgr.SparseGraph(to_dev(w.src), to_dev(w.dst), w.num_nodes, to_dev(w.input_nodes))
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    if path is not None:
+        assert sgr.recurrence_path(g, w.B) == path, f"requested {path} kernels are not taken"
+    return g
+
+
+def run_gpu(w, G=None, graph=None, backward=True, path=None):
     """Forward (+ backward with grad_out G, default w.grad_out) on the GPU."""
-    g = make_graph(w) if graph is None else graph
+    g = make_graph(w, path) if graph is None else graph
     ev, lk, bs = to_dev(w.edge_values), to_dev(w.leak), to_dev(w.bias)
     dr, st = to_dev(w.drives), to_dev(w.state0)
     out, saved, ws = sgr.recurrence_forward(g, ev, lk, bs, dr, st, w.microsteps)

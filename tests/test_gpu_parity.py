@@ -14,8 +14,8 @@ import torch
 import oracle
 import sparse_graph_recurrent_amd as sgr
 import synthetic
-from gpu_helpers import (column_masked_grad, compare_all, compare_floor, compare_with_fp32_floor, log, make_graph, run_gpu,
-                         run_oracle, to_dev)
+from gpu_helpers import (PATHS, column_masked_grad, compare_all, compare_floor,
+                         compare_with_fp32_floor, log, make_graph, run_gpu, run_oracle, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -101,10 +101,11 @@ def test_graph_validation_agrees_with_oracle(case):
 
 
 # ---------------------------------------------------------------- parity, small
-def test_tiny_workload_full_parity():
+@pytest.mark.parametrize("path", PATHS)
+def test_tiny_workload_full_parity(path):
     w = synthetic.make("tiny")
-    log("parity: tiny workload")
-    compare_all(run_gpu(w), run_oracle(w))
+    log(f"parity: tiny workload, {path} kernels")
+    compare_all(run_gpu(w, path=path), run_oracle(w))
 
 
 def _mixed_graph(seed, B, T, M, N=400, E=9000, n_in=9):
@@ -124,22 +125,25 @@ def _mixed_graph(seed, B, T, M, N=400, E=9000, n_in=9):
     return w
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 20, 31, 32, 33, 64, 65, 100])
-def test_batch_widths_parity(B):
+@pytest.mark.parametrize("B,path", [(b, p) for b in (1, 2, 3, 5, 8, 20, 31, 32) for p in PATHS]
+                         + [(b, "per_microstep") for b in (33, 64, 65, 100)])
+def test_batch_widths_parity(B, path):
     w = _mixed_graph(100 + B, B=B, T=3, M=2)
-    log(f"parity: mixed graph B={B} E={w.num_edges}")
-    compare_all(run_gpu(w), run_oracle(w))
+    log(f"parity: mixed graph B={B} E={w.num_edges}, {path} kernels")
+    compare_all(run_gpu(w, path=path), run_oracle(w))
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("M", [1, 2, 3])
-def test_microsteps_parity(M):
+def test_microsteps_parity(M, path):
     w = _mixed_graph(200 + M, B=32, T=4, M=M)
-    log(f"parity: mixed graph M={M}")
-    compare_all(run_gpu(w), run_oracle(w))
+    log(f"parity: mixed graph M={M}, {path} kernels")
+    compare_all(run_gpu(w, path=path), run_oracle(w))
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("kind", ["no_edges", "no_inputs", "one_node", "empty_rows", "hub_rows"])
-def test_degenerate_graphs_parity(kind):
+def test_degenerate_graphs_parity(kind, path):
     rng = np.random.default_rng(77)
     w = _adversarial(kind, rng)
     B, T, M = 6, 3, 2
@@ -149,34 +153,37 @@ def test_degenerate_graphs_parity(kind):
     w.state0 = (0.3 * rng2.standard_normal((B, w.num_nodes))).astype(np.float32)
     w.grad_out = rng2.standard_normal((T, B, w.num_nodes)).astype(np.float32)
     w.microsteps = M
-    log(f"parity: degenerate {kind} N={w.num_nodes} E={w.num_edges}")
-    compare_all(run_gpu(w), run_oracle(w))
+    log(f"parity: degenerate {kind} N={w.num_nodes} E={w.num_edges}, {path} kernels")
+    compare_all(run_gpu(w, path=path), run_oracle(w))
 
 
-def test_saturated_preactivations():
+@pytest.mark.parametrize("path", PATHS)
+def test_saturated_preactivations(path):
     """A third of the nodes sit at |a| ~ 6..12 (bias +-6, strong drives), where
     tanh' must come from the pre-activation, not from 1 - tanh^2."""
     w = _mixed_graph(300, B=32, T=3, M=2)
     i = np.arange(w.num_nodes)
     w.bias = np.where(i % 3 == 0, np.where(i % 2 == 0, 6.0, -6.0), w.bias).astype(np.float32)
     w.drives = (6.0 * w.drives).astype(np.float32)
-    log("parity: saturated pre-activations")
-    compare_all(run_gpu(w), run_oracle(w))
+    log(f"parity: saturated pre-activations, {path} kernels")
+    compare_all(run_gpu(w, path=path), run_oracle(w))
 
 
 # ---------------------------------------------------------------- parity, full size
-def test_flygpt_full_parity():
+@pytest.mark.parametrize("path", PATHS)
+def test_flygpt_full_parity(path):
     w = synthetic.make("flygpt")
-    log("parity: flygpt launch shape, all columns")
-    gpu, ref = run_gpu(w), run_oracle(w)
+    log(f"parity: flygpt launch shape, all columns, {path} kernels")
+    gpu, ref = run_gpu(w, path=path), run_oracle(w)
     compare_all(gpu, ref)
     compare_floor(gpu, ref, run_oracle(w, precision="f32"))
 
 
-def test_edge_cases_full_parity():
+@pytest.mark.parametrize("path", PATHS)
+def test_edge_cases_full_parity(path):
     w = synthetic.make("edge_cases")
-    log("parity: edge-cases workload, all columns")
-    gpu, ref = run_gpu(w), run_oracle(w)
+    log(f"parity: edge-cases workload, all columns, {path} kernels")
+    gpu, ref = run_gpu(w, path=path), run_oracle(w)
     compare_all(gpu, ref)
     compare_floor(gpu, ref, run_oracle(w, precision="f32"))
 
@@ -218,25 +225,27 @@ def test_connectome_sampled_parity():
 
 
 # ---------------------------------------------------------------- properties
-def test_results_are_bitwise_deterministic():
+@pytest.mark.parametrize("path", PATHS)
+def test_results_are_bitwise_deterministic(path):
     w = synthetic.make("edge_cases")
-    log("determinism: edge-cases workload twice")
-    g = make_graph(w)
+    log(f"determinism: edge-cases workload twice, {path} kernels")
+    g = make_graph(w, path)
     a, b = run_gpu(w, graph=g), run_gpu(w, graph=g)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 
 
-def test_caller_edge_order_is_invisible_bitwise():
+@pytest.mark.parametrize("path", PATHS)
+def test_caller_edge_order_is_invisible_bitwise(path):
     w = _mixed_graph(400, B=20, T=3, M=2)
     key = w.dst * w.num_nodes + w.src
     _, first = np.unique(key, return_index=True)   # unique (src, dst) pairs only
     w.src, w.dst, w.edge_values = w.src[first], w.dst[first], w.edge_values[first]
-    log("edge-order invariance")
-    a = run_gpu(w)
+    log(f"edge-order invariance, {path} kernels")
+    a = run_gpu(w, path=path)
     p = np.random.default_rng(1).permutation(w.num_edges)
     w.src, w.dst, w.edge_values = w.src[p], w.dst[p], w.edge_values[p]
-    b = run_gpu(w)
+    b = run_gpu(w, path=path)
     for k in ("out", "g_leak", "g_bias", "g_drives", "g_state0"):
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
     np.testing.assert_array_equal(a["g_edge_values"][p], b["g_edge_values"])
@@ -266,13 +275,14 @@ def test_workspace_too_small_is_rejected():
     assert ei.value.status == 6
 
 
-def test_hip_graph_replay_matches_eager():
+@pytest.mark.parametrize("path", PATHS)
+def test_hip_graph_replay_matches_eager(path):
     """Forward+backward captured into a HIP graph (torch.cuda.CUDAGraph on the
     library's stream) and replayed several times, with eager work and
     synchronisation between replays: every replay equals the eager result."""
     w = synthetic.make("edge_cases", T=4)
-    log("HIP graph replay vs eager: edge-cases workload, T=4")
-    g = make_graph(w)
+    log(f"HIP graph replay vs eager: edge-cases workload, T=4, {path} kernels")
+    g = make_graph(w, path)
     ev, lk, bs, dr, st, G = (to_dev(x) for x in (w.edge_values, w.leak, w.bias, w.drives,
                                                   w.state0, w.grad_out))
     sb, wb = sgr.recurrence_sizes(g, w.T, w.B, w.microsteps)

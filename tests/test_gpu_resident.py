@@ -1,0 +1,65 @@
+"""GPU checks specific to the XCD-resident kernels (one launch per call, each
+XCD computing one group of 4 batch columns): which calls take them, and the
+failure path of their bounded waits, forced from the host.
+
+Parity of the resident kernels against the oracle is covered, path by path,
+in test_gpu_parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_graph_recurrent_amd as sgr
+import synthetic
+from gpu_helpers import compare_all, log, make_graph, run_gpu, run_oracle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_path_selection():
+    """Graphs of up to 9200 nodes take the resident kernels for B <= 32 (one
+    column group per XCD), wider batches and larger graphs the per-microstep
+    kernels; CK_RESIDENT=0 at creation turns the resident kernels off."""
+    w = synthetic.make("flygpt", T=2)
+    g = make_graph(w)
+    log("path selection: flygpt graph")
+    assert [sgr.recurrence_path(g, B) for B in (1, 8, 20, 32, 33, 64)] == \
+        ["resident"] * 4 + ["per_microstep"] * 2
+    assert sgr.recurrence_path(make_graph(w, env={"CK_RESIDENT": "0"}), 32) == "per_microstep"
+    big = synthetic.make("mid_scale", T=1)
+    log("path selection: mid-scale graph")
+    assert sgr.recurrence_path(make_graph(big), 32) == "per_microstep"
+
+
+def test_failed_wait_poisons_every_output():
+    """With every wait of the resident kernels forced to give up at once
+    (CK_RESIDENT_SPIN_LIMIT=-1 at creation; the kernels still run to their
+    end), forward and backward report the failure as NaN in every output.
+    A graph created afterwards computes correctly again."""
+    w = synthetic.make("tiny")
+    log("resident failure path: all waits give up")
+    g = make_graph(w, "resident", env={"CK_RESIDENT_SPIN_LIMIT": "-1"})
+    bad = run_gpu(w, graph=g)
+    for k, v in bad.items():
+        assert np.isnan(v).all(), k
+    log("resident failure path: healthy graph afterwards")
+    compare_all(run_gpu(w, path="resident"), run_oracle(w))
+
+
+def test_paths_agree_on_flygpt():
+    """The two kernel families compute the same sums in different orders:
+    on the FlyGPT launch shape they agree to the state / gradient
+    tolerances."""
+    w = synthetic.make("flygpt", T=8)
+    log("resident vs per-microstep: flygpt shape, T=8")
+    a = run_gpu(w, path="resident")
+    b = run_gpu(w, path="per_microstep")
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-5, atol=1e-6)
+    for k in ("g_edge_values", "g_leak", "g_bias", "g_drives", "g_state0"):
+        scale = np.sqrt(np.mean(b[k].astype(np.float64) ** 2))
+        np.testing.assert_allclose(a[k], b[k], rtol=1e-4, atol=1e-6 + 1e-5 * scale, err_msg=k)

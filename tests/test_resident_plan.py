@@ -1,0 +1,168 @@
+"""Host-side checks of the resident plan (csrc/schedule.cpp, plain C++): the
+split of one orientation's rows over the workgroups of one XCD, each lane of
+a workgroup holding one piece of at most D consecutive edges of a row.
+
+The plan is built with g++ and a small driver, then replayed the way the
+resident kernels use it: lane l of workgroup r sums the edges of its piece,
+and the owner of the range's o-th row adds the partial sums of lanes
+[owner_pbeg[o], owner_pbeg[o + 1]) in lane order.  The replay must give every
+row sum exactly once, every edge must lie in exactly one piece, and the plan
+must stay inside the limits the kernels rely on (1024 lanes and 1024 rows
+per workgroup, D among the built piece lengths).
+"""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import synthetic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "sparse_graph_recurrent_amd", "csrc")
+LANES = 1024
+LENS = (8, 12, 16, 20, 24)
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path_factory.mktemp("res") / "resident_driver")
+    subprocess.run([gxx, "-std=c++17", "-O2", "-Wall", "-Werror", "-I", CSRC, "-o", exe,
+                    os.path.join(ROOT, "tests", "resident_driver.cpp"),
+                    os.path.join(CSRC, "schedule.cpp")], check=True)
+    return exe
+
+
+def plan(driver, ptr, ranks, lens):
+    N = len(ptr) - 1
+    text = f"{N} {ranks} {lens}\n" + " ".join(map(str, ptr)) + "\n"
+    out = subprocess.run([driver], input=text, capture_output=True, text=True, check=True).stdout
+    lines = out.strip("\n").split("\n")
+    if lines[0] == "none":
+        return None
+    D, r, max_pieces, blk = map(int, lines[0].split())
+    arr = [np.array(ln.split(), dtype=np.int64) for ln in lines[1:7]]
+    return dict(D=D, ranks=r, max_pieces=max_pieces, blk=blk, rank_rows=arr[0],
+                owner_pbeg=arr[1].reshape(r, LANES + 1), piece_row=arr[2].reshape(r, LANES),
+                piece_kbeg=arr[3].reshape(r, LANES), piece_cnt=arr[4].reshape(r, LANES),
+                piece_blk=arr[5].reshape(r, LANES))
+
+
+def replay(driver, major, N, ranks=32, lens=5):
+    major = np.asarray(major, dtype=np.int64)
+    deg = np.bincount(major, minlength=N).astype(np.int64) if len(major) else np.zeros(N, np.int64)
+    ptr = np.concatenate([[0], np.cumsum(deg)])
+    p = plan(driver, ptr.tolist(), ranks, lens)
+    if p is None:
+        return None
+    D = p["D"]
+    assert D in LENS[:lens] and p["ranks"] == ranks
+    rr = p["rank_rows"]
+    assert rr[0] == 0 and rr[-1] == N and (np.diff(rr) >= 0).all() and (np.diff(rr) <= LANES).all()
+    E = int(ptr[-1])
+    val = np.random.default_rng(0).integers(-1000, 1000, E)  # exact integer sums
+    csum = np.concatenate([[0], np.cumsum(val)])
+    want = csum[ptr[1:]] - csum[ptr[:-1]]
+    got = np.full(N, np.iinfo(np.int64).min)
+    cover = np.zeros(E, np.int64)
+    max_pieces = 0
+    for r in range(ranks):
+        kb, cnt, prow = p["piece_kbeg"][r], p["piece_cnt"][r], p["piece_row"][r]
+        assert ((cnt >= 0) & (cnt <= D)).all()
+        part = csum[kb + cnt] - csum[kb]
+        for l in np.nonzero(cnt)[0]:
+            cover[kb[l]:kb[l] + cnt[l]] += 1
+            assert ptr[prow[l]] <= kb[l] and kb[l] + cnt[l] <= ptr[prow[l] + 1], "piece outside its row"
+        assert (prow[cnt == 0] == -1).all() and (prow[cnt > 0] >= 0).all()
+        ob = p["owner_pbeg"][r]
+        nrows = int(rr[r + 1] - rr[r])
+        assert (np.diff(ob) >= 0).all()
+        assert (ob[nrows:] == ob[nrows]).all(), "owner ranges past the rows must be empty"
+        max_pieces = max(max_pieces, int(ob[nrows]))
+        assert ob[nrows] <= LANES
+        assert (cnt[ob[nrows]:] == 0).all(), "lanes past the pieces hold no edges"
+        # level 1: block heads of rows with more than blk pieces add their block in place
+        blk, hb = p["blk"], p["piece_blk"][r]
+        assert 8 <= blk <= 32 and ((hb >= 0) & (hb <= blk)).all()
+        part = part.copy()
+        level1 = part.copy()
+        for l in np.nonzero(hb)[0]:
+            assert (prow[l:l + hb[l]] == prow[l]).all(), "a block spans two rows"
+            level1[l] = part[l:l + hb[l]].sum()
+        # level 2: the owner adds its pieces (stride 1) or its block sums (stride blk)
+        heads = set()
+        for o in range(nrows):
+            row = int(rr[r] + o)
+            lanes = np.arange(ob[o], ob[o + 1])
+            assert (prow[lanes] == row).all(), "owner combines another row's piece"
+            assert got[row] == np.iinfo(np.int64).min
+            if len(lanes) > blk:
+                hl = lanes[::blk]
+                assert (hb[hl] == np.minimum(blk, ob[o + 1] - hl)).all(), "block head counts"
+                heads.update(hl.tolist())
+                got[row] = int(level1[hl].sum())
+            else:
+                assert (hb[lanes] == 0).all()
+                got[row] = int(part[lanes].sum())
+        assert heads == set(np.nonzero(hb)[0].tolist()), "a block head outside a long row"
+    assert (cover == 1).all(), "every edge in exactly one piece"
+    np.testing.assert_array_equal(got, want)
+    assert max_pieces == p["max_pieces"]
+    return p
+
+
+@pytest.mark.parametrize("name", ["tiny", "flygpt", "edge_cases"])
+def test_workload_plans(driver, name):
+    w = synthetic.make(name, synthetic.DEFAULT_SEEDS[name])
+    for major, lens in ((w.dst, 5), (w.src, 4)):
+        p = replay(driver, major, w.num_nodes, lens=lens)
+        assert p is not None
+
+
+def test_flygpt_plan_balance(driver):
+    """FlyGPT shape: the busiest workgroup's gather work (pieces x D) is within
+    15 % of the average padded edge count per workgroup."""
+    w = synthetic.make("flygpt", synthetic.DEFAULT_SEEDS["flygpt"])
+    for major, lens in ((w.dst, 5), (w.src, 4)):
+        p = replay(driver, major, w.num_nodes, lens=lens)
+        avg = len(major) / 32
+        assert p["max_pieces"] * p["D"] <= 1.15 * avg + p["D"] * 160
+
+
+@pytest.mark.parametrize("case", ["empty", "one_node", "single_edge", "one_row", "hub",
+                                  "isolated", "many_rows"])
+def test_degenerate_plans(driver, case):
+    rng = np.random.default_rng(1)
+    major, N, feasible = {
+        "empty": ([], 7, True),
+        "one_node": ([], 1, True),
+        "single_edge": ([0], 1, True),
+        "one_row": ([3] * 5000, 10, True),
+        "hub": (list(rng.integers(0, 50, 3000)) + [7] * 20000, 50, True),
+        "isolated": ([1, 1, 999], 1000, True),
+        "many_rows": ([], 32 * LANES + 1, False),  # more rows than 32 workgroups can own
+    }[case]
+    p = replay(driver, major, N)
+    assert (p is not None) == feasible
+
+
+def test_row_beyond_a_workgroup(driver):
+    """A row of more than 1024 x D edges fits no workgroup at any piece
+    length: no plan (the per-microstep kernels run instead)."""
+    assert replay(driver, [0] * (LANES * 24 + 1), 2) is None
+    assert replay(driver, [0] * (LANES * 20 + 1), 2, lens=4) is None
+    assert replay(driver, [0] * (LANES * 20 + 1), 2, lens=5) is not None
+
+
+def test_random_plans(driver):
+    rng = np.random.default_rng(2)
+    for _ in range(10):
+        N = int(rng.integers(1, 9000))
+        E = int(rng.integers(0, 200000))
+        p = np.arange(1, N + 1, dtype=np.float64) ** -float(rng.choice([0.0, 1.0, 2.0]))
+        major = rng.choice(N, size=E, p=p / p.sum())
+        replay(driver, major, N, ranks=int(rng.choice([32, 8, 1])), lens=int(rng.choice([4, 5])))
