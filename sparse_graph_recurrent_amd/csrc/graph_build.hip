@@ -553,7 +553,8 @@ extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int
     const bool wanted = !(env && env[0] == '0' && env[1] == '\0');
     const char* spin = getenv("CK_RESIDENT_SPIN_LIMIT");
     g->res_spin_limit = spin && spin[0] ? atoi(spin) : (1 << 20);
-    if (wanted && N <= kResMaxN && xcds_as_expected(num_cus, stream)) {
+    // (the resident kernels' progress flags hold at most 32 workgroups per XCD)
+    if (wanted && N <= kResMaxN && num_cus <= 32 * kResXcds && xcds_as_expected(num_cus, stream)) {
       const int ranks = num_cus / kResXcds;
       bool pf = false, pb = false;
       rc = build_resident(hptr, N, g->col_idx, g->perm, ranks, kResNumPieceLens, stream,

@@ -193,12 +193,17 @@ __device__ bool res_barrier(const ResCommon& c, int grp, int round, volatile int
 }
 
 // Rows [0, N) of a plane of float4 rows into LDS, 64 rows per wave
-// instruction (global -> LDS, no registers).
-__device__ __forceinline__ void res_load_plane(float4* lds, const float* src, int N) {
+// instruction (global -> LDS, no registers).  The 64-row chunks are taken in
+// an order rotated by `rot`: the XCD's workgroups all copy the same plane at
+// the same moment, and starting each at a different place spreads their
+// requests over the L2 channels.
+__device__ __forceinline__ void res_load_plane(float4* lds, const float* src, int N, int rot = 0) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const float4* s4 = reinterpret_cast<const float4*>(src);
-  for (int ch = wave; ch * 64 < N; ch += kResLanes / 64) {
+  const int nch = (N + 63) / 64;
+  for (int k = wave; k < nch; k += kResLanes / 64) {
+    const int ch = (k + rot) % nch;
     const int i = ch * 64 + lane;
     if (i < N)
       __builtin_amdgcn_global_load_lds((const void*)(s4 + i),
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
     }
     if (s == p.c.S) break;
     if (!res_barrier(p.c, grp, s, &s_fail)) return;
-    res_load_plane(plane, p.hplanes + (size_t)(s - 1) * psz + goff, N);
+    res_load_plane(plane, p.hplanes + (size_t)(s - 1) * psz + goff, N, rank * ((N + 63) / 64) / p.c.ranks);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
   if (owner) k1(S, f4(0.f), gin(S), bld4(apl(S), rowb, 0), bld4(hpl(S - 1), rowb, 0));
   float4 hq = prow >= 0 ? bld4(hpl(S - 1), prowb, 0) : f4(0.f);
   if (!res_barrier(p.c, grp, 1, &s_fail)) return;
-  res_load_plane(plane, gapl(S), N);
+  res_load_plane(plane, gapl(S), N, rank * ((N + 63) / 64) / p.c.ranks);
   if (tid == 0) plane[N] = f4(0.f);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -473,7 +478,7 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
     hq = hq_next;
     if (s == 1) break;
     if (!res_barrier(p.c, grp, S - s + 2, &s_fail)) return;
-    res_load_plane(plane, gapl(s - 1), N);
+    res_load_plane(plane, gapl(s - 1), N, rank * ((N + 63) / 64) / p.c.ranks);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
