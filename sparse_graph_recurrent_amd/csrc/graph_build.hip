@@ -329,25 +329,17 @@ __global__ void xcc_of_workgroups(int32_t* __restrict__ out) {
   if (threadIdx.x == 0) out[blockIdx.x] = (int32_t)xcc_id();
 }
 
-// Resident slot q = ((r * D) + j) * kResLanes + l: edge j of lane l's piece on
-// workgroup r, or an empty slot (node N, caller index -1).
-__global__ void pad_resident(const int32_t* __restrict__ kbeg, const int32_t* __restrict__ cnt,
-                             int D, int64_t slots, const int32_t* __restrict__ col,
-                             const int32_t* __restrict__ perm, int32_t N,
-                             int32_t* __restrict__ pcol, int32_t* __restrict__ pperm) {
+// Resident slot q = ((r * D) + j) * kResLanes + l (slot j of lane l on
+// workgroup r): its compressed edge slot_edge[q], or an empty slot (node N,
+// caller index -1).
+__global__ void pad_resident(const int32_t* __restrict__ slot_edge, int64_t slots,
+                             const int32_t* __restrict__ col, const int32_t* __restrict__ perm,
+                             int32_t N, int32_t* __restrict__ pcol, int32_t* __restrict__ pperm) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= slots) return;
-  const int64_t l = q % kResLanes, rj = q / kResLanes;
-  const int64_t r = rj / D, j = rj % D;
-  const int64_t lane = r * kResLanes + l;
-  if (j < cnt[lane]) {
-    const int32_t k = kbeg[lane] + (int32_t)j;
-    pcol[q] = col[k];
-    pperm[q] = perm[k];
-  } else {
-    pcol[q] = N;
-    pperm[q] = -1;
-  }
+  const int32_t k = slot_edge[q];
+  pcol[q] = k >= 0 ? col[k] : N;
+  pperm[q] = k >= 0 ? perm[k] : -1;
 }
 
 // True when a launch of num_cus workgroups puts num_cus / kResXcds of them on
@@ -379,6 +371,16 @@ ck_status build_resident(const std::vector<int32_t>& ptr, int64_t N, const int32
   ResidentPlan plan;
   *planned = plan_resident(ptr.data(), N, ranks, max_lens, &plan);
   if (!*planned) return CK_OK;
+  {
+    // order each piece's edges against LDS bank conflicts (needs the rows read)
+    std::vector<int32_t> hcol(std::max<int32_t>(ptr[N], 1));
+    if (ptr[N] > 0) {
+      CK_HIP_TRY(hipMemcpyAsync(hcol.data(), col, (size_t)ptr[N] * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, stream));
+      CK_HIP_TRY(hipStreamSynchronize(stream));
+    }
+    order_resident_slots(hcol.data(), N, &plan);
+  }
   out->D = plan.D;
   out->ranks = plan.ranks;
   out->slots = (int64_t)plan.ranks * plan.D * kResLanes;
@@ -395,19 +397,17 @@ ck_status build_resident(const std::vector<int32_t>& ptr, int64_t N, const int32
   out->blk = plan.blk;
   out->two_level = false;
   for (int32_t v : plan.piece_blk) out->two_level = out->two_level || v > 0;
-  int32_t *kbeg = nullptr, *cnt = nullptr;
-  hipError_t e = upload(&kbeg, plan.piece_kbeg);
-  if (e == hipSuccess) e = upload(&cnt, plan.piece_cnt);
+  int32_t* slot_edge = nullptr;
+  hipError_t e = upload(&slot_edge, plan.slot_edge);
   if (e == hipSuccess) e = hipMalloc(&out->pcol, out->slots * sizeof(int32_t));
   if (e == hipSuccess) e = hipMalloc(&out->pperm, out->slots * sizeof(int32_t));
   if (e == hipSuccess) {
     pad_resident<<<grid_for(out->slots, 256), 256, 0, stream>>>(
-        kbeg, cnt, plan.D, out->slots, col, perm, (int32_t)N, out->pcol, out->pperm);
+        slot_edge, out->slots, col, perm, (int32_t)N, out->pcol, out->pperm);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  (void)hipFree(kbeg);
-  (void)hipFree(cnt);
+  (void)hipFree(slot_edge);
   CK_HIP_TRY(e);
   return CK_OK;
 }

@@ -3,6 +3,7 @@
 #include "schedule.h"
 
 #include <algorithm>
+#include <functional>
 
 namespace ckhip {
 
@@ -252,7 +253,142 @@ bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_lens, Resid
     for (int o = r1 - r0; o <= kResLanes; ++o) pb[o] = lane;
     p.max_pieces = std::max(p.max_pieces, lane);
   }
+  p.slot_edge.assign((size_t)ranks * D * kResLanes, -1);
+  for (int r = 0; r < ranks; ++r)
+    for (int l = 0; l < kResLanes; ++l) {
+      const size_t q = (size_t)r * kResLanes + l;
+      for (int j = 0; j < p.piece_cnt[q]; ++j)
+        p.slot_edge[((size_t)r * D + j) * kResLanes + l] = p.piece_kbeg[q] + j;
+    }
   return true;
 }
+
+namespace {
+
+// Distinct rows sharing the most-shared bank group among `rows` (-1 = none).
+int group_cost(const int32_t* rows, int n) {
+  int cnt[kResBankGroups] = {0};
+  int best = 0;
+  for (int a = 0; a < n; ++a) {
+    if (rows[a] < 0) continue;
+    bool dup = false;
+    for (int b = 0; b < a && !dup; ++b) dup = rows[b] == rows[a];
+    if (dup) continue;
+    best = std::max(best, ++cnt[rows[a] % kResBankGroups]);
+  }
+  return best;
+}
+
+}  // namespace
+
+int64_t resident_conflict_cost(const int32_t* col, int64_t N, const ResidentPlan& p) {
+  int64_t cost = 0;
+  int32_t rows[kResBankGroups];
+  for (int r = 0; r < p.ranks; ++r)
+    for (int j = 0; j < p.D; ++j)
+      for (int g = 0; g < kResLanes; g += kResBankGroups) {
+        bool any = false;
+        for (int u = 0; u < kResBankGroups; ++u) {
+          const int32_t e = p.slot_edge[((size_t)r * p.D + j) * kResLanes + g + u];
+          rows[u] = e >= 0 ? col[e] : (int32_t)N;
+          any = any || e >= 0;
+        }
+        if (any) cost += group_cost(rows, kResBankGroups);
+      }
+  return cost;
+}
+
+// Per aligned group of 16 lanes, slot by slot: a maximum matching of lanes
+// (with edges left) to bank groups not yet used in this slot, found with
+// augmenting paths, trying for each lane first the bank groups it has most
+// edges left in (those are the hard ones to place later).  A lane left
+// unmatched takes an empty slot if its piece is short (the all-zero row),
+// else the edge of its most frequent bank group (a conflict).
+void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out) {
+  ResidentPlan& p = *out;
+  const int D = p.D;
+  constexpr int G = kResBankGroups;
+  for (int r = 0; r < p.ranks; ++r)
+    for (int g0 = 0; g0 < kResLanes; g0 += G) {
+      // remaining edges of each lane, by bank group
+      std::vector<int32_t> left[G][G];
+      int nleft[G] = {0}, pads[G] = {0};
+      bool any = false;
+      for (int u = 0; u < G; ++u) {
+        const size_t q = (size_t)r * kResLanes + g0 + u;
+        for (int j = 0; j < p.piece_cnt[q]; ++j) {
+          const int32_t e = p.piece_kbeg[q] + j;
+          left[u][col[e] % G].push_back(e);
+        }
+        nleft[u] = p.piece_cnt[q];
+        pads[u] = D - p.piece_cnt[q];
+        any = any || nleft[u] > 0;
+      }
+      if (!any) continue;
+      for (int j = 0; j < D; ++j) {
+        int owner_of[G];  // bank group -> lane matched to it in this slot
+        int match[G];     // lane -> bank group, or -1
+        for (int b = 0; b < G; ++b) owner_of[b] = -1;
+        for (int u = 0; u < G; ++u) match[u] = -1;
+        // the lane's bank groups with edges left, most edges first
+        auto prefs = [&](int u, int* order) {
+          int n = 0;
+          for (int b = 0; b < G; ++b)
+            if (!left[u][b].empty()) order[n++] = b;
+          std::sort(order, order + n, [&](int x, int y) {
+            return left[u][x].size() != left[u][y].size() ? left[u][x].size() > left[u][y].size() : x < y;
+          });
+          return n;
+        };
+        std::function<bool(int, bool*)> augment = [&](int u, bool* seen) -> bool {
+          int order[G];
+          const int n = prefs(u, order);
+          for (int k = 0; k < n; ++k) {
+            const int b = order[k];
+            if (seen[b]) continue;
+            seen[b] = true;
+            if (owner_of[b] < 0 || augment(owner_of[b], seen)) {
+              owner_of[b] = u;
+              match[u] = b;
+              return true;
+            }
+          }
+          return false;
+        };
+        // lanes with the fewest empty slots to spare go first
+        int lanes[G];
+        for (int u = 0; u < G; ++u) lanes[u] = u;
+        std::sort(lanes, lanes + G, [&](int x, int y) {
+          const int sx = pads[x] - 0, sy = pads[y];
+          return sx != sy ? sx < sy : x < y;
+        });
+        for (int k = 0; k < G; ++k) {
+          const int u = lanes[k];
+          if (nleft[u] == 0) continue;
+          bool seen[G] = {false};
+          augment(u, seen);
+        }
+        for (int u = 0; u < G; ++u) {
+          const size_t slot = ((size_t)r * D + j) * kResLanes + g0 + u;
+          int b = match[u];
+          if (b < 0) {
+            if (nleft[u] == 0 || pads[u] > 0) {
+              if (pads[u] > 0) --pads[u];
+              p.slot_edge[slot] = -1;
+              continue;
+            }
+            int order[G];
+            prefs(u, order);
+            b = order[0];
+          }
+          p.slot_edge[slot] = left[u][b].back();
+          left[u][b].pop_back();
+          --nleft[u];
+        }
+      }
+    }
+  (void)N;
+}
+
 
 }  // namespace ckhip

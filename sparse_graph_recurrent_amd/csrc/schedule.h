@@ -109,7 +109,28 @@ struct ResidentPlan {
   int blk = 0;                      // block length of the two-level sums
   std::vector<int32_t> piece_blk;   // [ranks][kResLanes]: pieces in the lane's block if it is
                                     // a block head of a row of more than blk pieces, else 0
+  std::vector<int32_t> slot_edge;   // [ranks][D][kResLanes]: edge of slot j of lane l, or -1
+                                    // (compressed order unless order_resident_slots ran)
 };
+
+// LDS rows are 16 bytes and the LDS serves a 16-byte-per-lane read 16 lanes at
+// a time, conflict-free when those 16 lanes read rows in distinct bank
+// groups (row index mod kResBankGroups) or the same row.
+constexpr int kResBankGroups = 16;
+
+// Order the edges inside each piece (slot j of lane l) so that, for every
+// slot and every aligned group of 16 lanes, the rows read fall in as many
+// distinct bank groups as possible (a bipartite matching of lanes to bank
+// groups per slot).  col[k] is the row read by compressed edge k; rows >= N
+// do not occur.  Fills out->slot_edge ([ranks][D][kResLanes]: compressed edge
+// index, or -1 for an empty slot, which reads the all-zero row N).  Without
+// this call a piece's edges keep their compressed order.
+void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out);
+
+// Bank-conflict cost of a slot table: over all slots and 16-lane groups, the
+// sum of the largest number of distinct rows sharing one bank group (1 = no
+// conflict).  Used to compare orderings.
+int64_t resident_conflict_cost(const int32_t* col, int64_t N, const ResidentPlan& p);
 
 // Plan the pieces of ptr[0..N] for `ranks` workgroups, choosing the piece
 // length among kResPieceLens[0 .. max_lens) that minimises the busiest

@@ -1,7 +1,9 @@
-// CPU driver for the resident planner: reads "N ranks max_lens" and the N + 1
-// row pointers from stdin; prints "none", or "D ranks max_pieces blk" followed by
-// rank_rows, owner_pbeg, piece_row, piece_kbeg, piece_cnt and piece_blk (one
-// array per line).
+// CPU driver for the resident planner: reads "N ranks max_lens order" and the
+// N + 1 row pointers from stdin, then (order = 1) the row read by each
+// compressed edge; prints "none", or "D ranks max_pieces blk cost cost_ordered"
+// (bank-conflict costs of the slot table in compressed order and after
+// ordering; 0 when not ordered) followed by rank_rows, owner_pbeg, piece_row,
+// piece_kbeg, piece_cnt, piece_blk and slot_edge (one array per line).
 #include <cstdio>
 #include <vector>
 
@@ -14,22 +16,35 @@ static void put(const std::vector<int32_t>& v) {
 
 int main() {
   long long N = 0;
-  int ranks = 0, lens = 0;
-  if (std::scanf("%lld %d %d", &N, &ranks, &lens) != 3 || N < 0) return 2;
+  int ranks = 0, lens = 0, order = 0;
+  if (std::scanf("%lld %d %d %d", &N, &ranks, &lens, &order) != 4 || N < 0) return 2;
   std::vector<int32_t> ptr(N + 1);
   for (auto& v : ptr)
     if (std::scanf("%d", &v) != 1) return 2;
+  std::vector<int32_t> col;
+  if (order) {
+    col.resize(ptr[N]);
+    for (auto& v : col)
+      if (std::scanf("%d", &v) != 1) return 2;
+  }
   ckhip::ResidentPlan plan;
   if (!ckhip::plan_resident(ptr.data(), N, ranks, lens, &plan)) {
     std::printf("none\n");
     return 0;
   }
-  std::printf("%d %d %d %d\n", plan.D, plan.ranks, plan.max_pieces, plan.blk);
+  long long c0 = 0, c1 = 0;
+  if (order) {
+    c0 = ckhip::resident_conflict_cost(col.data(), N, plan);
+    ckhip::order_resident_slots(col.data(), N, &plan);
+    c1 = ckhip::resident_conflict_cost(col.data(), N, plan);
+  }
+  std::printf("%d %d %d %d %lld %lld\n", plan.D, plan.ranks, plan.max_pieces, plan.blk, c0, c1);
   put(plan.rank_rows);
   put(plan.owner_pbeg);
   put(plan.piece_row);
   put(plan.piece_kbeg);
   put(plan.piece_cnt);
   put(plan.piece_blk);
+  put(plan.slot_edge);
   return 0;
 }
