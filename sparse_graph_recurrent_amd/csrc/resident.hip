@@ -135,6 +135,15 @@ __device__ __forceinline__ void bst4(float4 v, void* base, uint32_t voff, uint32
 __device__ __forceinline__ void bst1(float v, void* base, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc(base), voff, soff, 0);
 }
+// tanh from the identity tanh(a) = sign(a) (1 - e) / (1 + e), e = exp(-2|a|)
+// (0 < e <= 1, so nothing overflows), with the hardware exponential and
+// reciprocal: absolute error about 2^-23, below the fp32 rounding of the
+// row sums that feed it.  The backward shares e between tanh and
+// sech^2(a) = 4 e / (1 + e)^2.
+__device__ __forceinline__ float ftanh(float a) {
+  const float e = __expf(-2.0f * fabsf(a));
+  return copysignf((1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), a);
+}
 __device__ __forceinline__ float comp(float4 v, int c) {
   return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
 }
@@ -304,10 +313,10 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
       a.y = sum.y + drv.y + beta;
       a.z = sum.z + drv.z + beta;
       a.w = sum.w + drv.w + beta;
-      h.x = (1.0f - lam) * hp.x + lam * tanhf(a.x);
-      h.y = (1.0f - lam) * hp.y + lam * tanhf(a.y);
-      h.z = (1.0f - lam) * hp.z + lam * tanhf(a.z);
-      h.w = (1.0f - lam) * hp.w + lam * tanhf(a.w);
+      h.x = (1.0f - lam) * hp.x + lam * ftanh(a.x);
+      h.y = (1.0f - lam) * hp.y + lam * ftanh(a.y);
+      h.z = (1.0f - lam) * hp.z + lam * ftanh(a.z);
+      h.w = (1.0f - lam) * hp.w + lam * ftanh(a.w);
       bst4(a, p.aplanes + (size_t)(s - 1) * psz + goff, rowb, 0);
       bst4(h, p.hplanes + (size_t)(s - 1) * psz + goff, rowb, 0);
     }
@@ -391,8 +400,13 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if (c < live) {
-        ls += gg[c] * (tanhf(av[c]) - qv[c]);
-        ga[c] = gg[c] * lam * sech2f(av[c]);
+        // e = exp(-2|a|), r = 1/(1+e): tanh(a) = sign(a)(1-e)r, sech^2(a) = 4e r^2
+        // (from a itself, not 1 - tanh^2, which cancels once |a| is a few units)
+        const float e = __expf(-2.0f * fabsf(av[c]));
+        const float r = __builtin_amdgcn_rcpf(1.0f + e);
+        const float th = copysignf((1.0f - e) * r, av[c]);
+        ls += gg[c] * (th - qv[c]);
+        ga[c] = gg[c] * lam * (4.0f * e * r * r);
       } else {
         gg[c] = 0.f;
         ga[c] = 0.f;
