@@ -298,23 +298,24 @@ int64_t resident_conflict_cost(const int32_t* col, int64_t N, const ResidentPlan
   return cost;
 }
 
-// Per aligned group of 16 lanes, slot by slot: a maximum matching of lanes
-// (with edges left) to bank groups not yet used in this slot, found with
-// augmenting paths, trying for each lane first the bank groups it has most
-// edges left in (those are the hard ones to place later).  A lane left
+// Per aligned group of kResBankGroups lanes, slot by slot: a maximum matching
+// of lanes (with edges left) to bank groups not yet used in this slot, found
+// with augmenting paths, trying for each lane first the bank groups it has
+// most edges left in (those are the hard ones to place later).  A lane left
 // unmatched takes an empty slot if its piece is short (the all-zero row),
 // else the edge of its most frequent bank group (a conflict).
 void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out) {
   ResidentPlan& p = *out;
   const int D = p.D;
   constexpr int G = kResBankGroups;
+  std::vector<int32_t> left[G][G];
   for (int r = 0; r < p.ranks; ++r)
     for (int g0 = 0; g0 < kResLanes; g0 += G) {
       // remaining edges of each lane, by bank group
-      std::vector<int32_t> left[G][G];
       int nleft[G] = {0}, pads[G] = {0};
       bool any = false;
       for (int u = 0; u < G; ++u) {
+        for (int b = 0; b < G; ++b) left[u][b].clear();
         const size_t q = (size_t)r * kResLanes + g0 + u;
         for (int j = 0; j < p.piece_cnt[q]; ++j) {
           const int32_t e = p.piece_kbeg[q] + j;
@@ -328,23 +329,23 @@ void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out) {
       for (int j = 0; j < D; ++j) {
         int owner_of[G];  // bank group -> lane matched to it in this slot
         int match[G];     // lane -> bank group, or -1
-        for (int b = 0; b < G; ++b) owner_of[b] = -1;
-        for (int u = 0; u < G; ++u) match[u] = -1;
-        // the lane's bank groups with edges left, most edges first
-        auto prefs = [&](int u, int* order) {
+        int order[G][G];  // per lane: its bank groups with edges left, most edges first
+        int nord[G];
+        for (int u = 0; u < G; ++u) {
+          owner_of[u] = -1;
+          match[u] = -1;
           int n = 0;
           for (int b = 0; b < G; ++b)
-            if (!left[u][b].empty()) order[n++] = b;
-          std::sort(order, order + n, [&](int x, int y) {
-            return left[u][x].size() != left[u][y].size() ? left[u][x].size() > left[u][y].size() : x < y;
+            if (!left[u][b].empty()) order[u][n++] = b;
+          std::sort(order[u], order[u] + n, [&](int x, int y) {
+            return left[u][x].size() != left[u][y].size() ? left[u][x].size() > left[u][y].size()
+                                                           : x < y;
           });
-          return n;
-        };
+          nord[u] = n;
+        }
         std::function<bool(int, bool*)> augment = [&](int u, bool* seen) -> bool {
-          int order[G];
-          const int n = prefs(u, order);
-          for (int k = 0; k < n; ++k) {
-            const int b = order[k];
+          for (int k = 0; k < nord[u]; ++k) {
+            const int b = order[u][k];
             if (seen[b]) continue;
             seen[b] = true;
             if (owner_of[b] < 0 || augment(owner_of[b], seen)) {
@@ -359,8 +360,7 @@ void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out) {
         int lanes[G];
         for (int u = 0; u < G; ++u) lanes[u] = u;
         std::sort(lanes, lanes + G, [&](int x, int y) {
-          const int sx = pads[x] - 0, sy = pads[y];
-          return sx != sy ? sx < sy : x < y;
+          return pads[x] != pads[y] ? pads[x] < pads[y] : x < y;
         });
         for (int k = 0; k < G; ++k) {
           const int u = lanes[k];
@@ -377,9 +377,7 @@ void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out) {
               p.slot_edge[slot] = -1;
               continue;
             }
-            int order[G];
-            prefs(u, order);
-            b = order[0];
+            b = order[u][0];
           }
           p.slot_edge[slot] = left[u][b].back();
           left[u][b].pop_back();
