@@ -197,11 +197,16 @@ def main():
     # forward (backward) launches: S + 1 per-microstep backward launches (the
     # first has no edge pass), or one resident launch per direction
     resident = path == "resident"
-    if prof["bwd_ms"] >= prof["fwd_ms"]:
-        name, per_b, us = ("res_bwd" if resident else "bwd_step"), bwd_b * S / bwd_n, bwd_us
-    else:
-        name, per_b, us = ("res_fwd" if resident else "fwd_step"), fwd_b * S / fwd_n, fwd_us
-    achieved = per_b / (us * 1e-6) / 1e9
+    per_kernel = {}
+    for kname, per_b, us in ((("res_fwd" if resident else "fwd_step"), fwd_b * S / fwd_n, fwd_us),
+                             (("res_bwd" if resident else "bwd_step"), bwd_b * S / bwd_n, bwd_us)):
+        a = per_b / (us * 1e-6) / 1e9
+        per_kernel[kname] = {"achieved": a, "frac": a / HBM_PEAK_GBS, "launch_us": us,
+                             "algorithmic_bytes_per_launch": per_b,
+                             "traffic": measured_traffic(kname)}
+    # the dominant kernel is the one with the larger share of the step's time
+    name = list(per_kernel)[1] if prof["bwd_ms"] >= prof["fwd_ms"] else list(per_kernel)[0]
+    achieved = per_kernel[name]["achieved"]
     visits = S * E * B
     res = {
         "metric": METRIC,
@@ -225,7 +230,8 @@ def main():
                     "fwd_launches_per_step": fwd_n, "bwd_launches_per_step": bwd_n},
         "roofline": {"bound": "hbm", "kernel": name, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(name)},
+                     "traffic": per_kernel[name]["traffic"]},
+        "roofline_by_kernel": per_kernel,
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w)
