@@ -124,9 +124,10 @@ ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int64_t micros
  *
  * Per-microstep kernels: one fused launch per microstep and direction, the
  * rows of all batch columns spread over every compute unit.
- * XCD-resident kernels (graphs planned for them at creation, B <= 32): one
- * launch per call.  Batch column group c (4 columns) is computed by the
- * compute units of XCD c alone, which keep its whole state plane in LDS and
+ * XCD-resident kernels (graphs planned for them at creation): one launch per
+ * call.  Batch column group c (4 columns) is computed by the compute units of
+ * XCD c mod 8 alone (an XCD with several groups computes them in turn), which
+ * keep its whole state plane in LDS and
  * their share of the edges in registers, and exchange each microstep's new
  * state through their shared L2 behind a barrier local to the XCD.  Such a
  * launch holds one workgroup on every compute unit and its workgroups wait

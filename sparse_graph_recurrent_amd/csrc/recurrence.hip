@@ -877,7 +877,7 @@ ck_status make_dims(const ck_graph* g, int64_t T, int64_t B, int64_t M, Dims* d)
   d->slots_f = g->fwd[d->wide].slots;
   d->slots_b = g->bwd[d->wide].slots;
   d->plane = (size_t)g->N * Bp;
-  d->resident = g->res_ok != 0 && Bp <= 4 * kResXcds;
+  d->resident = g->res_ok != 0;
   d->rd = ResDims{g->N, (g->N + 7) / 8 * 8, B, Bp / 4, g->n_in, T, M, T * M};
   return CK_OK;
 }

@@ -148,15 +148,16 @@ __device__ __forceinline__ float comp(float4 v, int c) {
   return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
 }
 
-// Join the launch: the workgroup's XCD is its column group, its rank in the
-// XCD comes from the XCD's ticket counter.  Returns the rank, or -1 when the
-// workgroup has nothing to do (an XCD beyond the column groups) or the
-// grouping is not the expected one (error flag raised).
-__device__ int res_join(const ResCommon& c, int grp, int* s_rank) {
+// Join the launch: the workgroup's XCD computes column groups xcc, xcc + 8,
+// ..., one after the other; its rank in the XCD comes from the XCD's ticket
+// counter.  Returns the rank, or -1 when the workgroup has nothing to do (an
+// XCD beyond the column groups) or the grouping is not the expected one
+// (error flag raised).
+__device__ int res_join(const ResCommon& c, int xcc, int* s_rank) {
   if (threadIdx.x == 0) {
     int rank = -1;
-    if (grp < kResXcds) {
-      rank = (int)__hip_atomic_fetch_add(&c.ctl[kCtlTicket + grp * kCtlStride], 1u,
+    if (xcc < kResXcds) {
+      rank = (int)__hip_atomic_fetch_add(&c.ctl[kCtlTicket + xcc * kCtlStride], 1u,
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (rank >= c.ranks) rank = -2;
     } else {
@@ -166,22 +167,22 @@ __device__ int res_join(const ResCommon& c, int grp, int* s_rank) {
       __hip_atomic_fetch_or(&c.ctl[kCtlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       rank = -1;
     }
-    if (grp >= c.G) rank = -1;
+    if (xcc >= c.G) rank = -1;
     *s_rank = rank;
   }
   __syncthreads();
   return *s_rank;
 }
 
-// Barrier of the XCD's workgroups after microstep number `round` (1-based).
+// Barrier of the XCD's workgroups, the `round`-th of the launch (1-based).
 // Stores issued before it are complete in the XCD's L2 when it returns, and
 // this CU's vector L1 holds no line older than that.  Returns false (after
 // raising the error flag) if the other workgroups did not all arrive in time.
-__device__ bool res_barrier(const ResCommon& c, int grp, int round, volatile int* s_fail) {
+__device__ bool res_barrier(const ResCommon& c, int xcc, int round, volatile int* s_fail) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned* cnt = &c.ctl[kCtlCount + grp * kCtlStride];
+    unsigned* cnt = &c.ctl[kCtlCount + xcc * kCtlStride];
     const unsigned target = (unsigned)c.ranks * (unsigned)round;
     __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int spins = 0;
@@ -248,15 +249,17 @@ struct Piece {
   }
 };
 
-template <int D>
+// MULTI: more than kResXcds column groups, so each XCD computes several in
+// turn (a separate instantiation keeps the one-group kernel's registers).
+template <int D, bool MULTI>
 __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
   extern __shared__ float4 sm[];
   __shared__ int s_rank;
   __shared__ int s_fail;
   const int tid = threadIdx.x;
-  const int grp = (int)xcc_id();
+  const int xcc = (int)xcc_id();
   if (tid == 0) s_fail = 0;
-  const int rank = res_join(p.c, grp, &s_rank);
+  const int rank = res_join(p.c, xcc, &s_rank);
   if (rank < 0) return;
   const int N = p.c.N, B = p.c.B;
   float4* plane = sm;             // [N + 1]
@@ -279,10 +282,14 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
     ks = p.c.input_slot[row];
   }
   const uint32_t ksb = (uint32_t)(ks >= 0 ? ks : 0) * (uint32_t)B * 4u;
-  const int b0 = grp * 4;
   const size_t gsz = (size_t)p.c.Np * 4;   // floats per column-group slice
   const size_t psz = gsz * p.c.G;          // floats per microstep plane
+  int round = 0;
+  const int gend = MULTI ? p.c.G : xcc + 1;
+  for (int grp = xcc; grp < gend; grp += kResXcds) {
+  const int b0 = grp * 4;
   const size_t goff = (size_t)grp * gsz;
+  if (grp != xcc) __syncthreads();  // the previous group's last reads of the plane are done
   res_load_plane(plane, p.h0 + goff, N);
   if (tid == 0) plane[N] = f4(0.f);
   __builtin_amdgcn_s_waitcnt(0);
@@ -321,22 +328,23 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
       bst4(h, p.hplanes + (size_t)(s - 1) * psz + goff, rowb, 0);
     }
     if (s == p.c.S) break;
-    if (!res_barrier(p.c, grp, s, &s_fail)) return;
+    if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
     res_load_plane(plane, p.hplanes + (size_t)(s - 1) * psz + goff, N, rank * ((N + 63) / 64) / p.c.ranks);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  }
 }
 
-template <int D>
+template <int D, bool MULTI>
 __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
   extern __shared__ float4 sm[];
   __shared__ int s_rank;
   __shared__ int s_fail;
   const int tid = threadIdx.x;
-  const int grp = (int)xcc_id();
+  const int xcc = (int)xcc_id();
   if (tid == 0) s_fail = 0;
-  const int rank = res_join(p.c, grp, &s_rank);
+  const int rank = res_join(p.c, xcc, &s_rank);
   if (rank < 0) return;
   const int N = p.c.N, B = p.c.B, M = p.c.M, S = p.c.S;
   float4* plane = sm;
@@ -363,13 +371,13 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
     ks = p.c.input_slot[row];
   }
   const uint32_t ksb = (uint32_t)(ks >= 0 ? ks : 0) * (uint32_t)B * 4u;
-  const int b0 = grp * 4;
-  // number of real batch columns in this group (the rest are padding)
-  const int live = B - b0 < 4 ? B - b0 : 4;
+  // the column group being computed (set per pass below): its first batch
+  // column, its number of real columns (the rest are padding), its slice
+  int b0 = 0, live = 0;
+  size_t goff = 0;
   const uint32_t colN = (uint32_t)N * 4u;  // bytes between batch columns of [B][N] tensors
   const size_t gsz = (size_t)p.c.Np * 4;
   const size_t psz = gsz * p.c.G;
-  const size_t goff = (size_t)grp * gsz;
   // h^(s) of the group (s = 0: the initial state), a^(s), ga^(s)
   auto hpl = [&](int s) { return s == 0 ? p.h0 + goff : p.hplanes + (size_t)(s - 1) * psz + goff; };
   auto apl = [&](int s) { return p.aplanes + (size_t)(s - 1) * psz + goff; };
@@ -430,10 +438,23 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
     }
     bst4(ga4, gapl(k), rowb, 0);
   };
+  int round = 0;
+  const int gend = MULTI ? p.c.G : xcc + 1;
+  for (int grp = xcc; grp < gend; grp += kResXcds) {
+  b0 = grp * 4;
+  live = B - b0 < 4 ? B - b0 : 4;
+  goff = (size_t)grp * gsz;
+  gh = f4(0.f);
+  gd = f4(0.f);
+  gl = 0.f;
+  gb = 0.f;
+#pragma unroll
+  for (int j = 0; j < D; ++j) gvacc[j] = 0.f;
+  if (grp != xcc) __syncthreads();  // the previous group's last reads of the plane are done
   // the last microstep's elementwise pass seeds the reverse sweep
   if (owner) k1(S, f4(0.f), gin(S), bld4(apl(S), rowb, 0), bld4(hpl(S - 1), rowb, 0));
   float4 hq = prow >= 0 ? bld4(hpl(S - 1), prowb, 0) : f4(0.f);
-  if (!res_barrier(p.c, grp, 1, &s_fail)) return;
+  if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
   res_load_plane(plane, gapl(S), N, rank * ((N + 63) / 64) / p.c.ranks);
   if (tid == 0) plane[N] = f4(0.f);
   __builtin_amdgcn_s_waitcnt(0);
@@ -491,7 +512,7 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
     }
     hq = hq_next;
     if (s == 1) break;
-    if (!res_barrier(p.c, grp, S - s + 2, &s_fail)) return;
+    if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
     res_load_plane(plane, gapl(s - 1), N, rank * ((N + 63) / 64) / p.c.ranks);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -504,6 +525,7 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
   if (owner) {
     p.glpart[(size_t)grp * N + row] = gl;
     p.gbpart[(size_t)grp * N + row] = gb;
+  }
   }
 }
 
@@ -601,23 +623,23 @@ inline unsigned res_grid(int64_t n) {
 using ResFwdFn = void (*)(ResFwdArgs);
 using ResBwdFn = void (*)(ResBwdArgs);
 
-ResFwdFn fwd_kernel(int D) {
+ResFwdFn fwd_kernel(int D, bool multi) {
   switch (D) {
-    case 8: return &res_fwd<8>;
-    case 12: return &res_fwd<12>;
-    case 16: return &res_fwd<16>;
-    case 20: return &res_fwd<20>;
-    case 24: return &res_fwd<24>;
+    case 8: return multi ? &res_fwd<8, true> : &res_fwd<8, false>;
+    case 12: return multi ? &res_fwd<12, true> : &res_fwd<12, false>;
+    case 16: return multi ? &res_fwd<16, true> : &res_fwd<16, false>;
+    case 20: return multi ? &res_fwd<20, true> : &res_fwd<20, false>;
+    case 24: return multi ? &res_fwd<24, true> : &res_fwd<24, false>;
   }
   return nullptr;
 }
-ResBwdFn bwd_kernel(int D) {
+ResBwdFn bwd_kernel(int D, bool multi) {
   switch (D) {
-    case 8: return &res_bwd<8>;
-    case 12: return &res_bwd<12>;
-    case 16: return &res_bwd<16>;
-    case 20: return &res_bwd<20>;
-    case 24: return &res_bwd<24>;
+    case 8: return multi ? &res_bwd<8, true> : &res_bwd<8, false>;
+    case 12: return multi ? &res_bwd<12, true> : &res_bwd<12, false>;
+    case 16: return multi ? &res_bwd<16, true> : &res_bwd<16, false>;
+    case 20: return multi ? &res_bwd<20, true> : &res_bwd<20, false>;
+    case 24: return multi ? &res_bwd<24, true> : &res_bwd<24, false>;
   }
   return nullptr;
 }
@@ -659,12 +681,13 @@ ck_status res_prepare() {
   // the largest dynamic LDS a resident launch asks for (the plane of
   // kResMaxN nodes and the partial sums), allowed once for every kernel
   const int lds = (int)res_lds_bytes((int)kResMaxN);
-  for (int D : kResPieceLens) {
-    CK_HIP_TRY(hipFuncSetAttribute((const void*)fwd_kernel(D),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-    CK_HIP_TRY(hipFuncSetAttribute((const void*)bwd_kernel(D),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-  }
+  for (int D : kResPieceLens)
+    for (bool multi : {false, true}) {
+      CK_HIP_TRY(hipFuncSetAttribute((const void*)fwd_kernel(D, multi),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+      CK_HIP_TRY(hipFuncSetAttribute((const void*)bwd_kernel(D, multi),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    }
   return CK_OK;
 }
 
@@ -691,7 +714,7 @@ ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_val
                       const float* state0, float* out, void* saved, void* workspace,
                       hipStream_t stream) {
   const Resident& r = g->res_fwd;
-  const ResFwdFn kern = fwd_kernel(r.D);
+  const ResFwdFn kern = fwd_kernel(r.D, d.G > kResXcds);
   if (!kern) {
     set_error("no resident forward kernel for piece length %d", r.D);
     return CK_ERR_HIP;
@@ -730,7 +753,7 @@ ck_status res_backward(const ck_graph* g, const ResDims& d, const float* edge_va
                        float* grad_bias, float* grad_drives, float* grad_state0, void* workspace,
                        hipStream_t stream) {
   const Resident& r = g->res_bwd;
-  const ResBwdFn kern = bwd_kernel(r.D);
+  const ResBwdFn kern = bwd_kernel(r.D, d.G > kResXcds);
   if (!kern) {
     set_error("no resident backward kernel for piece length %d", r.D);
     return CK_ERR_HIP;

@@ -125,8 +125,8 @@ def _mixed_graph(seed, B, T, M, N=400, E=9000, n_in=9):
     return w
 
 
-@pytest.mark.parametrize("B,path", [(b, p) for b in (1, 2, 3, 5, 8, 20, 31, 32) for p in PATHS]
-                         + [(b, "per_microstep") for b in (33, 64, 65, 100)])
+@pytest.mark.parametrize("B,path", [(b, p) for b in (1, 2, 3, 5, 8, 20, 31, 32, 33, 64, 65, 100)
+                                    for p in PATHS])
 def test_batch_widths_parity(B, path):
     w = _mixed_graph(100 + B, B=B, T=3, M=2)
     log(f"parity: mixed graph B={B} E={w.num_edges}, {path} kernels")
