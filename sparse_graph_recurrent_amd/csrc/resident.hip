@@ -267,7 +267,17 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
   const int r0 = p.c.rank_rows[rank], r1 = p.c.rank_rows[rank + 1];
   Piece<D> pc;
   pc.load(p.c.pedge, rank, tid);
-  const int hb = p.c.piece_blk[(size_t)rank * kResLanes + tid];
+  // the lane's segment: the run of lanes of its wave holding pieces of the
+  // same row (pieces of a row take consecutive lanes), from its first lane
+  const int prow = p.c.piece_row[(size_t)rank * kResLanes + tid];
+  const int lane = tid & 63;
+  int seg0;
+  {
+    const int before = __shfl_up(prow, 1);
+    const unsigned long long starts = __ballot(lane == 0 || before != prow);
+    const unsigned long long upto = starts & (lane == 63 ? ~0ull : ((2ull << lane) - 1ull));
+    seg0 = 63 - __builtin_clzll(upto);
+  }
   const bool owner = r0 + tid < r1;
   const int row = owner ? r0 + tid : 0;
   const uint32_t rowb = (uint32_t)row * 16u;
@@ -309,11 +319,24 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
     float4 acc = f4(0.f);
 #pragma unroll
     for (int j = 0; j < D; ++j) acc = fma4(pc.val[j], plane[pc.at(j)], acc);
+    // inclusive scan of the partial sums inside each segment: the segment's
+    // last lane ends with the sum of the row's pieces held by this wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float4 u = make_float4(__shfl_up(acc.x, d), __shfl_up(acc.y, d), __shfl_up(acc.z, d),
+                                   __shfl_up(acc.w, d));
+      const bool in = lane - d >= seg0;
+      acc.x = in ? acc.x + u.x : acc.x;
+      acc.y = in ? acc.y + u.y : acc.y;
+      acc.z = in ? acc.z + u.z : acc.z;
+      acc.w = in ? acc.w + u.w : acc.w;
+    }
     part[tid] = acc;
     __syncthreads();
-    block_sums(p.c, part, hb);
     if (owner) {
-      const float4 sum = row_sum(p.c, part, pb, pe);
+      // one segment end per wave the row's pieces touch
+      float4 sum = f4(0.f);
+      for (int q = pb; q < pe; q = (q | 63) + 1) sum = add4(sum, part[min(pe - 1, q | 63)]);
       const float4 hp = plane[row];
       float4 a, h;
       a.x = sum.x + drv.x + beta;
