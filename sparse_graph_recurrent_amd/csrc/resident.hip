@@ -9,21 +9,25 @@
 // kernel-boundary cache flush every microstep.  Here one launch runs every
 // microstep of a call.  Batch columns never interact, so the batch is cut
 // into groups of 4 columns and group c is computed entirely by the
-// workgroups of XCD c: those share one L2, so a microstep's new state
-// (written by all of them) is exchanged through that L2 behind a counter
-// barrier local to the XCD, with no cross-XCD coherence traffic.
+// workgroups of XCD c mod 8 (an XCD with several groups computes them in
+// turn): those share one L2, so a microstep's new state (written by all of
+// them) is exchanged through that L2 behind a counter barrier local to the
+// XCD, with no cross-XCD coherence traffic.
 //
 // Each workgroup (1024 threads, one per CU) keeps the whole state plane of its
 // column group ([N + 1] x float4, row N all zeros) in LDS, and holds its share
 // of the edges in registers for the whole launch: lane l holds one "piece" of
-// at most D consecutive edges of one row (host plan in schedule.cpp).  A
-// microstep is
+// at most D edges of one row (host plan in schedule.cpp; a row's pieces take
+// consecutive lanes, and each piece's edges are ordered against LDS bank
+// conflicts).  A microstep is
 //   1. every lane gathers its D source rows from LDS and forms the piece's
 //      partial sum (float4 over the group's 4 columns);
-//   2. each row's owner lane adds its pieces' partials in lane order and runs
-//      the row's epilogue, writing the new row to this microstep's plane in
-//      global memory (the saved-state arena, or the exchange planes of the
-//      backward);
+//   2. the pieces' partial sums are added per row (forward: a segmented
+//      scan across each wave, then the row's owner lane adds one value per
+//      wave; backward: the owner adds its pieces, in two levels for long
+//      rows) and the owner runs the row's epilogue, writing the new row to
+//      this microstep's plane in global memory (the saved-state arena, or the
+//      exchange planes of the backward);
 //   3. the XCD's workgroups meet at a counter barrier, and every workgroup
 //      copies the new plane into its LDS (global -> LDS loads, 16 B per lane).
 // Every sum has a fixed order, so results are bitwise reproducible.  Every
@@ -297,65 +301,65 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
   int round = 0;
   const int gend = MULTI ? p.c.G : xcc + 1;
   for (int grp = xcc; grp < gend; grp += kResXcds) {
-  const int b0 = grp * 4;
-  const size_t goff = (size_t)grp * gsz;
-  if (grp != xcc) __syncthreads();  // the previous group's last reads of the plane are done
-  res_load_plane(plane, p.h0 + goff, N);
-  if (tid == 0) plane[N] = f4(0.f);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int s = 1; s <= p.c.S; ++s) {
-    const int t = (s - 1) / p.c.M;
-    // the drive of an input row, requested before the gathers
-    float4 drv = f4(0.f);
-    if (owner && ks >= 0) {
-      const float* dr = p.drives + (size_t)t * p.c.n_in * B;
-      if (b0 < B) drv.x = bld1(dr, ksb, (uint32_t)b0 * 4u);
-      if (b0 + 1 < B) drv.y = bld1(dr, ksb, (uint32_t)(b0 + 1) * 4u);
-      if (b0 + 2 < B) drv.z = bld1(dr, ksb, (uint32_t)(b0 + 2) * 4u);
-      if (b0 + 3 < B) drv.w = bld1(dr, ksb, (uint32_t)(b0 + 3) * 4u);
-    }
-    pc.launder();
-    float4 acc = f4(0.f);
-#pragma unroll
-    for (int j = 0; j < D; ++j) acc = fma4(pc.val[j], plane[pc.at(j)], acc);
-    // inclusive scan of the partial sums inside each segment: the segment's
-    // last lane ends with the sum of the row's pieces held by this wave
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float4 u = make_float4(__shfl_up(acc.x, d), __shfl_up(acc.y, d), __shfl_up(acc.z, d),
-                                   __shfl_up(acc.w, d));
-      const bool in = lane - d >= seg0;
-      acc.x = in ? acc.x + u.x : acc.x;
-      acc.y = in ? acc.y + u.y : acc.y;
-      acc.z = in ? acc.z + u.z : acc.z;
-      acc.w = in ? acc.w + u.w : acc.w;
-    }
-    part[tid] = acc;
-    __syncthreads();
-    if (owner) {
-      // one segment end per wave the row's pieces touch
-      float4 sum = f4(0.f);
-      for (int q = pb; q < pe; q = (q | 63) + 1) sum = add4(sum, part[min(pe - 1, q | 63)]);
-      const float4 hp = plane[row];
-      float4 a, h;
-      a.x = sum.x + drv.x + beta;
-      a.y = sum.y + drv.y + beta;
-      a.z = sum.z + drv.z + beta;
-      a.w = sum.w + drv.w + beta;
-      h.x = (1.0f - lam) * hp.x + lam * ftanh(a.x);
-      h.y = (1.0f - lam) * hp.y + lam * ftanh(a.y);
-      h.z = (1.0f - lam) * hp.z + lam * ftanh(a.z);
-      h.w = (1.0f - lam) * hp.w + lam * ftanh(a.w);
-      bst4(a, p.aplanes + (size_t)(s - 1) * psz + goff, rowb, 0);
-      bst4(h, p.hplanes + (size_t)(s - 1) * psz + goff, rowb, 0);
-    }
-    if (s == p.c.S) break;
-    if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
-    res_load_plane(plane, p.hplanes + (size_t)(s - 1) * psz + goff, N, rank * ((N + 63) / 64) / p.c.ranks);
+    const int b0 = grp * 4;
+    const size_t goff = (size_t)grp * gsz;
+    if (grp != xcc) __syncthreads();  // the previous group's last reads of the plane are done
+    res_load_plane(plane, p.h0 + goff, N);
+    if (tid == 0) plane[N] = f4(0.f);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+    for (int s = 1; s <= p.c.S; ++s) {
+      const int t = (s - 1) / p.c.M;
+      // the drive of an input row, requested before the gathers
+      float4 drv = f4(0.f);
+      if (owner && ks >= 0) {
+        const float* dr = p.drives + (size_t)t * p.c.n_in * B;
+        if (b0 < B) drv.x = bld1(dr, ksb, (uint32_t)b0 * 4u);
+        if (b0 + 1 < B) drv.y = bld1(dr, ksb, (uint32_t)(b0 + 1) * 4u);
+        if (b0 + 2 < B) drv.z = bld1(dr, ksb, (uint32_t)(b0 + 2) * 4u);
+        if (b0 + 3 < B) drv.w = bld1(dr, ksb, (uint32_t)(b0 + 3) * 4u);
+      }
+      pc.launder();
+      float4 acc = f4(0.f);
+#pragma unroll
+      for (int j = 0; j < D; ++j) acc = fma4(pc.val[j], plane[pc.at(j)], acc);
+      // inclusive scan of the partial sums inside each segment: the segment's
+      // last lane ends with the sum of the row's pieces held by this wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float4 u = make_float4(__shfl_up(acc.x, d), __shfl_up(acc.y, d), __shfl_up(acc.z, d),
+                                     __shfl_up(acc.w, d));
+        const bool in = lane - d >= seg0;
+        acc.x = in ? acc.x + u.x : acc.x;
+        acc.y = in ? acc.y + u.y : acc.y;
+        acc.z = in ? acc.z + u.z : acc.z;
+        acc.w = in ? acc.w + u.w : acc.w;
+      }
+      part[tid] = acc;
+      __syncthreads();
+      if (owner) {
+        // one segment end per wave the row's pieces touch
+        float4 sum = f4(0.f);
+        for (int q = pb; q < pe; q = (q | 63) + 1) sum = add4(sum, part[min(pe - 1, q | 63)]);
+        const float4 hp = plane[row];
+        float4 a, h;
+        a.x = sum.x + drv.x + beta;
+        a.y = sum.y + drv.y + beta;
+        a.z = sum.z + drv.z + beta;
+        a.w = sum.w + drv.w + beta;
+        h.x = (1.0f - lam) * hp.x + lam * ftanh(a.x);
+        h.y = (1.0f - lam) * hp.y + lam * ftanh(a.y);
+        h.z = (1.0f - lam) * hp.z + lam * ftanh(a.z);
+        h.w = (1.0f - lam) * hp.w + lam * ftanh(a.w);
+        bst4(a, p.aplanes + (size_t)(s - 1) * psz + goff, rowb, 0);
+        bst4(h, p.hplanes + (size_t)(s - 1) * psz + goff, rowb, 0);
+      }
+      if (s == p.c.S) break;
+      if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
+      res_load_plane(plane, p.hplanes + (size_t)(s - 1) * psz + goff, N, rank * ((N + 63) / 64) / p.c.ranks);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 }
 
@@ -464,91 +468,91 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
   int round = 0;
   const int gend = MULTI ? p.c.G : xcc + 1;
   for (int grp = xcc; grp < gend; grp += kResXcds) {
-  b0 = grp * 4;
-  live = B - b0 < 4 ? B - b0 : 4;
-  goff = (size_t)grp * gsz;
-  gh = f4(0.f);
-  gd = f4(0.f);
-  gl = 0.f;
-  gb = 0.f;
+    b0 = grp * 4;
+    live = B - b0 < 4 ? B - b0 : 4;
+    goff = (size_t)grp * gsz;
+    gh = f4(0.f);
+    gd = f4(0.f);
+    gl = 0.f;
+    gb = 0.f;
 #pragma unroll
-  for (int j = 0; j < D; ++j) gvacc[j] = 0.f;
-  if (grp != xcc) __syncthreads();  // the previous group's last reads of the plane are done
-  // the last microstep's elementwise pass seeds the reverse sweep
-  if (owner) k1(S, f4(0.f), gin(S), bld4(apl(S), rowb, 0), bld4(hpl(S - 1), rowb, 0));
-  float4 hq = prow >= 0 ? bld4(hpl(S - 1), prowb, 0) : f4(0.f);
-  if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
-  res_load_plane(plane, gapl(S), N, rank * ((N + 63) / 64) / p.c.ranks);
-  if (tid == 0) plane[N] = f4(0.f);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int s = S; s >= 1; --s) {
-    // operands of this iteration's elementwise pass (microstep s-1) and of the
-    // next iteration's edge pass, requested before the gathers
-    float4 seed = f4(0.f), ak = f4(0.f), qk = f4(0.f), hq_next = f4(0.f);
-    if (s >= 2) {
-      if (owner) {
-        seed = gin(s - 1);
-        ak = bld4(apl(s - 1), rowb, 0);
-        qk = bld4(hpl(s - 2), rowb, 0);
-      }
-      if (prow >= 0) hq_next = bld4(hpl(s - 2), prowb, 0);
-    }
-    pc.launder();
-    // gathers in groups of 4 rows, so that at most 4 gathered rows occupy
-    // registers beside the piece and its edge-gradient sums
-    float4 acc = f4(0.f);
-#pragma unroll
-    for (int j0 = 0; j0 < D; j0 += 4) {
-      float4 x[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = plane[pc.at(j0 + u)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc = fma4(pc.val[j0 + u], x[u], acc);
-        gvacc[j0 + u] += dot4(x[u], hq);
-        // keep the update here (the optimiser would otherwise sink it past
-        // the barrier below and keep every gathered row alive until then)
-        asm volatile("" : "+v"(gvacc[j0 + u]));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    part[tid] = acc;
-    __syncthreads();
-    block_sums(p.c, part, hb);
-    if (owner) {
-      const float4 sum = row_sum(p.c, part, pb, pe);
-      float4 g;
-      g.x = fmaf(1.0f - lam, gh.x, sum.x);
-      g.y = fmaf(1.0f - lam, gh.y, sum.y);
-      g.z = fmaf(1.0f - lam, gh.z, sum.z);
-      g.w = fmaf(1.0f - lam, gh.w, sum.w);
-      if (s >= 2) {
-        k1(s - 1, g, seed, ak, qk);
-      } else {
-        const uint32_t cb = (uint32_t)b0 * colN;
-        if (live > 0) bst1(g.x, p.gstate0, rowf, cb);
-        if (live > 1) bst1(g.y, p.gstate0, rowf, cb + colN);
-        if (live > 2) bst1(g.z, p.gstate0, rowf, cb + 2 * colN);
-        if (live > 3) bst1(g.w, p.gstate0, rowf, cb + 3 * colN);
-      }
-    }
-    hq = hq_next;
-    if (s == 1) break;
+    for (int j = 0; j < D; ++j) gvacc[j] = 0.f;
+    if (grp != xcc) __syncthreads();  // the previous group's last reads of the plane are done
+    // the last microstep's elementwise pass seeds the reverse sweep
+    if (owner) k1(S, f4(0.f), gin(S), bld4(apl(S), rowb, 0), bld4(hpl(S - 1), rowb, 0));
+    float4 hq = prow >= 0 ? bld4(hpl(S - 1), prowb, 0) : f4(0.f);
     if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
-    res_load_plane(plane, gapl(s - 1), N, rank * ((N + 63) / 64) / p.c.ranks);
+    res_load_plane(plane, gapl(S), N, rank * ((N + 63) / 64) / p.c.ranks);
+    if (tid == 0) plane[N] = f4(0.f);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
-  // partial results of this column group
-  const int64_t slots = (int64_t)p.c.ranks * D * kResLanes;
-  float* gvp = p.gvpart + (size_t)grp * slots + (size_t)rank * D * kResLanes + tid;
+    for (int s = S; s >= 1; --s) {
+      // operands of this iteration's elementwise pass (microstep s-1) and of the
+      // next iteration's edge pass, requested before the gathers
+      float4 seed = f4(0.f), ak = f4(0.f), qk = f4(0.f), hq_next = f4(0.f);
+      if (s >= 2) {
+        if (owner) {
+          seed = gin(s - 1);
+          ak = bld4(apl(s - 1), rowb, 0);
+          qk = bld4(hpl(s - 2), rowb, 0);
+        }
+        if (prow >= 0) hq_next = bld4(hpl(s - 2), prowb, 0);
+      }
+      pc.launder();
+      // gathers in groups of 4 rows, so that at most 4 gathered rows occupy
+      // registers beside the piece and its edge-gradient sums
+      float4 acc = f4(0.f);
 #pragma unroll
-  for (int j = 0; j < D; ++j) gvp[(size_t)j * kResLanes] = gvacc[j];
-  if (owner) {
-    p.glpart[(size_t)grp * N + row] = gl;
-    p.gbpart[(size_t)grp * N + row] = gb;
-  }
+      for (int j0 = 0; j0 < D; j0 += 4) {
+        float4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = plane[pc.at(j0 + u)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc = fma4(pc.val[j0 + u], x[u], acc);
+          gvacc[j0 + u] += dot4(x[u], hq);
+          // keep the update here (the optimiser would otherwise sink it past
+          // the barrier below and keep every gathered row alive until then)
+          asm volatile("" : "+v"(gvacc[j0 + u]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      part[tid] = acc;
+      __syncthreads();
+      block_sums(p.c, part, hb);
+      if (owner) {
+        const float4 sum = row_sum(p.c, part, pb, pe);
+        float4 g;
+        g.x = fmaf(1.0f - lam, gh.x, sum.x);
+        g.y = fmaf(1.0f - lam, gh.y, sum.y);
+        g.z = fmaf(1.0f - lam, gh.z, sum.z);
+        g.w = fmaf(1.0f - lam, gh.w, sum.w);
+        if (s >= 2) {
+          k1(s - 1, g, seed, ak, qk);
+        } else {
+          const uint32_t cb = (uint32_t)b0 * colN;
+          if (live > 0) bst1(g.x, p.gstate0, rowf, cb);
+          if (live > 1) bst1(g.y, p.gstate0, rowf, cb + colN);
+          if (live > 2) bst1(g.z, p.gstate0, rowf, cb + 2 * colN);
+          if (live > 3) bst1(g.w, p.gstate0, rowf, cb + 3 * colN);
+        }
+      }
+      hq = hq_next;
+      if (s == 1) break;
+      if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
+      res_load_plane(plane, gapl(s - 1), N, rank * ((N + 63) / 64) / p.c.ranks);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    // partial results of this column group
+    const int64_t slots = (int64_t)p.c.ranks * D * kResLanes;
+    float* gvp = p.gvpart + (size_t)grp * slots + (size_t)rank * D * kResLanes + tid;
+#pragma unroll
+    for (int j = 0; j < D; ++j) gvp[(size_t)j * kResLanes] = gvacc[j];
+    if (owner) {
+      p.glpart[(size_t)grp * N + row] = gl;
+      p.gbpart[(size_t)grp * N + row] = gb;
+    }
   }
 }
 
