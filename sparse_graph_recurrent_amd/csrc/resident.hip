@@ -253,6 +253,22 @@ struct Piece {
   }
 };
 
+// One step of a segmented scan across a wave with a DPP lane move (CTRL:
+// row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143; rows
+// outside ROW_MASK and lanes the move brings nothing to read 0): the moved
+// value is added where `take` holds.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void seg_step(float4& acc, bool take) {
+  const float ux = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.x), CTRL, ROW_MASK, 0xF, false));
+  const float uy = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.y), CTRL, ROW_MASK, 0xF, false));
+  const float uz = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.z), CTRL, ROW_MASK, 0xF, false));
+  const float uw = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.w), CTRL, ROW_MASK, 0xF, false));
+  acc.x = take ? acc.x + ux : acc.x;
+  acc.y = take ? acc.y + uy : acc.y;
+  acc.z = take ? acc.z + uz : acc.z;
+  acc.w = take ? acc.w + uw : acc.w;
+}
+
 // MULTI: more than kResXcds column groups, so each XCD computes several in
 // turn (a separate instantiation keeps the one-group kernel's registers).
 template <int D, bool MULTI>
@@ -282,6 +298,11 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
     const unsigned long long upto = starts & (lane == 63 ? ~0ull : ((2ull << lane) - 1ull));
     seg0 = 63 - __builtin_clzll(upto);
   }
+  // a wave whose lanes hold no piece (the plan fills lanes from 0) skips the
+  // gathers: reads of the zero row cost the LDS as much as real ones.  (The
+  // same skip measured slightly slower in the backward, which has fewer idle
+  // waves, so it is not used there.)
+  const bool wlive = __ballot(prow >= 0) != 0ull;
   const bool owner = r0 + tid < r1;
   const int row = owner ? r0 + tid : 0;
   const uint32_t rowb = (uint32_t)row * 16u;
@@ -321,19 +342,20 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
       }
       pc.launder();
       float4 acc = f4(0.f);
+      if (wlive) {
 #pragma unroll
-      for (int j = 0; j < D; ++j) acc = fma4(pc.val[j], plane[pc.at(j)], acc);
-      // inclusive scan of the partial sums inside each segment: the segment's
-      // last lane ends with the sum of the row's pieces held by this wave
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float4 u = make_float4(__shfl_up(acc.x, d), __shfl_up(acc.y, d), __shfl_up(acc.z, d),
-                                     __shfl_up(acc.w, d));
-        const bool in = lane - d >= seg0;
-        acc.x = in ? acc.x + u.x : acc.x;
-        acc.y = in ? acc.y + u.y : acc.y;
-        acc.z = in ? acc.z + u.z : acc.z;
-        acc.w = in ? acc.w + u.w : acc.w;
+        for (int j = 0; j < D; ++j) acc = fma4(pc.val[j], plane[pc.at(j)], acc);
+        // inclusive scan of the partial sums inside each segment: the segment's
+        // last lane ends with the sum of the row's pieces held by this wave.
+        // DPP moves (within 16-lane rows, then row broadcasts) keep it off the
+        // LDS pipe, which the gathers saturate (shuffles through LDS permutes
+        // cost a sixth of the forward).
+        seg_step<0x111, 0xF>(acc, lane - 1 >= seg0);   // row_shr:1
+        seg_step<0x112, 0xF>(acc, lane - 2 >= seg0);   // row_shr:2
+        seg_step<0x114, 0xF>(acc, lane - 4 >= seg0);   // row_shr:4
+        seg_step<0x118, 0xF>(acc, lane - 8 >= seg0);   // row_shr:8
+        seg_step<0x142, 0xA>(acc, seg0 < (lane & ~15)); // row_bcast:15 into rows 1, 3
+        seg_step<0x143, 0xC>(acc, seg0 < 32);           // row_bcast:31 into rows 2, 3
       }
       part[tid] = acc;
       __syncthreads();
