@@ -50,9 +50,6 @@ struct Resident {
   int32_t* pcol = nullptr;        // [slots] node at the other end of the edge, or N (an all-zero row)
   int32_t* pperm = nullptr;       // [slots] caller index of the edge, or -1
   int64_t slots = 0;              // ranks * D * kResLanes
-  int blk = 0;                    // block length of two-level row sums
-  bool two_level = false;         // some row has more than blk pieces
-  int32_t* piece_blk = nullptr;   // [ranks][kResLanes] pieces in the block the lane heads, or 0
 };
 
 }  // namespace ckhip

@@ -393,10 +393,6 @@ ck_status build_resident(const std::vector<int32_t>& ptr, int64_t N, const int32
   CK_HIP_TRY(upload(&out->rank_rows, plan.rank_rows));
   CK_HIP_TRY(upload(&out->owner_pbeg, plan.owner_pbeg));
   CK_HIP_TRY(upload(&out->piece_row, plan.piece_row));
-  CK_HIP_TRY(upload(&out->piece_blk, plan.piece_blk));
-  out->blk = plan.blk;
-  out->two_level = false;
-  for (int32_t v : plan.piece_blk) out->two_level = out->two_level || v > 0;
   int32_t* slot_edge = nullptr;
   hipError_t e = upload(&slot_edge, plan.slot_edge);
   if (e == hipSuccess) e = hipMalloc(&out->pcol, out->slots * sizeof(int32_t));
@@ -416,7 +412,6 @@ void free_resident(Resident* r) {
   (void)hipFree(r->rank_rows);
   (void)hipFree(r->owner_pbeg);
   (void)hipFree(r->piece_row);
-  (void)hipFree(r->piece_blk);
   (void)hipFree(r->pcol);
   (void)hipFree(r->pperm);
   *r = Resident();

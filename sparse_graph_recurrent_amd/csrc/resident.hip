@@ -22,11 +22,10 @@
 // conflicts).  A microstep is
 //   1. every lane gathers its D source rows from LDS and forms the piece's
 //      partial sum (float4 over the group's 4 columns);
-//   2. the pieces' partial sums are added per row (forward: a segmented
-//      scan across each wave, then the row's owner lane adds one value per
-//      wave; backward: the owner adds its pieces, in two levels for long
-//      rows) and the owner runs the row's epilogue, writing the new row to
-//      this microstep's plane in global memory (the saved-state arena, or the
+//   2. the pieces' partial sums are added per row (a segmented scan across
+//      each wave, then the row's owner lane adds one value per wave) and the
+//      owner runs the row's epilogue, writing the new row to this
+//      microstep's plane in global memory (the saved-state arena, or the
 //      exchange planes of the backward);
 //   3. the XCD's workgroups meet at a counter barrier, and every workgroup
 //      copies the new plane into its LDS (global -> LDS loads, 16 B per lane).
@@ -56,39 +55,13 @@ struct ResCommon {
   const int32_t* rank_rows;
   const int32_t* owner_pbeg;
   const int32_t* piece_row;
-  const int32_t* piece_blk;
   const int2* pedge;  // [ranks][D][kResLanes] {node, value bits}
   unsigned* ctl;
   const float* leak;
   const int32_t* input_slot;
   int N, Np, B, G, n_in, M, S, ranks;
   int spin_limit;  // polls before a wait gives up (< 0: every wait gives up at once)
-  int blk;         // block length of two-level row sums
-  int two_level;   // some row is summed in two levels
 };
-
-// A row's sum from the partial sums of its pieces, lanes [pb, pe) of `part`:
-// in lane order, or, for a row of more than blk pieces, over the sums of its
-// blocks of blk lanes, which the block heads (hb = pieces in the block) have
-// written in place at the first lane of each block.  `part` must hold every
-// lane's partial sum when this is entered; it ends with a barrier only when
-// the plan has two-level rows.
-__device__ __forceinline__ void block_sums(const ResCommon& c, float4* part, int hb) {
-  if (!c.two_level) return;
-  if (hb > 0) {
-    const int tid = threadIdx.x;
-    float4 s = part[tid];
-    for (int u = 1; u < hb; ++u) s = add4(s, part[tid + u]);
-    part[tid] = s;
-  }
-  __syncthreads();
-}
-__device__ __forceinline__ float4 row_sum(const ResCommon& c, const float4* part, int pb, int pe) {
-  const int stride = pe - pb > c.blk ? c.blk : 1;
-  float4 sum = f4(0.f);
-  for (int q = pb; q < pe; q += stride) sum = add4(sum, part[q]);
-  return sum;
-}
 
 struct ResFwdArgs {
   ResCommon c;
@@ -269,6 +242,39 @@ __device__ __forceinline__ void seg_step(float4& acc, bool take) {
   acc.w = take ? acc.w + uw : acc.w;
 }
 
+// First lane of the lane's segment: the run of lanes of its wave holding
+// pieces of the same row (a row's pieces take consecutive lanes).
+__device__ __forceinline__ int segment_start(int prow) {
+  const int lane = threadIdx.x & 63;
+  const int before = __shfl_up(prow, 1);
+  const unsigned long long starts = __ballot(lane == 0 || before != prow);
+  const unsigned long long upto = starts & (lane == 63 ? ~0ull : ((2ull << lane) - 1ull));
+  return 63 - __builtin_clzll(upto);
+}
+
+// Inclusive scan of the pieces' partial sums inside each segment: the
+// segment's last lane ends with the sum of the row's pieces held by its wave.
+// DPP moves (within 16-lane rows, then row broadcasts) keep it off the LDS
+// pipe, which the gathers saturate (shuffles through LDS permutes cost a
+// sixth of the forward).
+__device__ __forceinline__ void segmented_scan(float4& acc, int seg0) {
+  const int lane = threadIdx.x & 63;
+  seg_step<0x111, 0xF>(acc, lane - 1 >= seg0);     // row_shr:1
+  seg_step<0x112, 0xF>(acc, lane - 2 >= seg0);     // row_shr:2
+  seg_step<0x114, 0xF>(acc, lane - 4 >= seg0);     // row_shr:4
+  seg_step<0x118, 0xF>(acc, lane - 8 >= seg0);     // row_shr:8
+  seg_step<0x142, 0xA>(acc, seg0 < (lane & ~15));  // row_bcast:15 into rows 1, 3
+  seg_step<0x143, 0xC>(acc, seg0 < 32);            // row_bcast:31 into rows 2, 3
+}
+
+// The owner's row sum: its pieces are lanes [pb, pe) of `part`, which holds
+// every lane's scanned value; one segment end per wave the pieces touch.
+__device__ __forceinline__ float4 row_sum(const float4* part, int pb, int pe) {
+  float4 sum = f4(0.f);
+  for (int q = pb; q < pe; q = (q | 63) + 1) sum = add4(sum, part[min(pe - 1, q | 63)]);
+  return sum;
+}
+
 // MULTI: more than kResXcds column groups, so each XCD computes several in
 // turn (a separate instantiation keeps the one-group kernel's registers).
 template <int D, bool MULTI>
@@ -287,17 +293,8 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
   const int r0 = p.c.rank_rows[rank], r1 = p.c.rank_rows[rank + 1];
   Piece<D> pc;
   pc.load(p.c.pedge, rank, tid);
-  // the lane's segment: the run of lanes of its wave holding pieces of the
-  // same row (pieces of a row take consecutive lanes), from its first lane
   const int prow = p.c.piece_row[(size_t)rank * kResLanes + tid];
-  const int lane = tid & 63;
-  int seg0;
-  {
-    const int before = __shfl_up(prow, 1);
-    const unsigned long long starts = __ballot(lane == 0 || before != prow);
-    const unsigned long long upto = starts & (lane == 63 ? ~0ull : ((2ull << lane) - 1ull));
-    seg0 = 63 - __builtin_clzll(upto);
-  }
+  const int seg0 = segment_start(prow);
   // a wave whose lanes hold no piece (the plan fills lanes from 0) skips the
   // gathers: reads of the zero row cost the LDS as much as real ones.  (The
   // same skip measured slightly slower in the backward, which has fewer idle
@@ -345,24 +342,12 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
       if (wlive) {
 #pragma unroll
         for (int j = 0; j < D; ++j) acc = fma4(pc.val[j], plane[pc.at(j)], acc);
-        // inclusive scan of the partial sums inside each segment: the segment's
-        // last lane ends with the sum of the row's pieces held by this wave.
-        // DPP moves (within 16-lane rows, then row broadcasts) keep it off the
-        // LDS pipe, which the gathers saturate (shuffles through LDS permutes
-        // cost a sixth of the forward).
-        seg_step<0x111, 0xF>(acc, lane - 1 >= seg0);   // row_shr:1
-        seg_step<0x112, 0xF>(acc, lane - 2 >= seg0);   // row_shr:2
-        seg_step<0x114, 0xF>(acc, lane - 4 >= seg0);   // row_shr:4
-        seg_step<0x118, 0xF>(acc, lane - 8 >= seg0);   // row_shr:8
-        seg_step<0x142, 0xA>(acc, seg0 < (lane & ~15)); // row_bcast:15 into rows 1, 3
-        seg_step<0x143, 0xC>(acc, seg0 < 32);           // row_bcast:31 into rows 2, 3
+        segmented_scan(acc, seg0);
       }
       part[tid] = acc;
       __syncthreads();
       if (owner) {
-        // one segment end per wave the row's pieces touch
-        float4 sum = f4(0.f);
-        for (int q = pb; q < pe; q = (q | 63) + 1) sum = add4(sum, part[min(pe - 1, q | 63)]);
+        const float4 sum = row_sum(part, pb, pe);
         const float4 hp = plane[row];
         float4 a, h;
         a.x = sum.x + drv.x + beta;
@@ -405,8 +390,10 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
 #pragma unroll
   for (int j = 0; j < D; ++j) gvacc[j] = 0.f;
   const int prow = p.c.piece_row[(size_t)rank * kResLanes + tid];
-  const int hb = p.c.piece_blk[(size_t)rank * kResLanes + tid];
   const uint32_t prowb = (uint32_t)(prow >= 0 ? prow : 0) * 16u;
+  // (every wave runs the gathers here: skipping idle waves measured slower
+  // in the backward)
+  const int seg0 = segment_start(prow);
   const bool owner = r0 + tid < r1;
   const int row = owner ? r0 + tid : 0;
   const uint32_t rowb = (uint32_t)row * 16u, rowf = (uint32_t)row * 4u;
@@ -539,11 +526,11 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      segmented_scan(acc, seg0);
       part[tid] = acc;
       __syncthreads();
-      block_sums(p.c, part, hb);
       if (owner) {
-        const float4 sum = row_sum(p.c, part, pb, pe);
+        const float4 sum = row_sum(part, pb, pe);
         float4 g;
         g.x = fmaf(1.0f - lam, gh.x, sum.x);
         g.y = fmaf(1.0f - lam, gh.y, sum.y);
@@ -705,9 +692,6 @@ ResCommon common(const Resident& r, const ResDims& d, const int2* pedge, unsigne
   c.rank_rows = r.rank_rows;
   c.owner_pbeg = r.owner_pbeg;
   c.piece_row = r.piece_row;
-  c.piece_blk = r.piece_blk;
-  c.blk = r.blk;
-  c.two_level = r.two_level ? 1 : 0;
   c.pedge = pedge;
   c.ctl = ctl;
   c.leak = leak;

@@ -222,14 +222,6 @@ bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_lens, Resid
   p.D = D;
   p.ranks = ranks;
   pack_ranges(pc, ranks, best_cap, &p.rank_rows);
-  // block length: about the square root of the largest row's piece count, so
-  // that neither level of its sum is long
-  int64_t maxp = 1;
-  for (int64_t i = 0; i < N; ++i) maxp = std::max(maxp, pc[i]);
-  int blk = 8;
-  while (blk < 32 && (int64_t)blk * blk < maxp) ++blk;
-  p.blk = blk;
-  p.piece_blk.assign((size_t)ranks * kResLanes, 0);
   p.owner_pbeg.assign((size_t)ranks * (kResLanes + 1), 0);
   p.piece_row.assign((size_t)ranks * kResLanes, -1);
   p.piece_kbeg.assign((size_t)ranks * kResLanes, 0);
@@ -240,9 +232,6 @@ bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_lens, Resid
     int lane = 0;
     for (int32_t i = r0; i < r1; ++i) {
       pb[i - r0] = lane;
-      if (pc[i] > blk)
-        for (int64_t h = 0; h < pc[i]; h += blk)
-          p.piece_blk[(size_t)r * kResLanes + lane + h] = (int32_t)std::min<int64_t>(blk, pc[i] - h);
       for (int32_t k = ptr[i]; k < ptr[i + 1]; k += D, ++lane) {
         const size_t q = (size_t)r * kResLanes + lane;
         p.piece_row[q] = i;

@@ -84,10 +84,9 @@ void plan_schedule(const int32_t* ptr, int64_t N, int num_cus, int waves, Schedu
 // threads, in registers, for the whole launch.  Rows are cut into contiguous
 // workgroup ranges; inside a range, the pieces of its rows take consecutive
 // lanes in row order, and the row's "owner" (the range's o-th row is owned by
-// lane o) adds its pieces' partial sums in lane order.  A row of more than
-// `blk` pieces is added in two levels: the lanes at its pieces 0, blk, 2 blk,
-// ... ("block heads") first add their block of at most blk partial sums in
-// place, then the owner adds the block sums.
+// lane o) forms the row's sum from its pieces' partial sums: a segmented scan
+// across each 64-lane wave leaves the sum of the row's pieces in that wave at
+// the last of them, and the owner adds these in wave order.
 constexpr int kResLanes = 1024;
 // Piece lengths the kernels are built for.
 constexpr int kResPieceLens[] = {8, 12, 16, 20, 24};
@@ -106,9 +105,6 @@ struct ResidentPlan {
   std::vector<int32_t> piece_row;   // [ranks][kResLanes]: row of the lane's piece, or -1
   std::vector<int32_t> piece_kbeg;  // [ranks][kResLanes]: first edge (compressed index) of the piece
   std::vector<int32_t> piece_cnt;   // [ranks][kResLanes]: edges in the piece (0 if none)
-  int blk = 0;                      // block length of the two-level sums
-  std::vector<int32_t> piece_blk;   // [ranks][kResLanes]: pieces in the lane's block if it is
-                                    // a block head of a row of more than blk pieces, else 0
   std::vector<int32_t> slot_edge;   // [ranks][D][kResLanes]: edge of slot j of lane l, or -1
                                     // (compressed order unless order_resident_slots ran)
 };

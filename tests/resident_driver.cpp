@@ -1,9 +1,9 @@
 // CPU driver for the resident planner: reads "N ranks max_lens order" and the
 // N + 1 row pointers from stdin, then (order = 1) the row read by each
-// compressed edge; prints "none", or "D ranks max_pieces blk cost cost_ordered"
+// compressed edge; prints "none", or "D ranks max_pieces cost cost_ordered"
 // (bank-conflict costs of the slot table in compressed order and after
 // ordering; 0 when not ordered) followed by rank_rows, owner_pbeg, piece_row,
-// piece_kbeg, piece_cnt, piece_blk and slot_edge (one array per line).
+// piece_kbeg, piece_cnt and slot_edge (one array per line).
 #include <cstdio>
 #include <vector>
 
@@ -38,13 +38,12 @@ int main() {
     ckhip::order_resident_slots(col.data(), N, &plan);
     c1 = ckhip::resident_conflict_cost(col.data(), N, plan);
   }
-  std::printf("%d %d %d %d %lld %lld\n", plan.D, plan.ranks, plan.max_pieces, plan.blk, c0, c1);
+  std::printf("%d %d %d %lld %lld\n", plan.D, plan.ranks, plan.max_pieces, c0, c1);
   put(plan.rank_rows);
   put(plan.owner_pbeg);
   put(plan.piece_row);
   put(plan.piece_kbeg);
   put(plan.piece_cnt);
-  put(plan.piece_blk);
   put(plan.slot_edge);
   return 0;
 }

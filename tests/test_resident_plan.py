@@ -4,8 +4,10 @@ a workgroup holding one piece of at most D consecutive edges of a row.
 
 The plan is built with g++ and a small driver, then replayed the way the
 resident kernels use it: lane l of workgroup r sums the edges of its piece,
-and the owner of the range's o-th row adds the partial sums of lanes
-[owner_pbeg[o], owner_pbeg[o + 1]) in lane order.  The replay must give every
+the partial sums are scanned over each run of lanes of a 64-lane wave that
+hold the same row, and the owner of the range's o-th row, whose pieces are
+lanes [owner_pbeg[o], owner_pbeg[o + 1]), adds the run ends of those lanes
+wave by wave.  The replay must give every
 row sum exactly once, every edge must lie in exactly one piece, and the plan
 must stay inside the limits the kernels rely on (1024 lanes and 1024 rows
 per workgroup, D among the built piece lengths).
@@ -46,13 +48,12 @@ def plan(driver, ptr, ranks, lens, col=None):
     lines = out.strip("\n").split("\n")
     if lines[0] == "none":
         return None
-    D, r, max_pieces, blk, c0, c1 = map(int, lines[0].split())
-    arr = [np.array(ln.split(), dtype=np.int64) for ln in lines[1:8]]
-    return dict(D=D, ranks=r, max_pieces=max_pieces, blk=blk, cost=c0, cost_ordered=c1,
+    D, r, max_pieces, c0, c1 = map(int, lines[0].split())
+    arr = [np.array(ln.split(), dtype=np.int64) for ln in lines[1:7]]
+    return dict(D=D, ranks=r, max_pieces=max_pieces, cost=c0, cost_ordered=c1,
                 rank_rows=arr[0], owner_pbeg=arr[1].reshape(r, LANES + 1),
                 piece_row=arr[2].reshape(r, LANES), piece_kbeg=arr[3].reshape(r, LANES),
-                piece_cnt=arr[4].reshape(r, LANES), piece_blk=arr[5].reshape(r, LANES),
-                slot_edge=arr[6].reshape(r, D, LANES))
+                piece_cnt=arr[4].reshape(r, LANES), slot_edge=arr[5].reshape(r, D, LANES))
 
 
 def replay(driver, major, N, ranks=32, lens=5, minor=None):
@@ -103,30 +104,23 @@ def replay(driver, major, N, ranks=32, lens=5, minor=None):
         max_pieces = max(max_pieces, int(ob[nrows]))
         assert ob[nrows] <= LANES
         assert (cnt[ob[nrows]:] == 0).all(), "lanes past the pieces hold no edges"
-        # level 1: block heads of rows with more than blk pieces add their block in place
-        blk, hb = p["blk"], p["piece_blk"][r]
-        assert 8 <= blk <= 32 and ((hb >= 0) & (hb <= blk)).all()
-        part = part.copy()
-        level1 = part.copy()
-        for l in np.nonzero(hb)[0]:
-            assert (prow[l:l + hb[l]] == prow[l]).all(), "a block spans two rows"
-            level1[l] = part[l:l + hb[l]].sum()
-        # level 2: the owner adds its pieces (stride 1) or its block sums (stride blk)
-        heads = set()
+        # the row sums as the kernels form them: an inclusive scan of the
+        # partial sums over each run of lanes of one 64-lane wave holding the
+        # same row, then the owner adds the run ends of its lanes, wave by wave
+        scanned = part.copy()
+        for l in range(1, LANES):
+            if l % 64 and prow[l] == prow[l - 1]:
+                scanned[l] += scanned[l - 1]
         for o in range(nrows):
             row = int(rr[r] + o)
-            lanes = np.arange(ob[o], ob[o + 1])
-            assert (prow[lanes] == row).all(), "owner combines another row's piece"
+            pb, pe = int(ob[o]), int(ob[o + 1])
+            assert (prow[pb:pe] == row).all(), "owner combines another row's piece"
             assert got[row] == np.iinfo(np.int64).min
-            if len(lanes) > blk:
-                hl = lanes[::blk]
-                assert (hb[hl] == np.minimum(blk, ob[o + 1] - hl)).all(), "block head counts"
-                heads.update(hl.tolist())
-                got[row] = int(level1[hl].sum())
-            else:
-                assert (hb[lanes] == 0).all()
-                got[row] = int(part[lanes].sum())
-        assert heads == set(np.nonzero(hb)[0].tolist()), "a block head outside a long row"
+            s, q = 0, pb
+            while q < pe:
+                s += int(scanned[min(pe - 1, q | 63)])
+                q = (q | 63) + 1
+            got[row] = s
     assert (cover == 1).all(), "every edge in exactly one piece"
     np.testing.assert_array_equal(got, want)
     assert max_pieces == p["max_pieces"]
