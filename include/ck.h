@@ -74,7 +74,7 @@ typedef enum {
  * the transposed CSR by source (rows ordered by (dst, caller index)), both
  * edge permutations, the input-slot map and the degree-balanced row schedules.
  * When the device deals a launch's workgroups evenly over 8 XCDs, num_nodes
- * is at most 9200 and the environment variable CK_RESIDENT is not "0" at
+ * is at most 9184 and the environment variable CK_RESIDENT is not "0" at
  * creation, it also plans the XCD-resident kernels (see
  * ck_recurrence_path), which run a whole forward or backward in one launch.
  * The caller's edge order is kept for edge values and their gradient: the

@@ -25,9 +25,9 @@ struct Schedule {
 };
 
 // Largest node count of the XCD-resident kernels: one workgroup holds a
-// whole [N + 1] x 16-byte state plane plus kResLanes 16-byte partial sums in
+// whole [N + kResZeroRows] x 16-byte state plane plus kResLanes 16-byte partial sums in
 // the 160 KiB of LDS of a gfx950 compute unit.
-constexpr int64_t kResMaxN = 9200;
+constexpr int64_t kResMaxN = 9184;
 // XCDs of an MI355X; a launch deals its workgroups round-robin over them.
 constexpr int kResXcds = 8;
 
@@ -47,7 +47,7 @@ struct Resident {
   int32_t* rank_rows = nullptr;   // [ranks + 1]
   int32_t* owner_pbeg = nullptr;  // [ranks][kResLanes + 1]
   int32_t* piece_row = nullptr;   // [ranks][kResLanes], -1 for a lane without a piece
-  int32_t* pcol = nullptr;        // [slots] node at the other end of the edge, or N (an all-zero row)
+  int32_t* pcol = nullptr;        // [slots] node at the other end of the edge, or N + z (all-zero rows)
   int32_t* pperm = nullptr;       // [slots] caller index of the edge, or -1
   int64_t slots = 0;              // ranks * D * kResLanes
 };

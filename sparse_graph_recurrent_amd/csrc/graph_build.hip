@@ -338,7 +338,7 @@ __global__ void pad_resident(const int32_t* __restrict__ slot_edge, int64_t slot
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= slots) return;
   const int32_t k = slot_edge[q];
-  pcol[q] = k >= 0 ? col[k] : N;
+  pcol[q] = k >= 0 ? col[k] : N - 1 - k;  // an empty slot reads zero row N + z, k = -1 - z
   pperm[q] = k >= 0 ? perm[k] : -1;
 }
 

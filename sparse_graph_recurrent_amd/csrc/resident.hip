@@ -15,7 +15,7 @@
 // XCD, with no cross-XCD coherence traffic.
 //
 // Each workgroup (1024 threads, one per CU) keeps the whole state plane of its
-// column group ([N + 1] x float4, row N all zeros) in LDS, and holds its share
+// column group ([N + 16] x float4, rows N.. all zeros) in LDS, and holds its share
 // of the edges in registers for the whole launch: lane l holds one "piece" of
 // at most D edges of one row (host plan in schedule.cpp; a row's pieces take
 // consecutive lanes, and each piece's edges are ordered against LDS bank
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
   if (rank < 0) return;
   const int N = p.c.N, B = p.c.B;
   float4* plane = sm;             // [N + 1]
-  float4* part = sm + (N + 1);    // [kResLanes]
+  float4* part = sm + (N + kResZeroRows);  // [kResLanes]
   const int r0 = p.c.rank_rows[rank], r1 = p.c.rank_rows[rank + 1];
   Piece<D> pc;
   pc.load(p.c.pedge, rank, tid);
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
     const size_t goff = (size_t)grp * gsz;
     if (grp != xcc) __syncthreads();  // the previous group's last reads of the plane are done
     res_load_plane(plane, p.h0 + goff, N);
-    if (tid == 0) plane[N] = f4(0.f);
+    if (tid < kResZeroRows) plane[N + tid] = f4(0.f);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int s = 1; s <= p.c.S; ++s) {
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
   if (rank < 0) return;
   const int N = p.c.N, B = p.c.B, M = p.c.M, S = p.c.S;
   float4* plane = sm;
-  float4* part = sm + (N + 1);
+  float4* part = sm + (N + kResZeroRows);
   const int r0 = p.c.rank_rows[rank], r1 = p.c.rank_rows[rank + 1];
   Piece<D> pc;
   pc.load(p.c.pedge, rank, tid);
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
     float4 hq = prow >= 0 ? bld4(hpl(S - 1), prowb, 0) : f4(0.f);
     if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
     res_load_plane(plane, gapl(S), N, rank * ((N + 63) / 64) / p.c.ranks);
-    if (tid == 0) plane[N] = f4(0.f);
+    if (tid < kResZeroRows) plane[N + tid] = f4(0.f);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int s = S; s >= 1; --s) {
@@ -681,10 +681,10 @@ ResBwdFn bwd_kernel(int D, bool multi) {
   return nullptr;
 }
 
-// LDS of a resident workgroup: the plane and the partial sums, and at least
-// 82 KiB so that a CU never holds two of them.
+// LDS of a resident workgroup: the plane with its zero rows and the partial
+// sums, and at least 82 KiB so that a CU never holds two of them.
 size_t res_lds_bytes(int N) {
-  return std::max<size_t>((size_t)(N + 1) * 16 + (size_t)kResLanes * 16, 82 * 1024);
+  return std::max<size_t>((size_t)(N + kResZeroRows) * 16 + (size_t)kResLanes * 16, 82 * 1024);
 }
 
 ResCommon common(const Resident& r, const ResDims& d, const int2* pedge, unsigned* ctl,

@@ -3,7 +3,6 @@
 #include "schedule.h"
 
 #include <algorithm>
-#include <functional>
 
 namespace ckhip {
 
@@ -279,7 +278,7 @@ int64_t resident_conflict_cost(const int32_t* col, int64_t N, const ResidentPlan
         bool any = false;
         for (int u = 0; u < kResBankGroups; ++u) {
           const int32_t e = p.slot_edge[((size_t)r * p.D + j) * kResLanes + g + u];
-          rows[u] = e >= 0 ? col[e] : (int32_t)N;
+          rows[u] = e >= 0 ? col[e] : (int32_t)N - 1 - e;
           any = any || e >= 0;
         }
         if (any) cost += group_cost(rows, kResBankGroups);
@@ -287,95 +286,110 @@ int64_t resident_conflict_cost(const int32_t* col, int64_t N, const ResidentPlan
   return cost;
 }
 
-// Per aligned group of kResBankGroups lanes, slot by slot: a maximum matching
-// of lanes (with edges left) to bank groups not yet used in this slot, found
-// with augmenting paths, trying for each lane first the bank groups it has
-// most edges left in (those are the hard ones to place later).  A lane left
-// unmatched takes an empty slot if its piece is short (the all-zero row),
-// else the edge of its most frequent bank group (a conflict).
+namespace {
+
+// Minimum-cost perfect assignment of rows to columns of an n x n integer cost
+// matrix (the Hungarian method with row and column potentials, shortest
+// augmenting paths).  Writes col_of_row[0..n).
+void assign_min_cost(const int* cost, int n, int* col_of_row) {
+  constexpr int kInf = 1 << 29;
+  std::vector<int> pu(n + 1, 0), pv(n + 1, 0), row_of(n + 1, 0), way(n + 1, 0), minv(n + 1);
+  std::vector<char> used(n + 1);
+  for (int i = 1; i <= n; ++i) {
+    row_of[0] = i;
+    int j0 = 0;
+    std::fill(minv.begin(), minv.end(), kInf);
+    std::fill(used.begin(), used.end(), 0);
+    do {
+      used[j0] = 1;
+      const int i0 = row_of[j0];
+      int delta = kInf, j1 = 0;
+      for (int j = 1; j <= n; ++j) {
+        if (used[j]) continue;
+        const int cur = cost[(i0 - 1) * n + (j - 1)] - pu[i0] - pv[j];
+        if (cur < minv[j]) {
+          minv[j] = cur;
+          way[j] = j0;
+        }
+        if (minv[j] < delta) {
+          delta = minv[j];
+          j1 = j;
+        }
+      }
+      for (int j = 0; j <= n; ++j) {
+        if (used[j]) {
+          pu[row_of[j]] += delta;
+          pv[j] -= delta;
+        } else {
+          minv[j] -= delta;
+        }
+      }
+      j0 = j1;
+    } while (row_of[j0] != 0);
+    do {
+      const int j1 = way[j0];
+      row_of[j0] = row_of[j1];
+      j0 = j1;
+    } while (j0 != 0);
+  }
+  for (int j = 1; j <= n; ++j) col_of_row[row_of[j] - 1] = j - 1;
+}
+
+}  // namespace
+
 void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out) {
   ResidentPlan& p = *out;
   const int D = p.D;
   constexpr int G = kResBankGroups;
-  std::vector<int32_t> left[G][G];
+  constexpr int W = 64;                 // lanes per wave
+  constexpr int kEdge = 10, kEmpty = 9;  // what a lane can offer a bank group
+  const int zero_group = (int)(N % G);  // bank group of zero row N
+  std::vector<int32_t> left[W][G];      // per lane: its remaining edges by bank group
+  p.order_misses = 0;
   for (int r = 0; r < p.ranks; ++r)
-    for (int g0 = 0; g0 < kResLanes; g0 += G) {
-      // remaining edges of each lane, by bank group
-      int nleft[G] = {0}, pads[G] = {0};
+    for (int w0 = 0; w0 < kResLanes; w0 += W) {
+      int empty[W];
       bool any = false;
-      for (int u = 0; u < G; ++u) {
+      for (int u = 0; u < W; ++u) {
         for (int b = 0; b < G; ++b) left[u][b].clear();
-        const size_t q = (size_t)r * kResLanes + g0 + u;
+        const size_t q = (size_t)r * kResLanes + w0 + u;
         for (int j = 0; j < p.piece_cnt[q]; ++j) {
           const int32_t e = p.piece_kbeg[q] + j;
           left[u][col[e] % G].push_back(e);
         }
-        nleft[u] = p.piece_cnt[q];
-        pads[u] = D - p.piece_cnt[q];
-        any = any || nleft[u] > 0;
+        empty[u] = D - p.piece_cnt[q];
+        any = any || p.piece_cnt[q] > 0;
       }
-      if (!any) continue;
+      if (!any) continue;  // a wave without pieces keeps reading zero row N
       for (int j = 0; j < D; ++j) {
-        int owner_of[G];  // bank group -> lane matched to it in this slot
-        int match[G];     // lane -> bank group, or -1
-        int order[G][G];  // per lane: its bank groups with edges left, most edges first
-        int nord[G];
-        for (int u = 0; u < G; ++u) {
-          owner_of[u] = -1;
-          match[u] = -1;
-          int n = 0;
-          for (int b = 0; b < G; ++b)
-            if (!left[u][b].empty()) order[u][n++] = b;
-          std::sort(order[u], order[u] + n, [&](int x, int y) {
-            return left[u][x].size() != left[u][y].size() ? left[u][x].size() > left[u][y].size()
-                                                           : x < y;
-          });
-          nord[u] = n;
-        }
-        std::function<bool(int, bool*)> augment = [&](int u, bool* seen) -> bool {
-          for (int k = 0; k < nord[u]; ++k) {
-            const int b = order[u][k];
-            if (seen[b]) continue;
-            seen[b] = true;
-            if (owner_of[b] < 0 || augment(owner_of[b], seen)) {
-              owner_of[b] = u;
-              match[u] = b;
-              return true;
-            }
+        int cost[G * G];
+        for (int c = 0; c < G; ++c)
+          for (int b = 0; b < G; ++b) {
+            int offer = 0;
+            for (int u = c; u < W; u += G)
+              offer += !left[u][b].empty() ? kEdge : (empty[u] > 0 ? kEmpty : 0);
+            cost[c * G + b] = (W / G) * kEdge - offer;
           }
-          return false;
-        };
-        // lanes with the fewest empty slots to spare go first
-        int lanes[G];
-        for (int u = 0; u < G; ++u) lanes[u] = u;
-        std::sort(lanes, lanes + G, [&](int x, int y) {
-          return pads[x] != pads[y] ? pads[x] < pads[y] : x < y;
-        });
-        for (int k = 0; k < G; ++k) {
-          const int u = lanes[k];
-          if (nleft[u] == 0) continue;
-          bool seen[G] = {false};
-          augment(u, seen);
-        }
-        for (int u = 0; u < G; ++u) {
-          const size_t slot = ((size_t)r * D + j) * kResLanes + g0 + u;
-          int b = match[u];
-          if (b < 0) {
-            if (nleft[u] == 0 || pads[u] > 0) {
-              if (pads[u] > 0) --pads[u];
-              p.slot_edge[slot] = -1;
+        int perm[G];
+        assign_min_cost(cost, G, perm);
+        for (int u = 0; u < W; ++u) {
+          int32_t& slot = p.slot_edge[((size_t)r * D + j) * kResLanes + w0 + u];
+          int b = perm[u % G];
+          if (left[u][b].empty()) {
+            if (empty[u] > 0) {
+              --empty[u];
+              slot = -1 - (b - zero_group + G) % G;
               continue;
             }
-            b = order[u][0];
+            for (int k = 0; k < G; ++k)
+              if (left[u][k].size() > left[u][b].size()) b = k;
+            ++p.order_misses;
           }
-          p.slot_edge[slot] = left[u][b].back();
+          slot = left[u][b].back();
           left[u][b].pop_back();
-          --nleft[u];
         }
       }
     }
-  (void)N;
 }
-
 
 }  // namespace ckhip

@@ -99,28 +99,39 @@ struct ResidentPlan {
   int D = 0;                        // edges per piece
   int ranks = 0;                    // workgroups per XCD
   int max_pieces = 0;               // pieces on the busiest workgroup
+  int64_t order_misses = 0;         // slots off their wave's bank-group permutation
+                                    // (set by order_resident_slots)
   std::vector<int32_t> rank_rows;   // [ranks + 1]: rows of workgroup r are [rank_rows[r], rank_rows[r+1])
   std::vector<int32_t> owner_pbeg;  // [ranks][kResLanes + 1]: the pieces of the r-th range's row o
                                     // are lanes [owner_pbeg[o], owner_pbeg[o+1]); constant past the range
   std::vector<int32_t> piece_row;   // [ranks][kResLanes]: row of the lane's piece, or -1
   std::vector<int32_t> piece_kbeg;  // [ranks][kResLanes]: first edge (compressed index) of the piece
   std::vector<int32_t> piece_cnt;   // [ranks][kResLanes]: edges in the piece (0 if none)
-  std::vector<int32_t> slot_edge;   // [ranks][D][kResLanes]: edge of slot j of lane l, or -1
-                                    // (compressed order unless order_resident_slots ran)
+  std::vector<int32_t> slot_edge;   // [ranks][D][kResLanes]: edge of slot j of lane l, or
+                                    // -1 - z for an empty slot, which reads zero row N + z
+                                    // (compressed order and z = 0 unless order_resident_slots ran)
 };
 
-// LDS rows are 16 bytes and the LDS serves a 16-byte-per-lane read 16 lanes at
-// a time, conflict-free when those 16 lanes read rows in distinct bank
-// groups (row index mod kResBankGroups) or the same row.
+// LDS rows are 16 bytes; a row's bank group is its index mod kResBankGroups.
+// Measured on gfx950: a wave's 16-byte-per-lane read runs at full rate when
+// lanes l, l + 16, l + 32 and l + 48 read rows of one bank group and the 16
+// lanes of each 16-lane group read 16 different bank groups (one permutation
+// of bank groups shared by the wave's four 16-lane groups); distinct bank
+// groups chosen separately per 16-lane group run at about 70 % of that rate,
+// random rows at about 45 %.
 constexpr int kResBankGroups = 16;
+// Each plane ends with this many all-zero rows (N, N + 1, ...), one per bank
+// group, so that an empty slot can read the bank group its slot wants.
+constexpr int kResZeroRows = 16;
 
-// Order the edges inside each piece (slot j of lane l) so that, for every
-// slot and every aligned group of 16 lanes, the rows read fall in as many
-// distinct bank groups as possible (a bipartite matching of lanes to bank
-// groups per slot).  col[k] is the row read by compressed edge k; rows >= N
-// do not occur.  Fills out->slot_edge ([ranks][D][kResLanes]: compressed edge
-// index, or -1 for an empty slot, which reads the all-zero row N).  Without
-// this call a piece's edges keep their compressed order.
+// Order the edges inside each piece (slot j of lane l) for the rule above:
+// per wave and slot, the permutation of bank groups over the 16 lane classes
+// (lane mod 16) that the most lanes can follow (an assignment problem,
+// solved exactly: an edge left in that bank group counts more than an empty
+// slot), then each lane takes an edge in its class's bank group, else an
+// empty slot (the zero row of that bank group), else an edge of its most
+// frequent remaining bank group (a miss, counted in out->order_misses).
+// col[k] is the row read by compressed edge k.  Fills out->slot_edge.
 void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out);
 
 // Bank-conflict cost of a slot table: over all slots and 16-lane groups, the

@@ -1,8 +1,9 @@
 // CPU driver for the resident planner: reads "N ranks max_lens order" and the
 // N + 1 row pointers from stdin, then (order = 1) the row read by each
-// compressed edge; prints "none", or "D ranks max_pieces cost cost_ordered"
+// compressed edge; prints "none", or "D ranks max_pieces cost cost_ordered misses"
 // (bank-conflict costs of the slot table in compressed order and after
-// ordering; 0 when not ordered) followed by rank_rows, owner_pbeg, piece_row,
+// ordering, and the ordering's slots off their wave's permutation; 0 when
+// not ordered) followed by rank_rows, owner_pbeg, piece_row,
 // piece_kbeg, piece_cnt and slot_edge (one array per line).
 #include <cstdio>
 #include <vector>
@@ -38,7 +39,8 @@ int main() {
     ckhip::order_resident_slots(col.data(), N, &plan);
     c1 = ckhip::resident_conflict_cost(col.data(), N, plan);
   }
-  std::printf("%d %d %d %lld %lld\n", plan.D, plan.ranks, plan.max_pieces, c0, c1);
+  std::printf("%d %d %d %lld %lld %lld\n", plan.D, plan.ranks, plan.max_pieces, c0, c1,
+              (long long)plan.order_misses);
   put(plan.rank_rows);
   put(plan.owner_pbeg);
   put(plan.piece_row);

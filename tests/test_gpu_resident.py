@@ -22,7 +22,7 @@ def _need_gpu():
 
 
 def test_path_selection():
-    """Graphs of up to 9200 nodes take the resident kernels at every batch
+    """Graphs of up to 9184 nodes take the resident kernels at every batch
     width (beyond 32 columns each XCD computes several column groups in
     turn), larger graphs the per-microstep kernels; CK_RESIDENT=0 at creation
     turns the resident kernels off."""

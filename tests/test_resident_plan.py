@@ -48,9 +48,9 @@ def plan(driver, ptr, ranks, lens, col=None):
     lines = out.strip("\n").split("\n")
     if lines[0] == "none":
         return None
-    D, r, max_pieces, c0, c1 = map(int, lines[0].split())
+    D, r, max_pieces, c0, c1, misses = map(int, lines[0].split())
     arr = [np.array(ln.split(), dtype=np.int64) for ln in lines[1:7]]
-    return dict(D=D, ranks=r, max_pieces=max_pieces, cost=c0, cost_ordered=c1,
+    return dict(D=D, ranks=r, max_pieces=max_pieces, cost=c0, cost_ordered=c1, misses=misses,
                 rank_rows=arr[0], owner_pbeg=arr[1].reshape(r, LANES + 1),
                 piece_row=arr[2].reshape(r, LANES), piece_kbeg=arr[3].reshape(r, LANES),
                 piece_cnt=arr[4].reshape(r, LANES), slot_edge=arr[5].reshape(r, D, LANES))
@@ -90,8 +90,9 @@ def replay(driver, major, N, ranks=32, lens=5, minor=None):
         for l in range(LANES):
             got_e = np.sort(se[:, l][se[:, l] >= 0])
             np.testing.assert_array_equal(got_e, np.arange(kb[l], kb[l] + cnt[l]), "slot table of a lane")
-        valp = np.concatenate([val, [0]])  # index -1 (an empty slot) reads 0
-        part_slots = valp[se].sum(axis=0)
+        # an empty slot is -1 - z and reads zero row N + z (z < 16)
+        assert (se >= -16).all()
+        part_slots = np.where(se >= 0, val[np.maximum(se, 0)] if E else 0, 0).sum(axis=0)
         np.testing.assert_array_equal(part_slots, part)
         for l in np.nonzero(cnt)[0]:
             cover[kb[l]:kb[l] + cnt[l]] += 1
@@ -127,16 +128,19 @@ def replay(driver, major, N, ranks=32, lens=5, minor=None):
     return p
 
 
-def test_flygpt_slot_order_cuts_bank_conflicts(driver):
-    """FlyGPT shape, both orientations: ordering the slots against LDS bank
-    conflicts keeps every piece intact (the replay) and cuts the conflict cost
-    (sum over slots and 16-lane groups of the most distinct rows sharing a
-    bank group) to at most 70 % of the compressed order's (the lower bound,
-    each group's most frequent bank group, is about 63 % here)."""
+def test_flygpt_slot_order(driver):
+    """FlyGPT shape, both orientations: ordering the slots keeps every piece
+    intact (the replay), leaves at most 24 % (forward) / 28 % (backward) of
+    the slots of waves that hold pieces off their wave's shared bank-group
+    permutation (about 22 % / 26 % here), and still cuts the conflict cost
+    within each 16-lane group (sum over slots and groups of the most distinct
+    rows sharing a bank group) to at most 80 % of the compressed order's."""
     w = synthetic.make("flygpt", synthetic.DEFAULT_SEEDS["flygpt"])
-    for major, minor, lens in ((w.dst, w.src, 5), (w.src, w.dst, 4)):
+    for major, minor, lens, most in ((w.dst, w.src, 5, 0.24), (w.src, w.dst, 4, 0.28)):
         p = replay(driver, major, w.num_nodes, lens=lens, minor=minor)
-        assert p["cost_ordered"] <= 0.70 * p["cost"], (p["cost"], p["cost_ordered"])
+        live_waves = int((p["piece_cnt"].reshape(32, 16, 64).max(axis=2) > 0).sum())
+        assert p["misses"] <= most * live_waves * 64 * p["D"], p["misses"]
+        assert p["cost_ordered"] <= 0.80 * p["cost"], (p["cost"], p["cost_ordered"])
 
 
 @pytest.mark.parametrize("name", ["tiny", "flygpt", "edge_cases"])
