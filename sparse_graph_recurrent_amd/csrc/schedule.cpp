@@ -286,11 +286,6 @@ int64_t resident_conflict_cost(const int32_t* col, int64_t N, const ResidentPlan
   return cost;
 }
 
-namespace {
-
-// Minimum-cost perfect assignment of rows to columns of an n x n integer cost
-// matrix (the Hungarian method with row and column potentials, shortest
-// augmenting paths).  Writes col_of_row[0..n).
 void assign_min_cost(const int* cost, int n, int* col_of_row) {
   constexpr int kInf = 1 << 29;
   std::vector<int> pu(n + 1, 0), pv(n + 1, 0), row_of(n + 1, 0), way(n + 1, 0), minv(n + 1);
@@ -334,8 +329,6 @@ void assign_min_cost(const int* cost, int n, int* col_of_row) {
   }
   for (int j = 1; j <= n; ++j) col_of_row[row_of[j] - 1] = j - 1;
 }
-
-}  // namespace
 
 void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out) {
   ResidentPlan& p = *out;

@@ -124,6 +124,12 @@ constexpr int kResBankGroups = 16;
 // group, so that an empty slot can read the bank group its slot wants.
 constexpr int kResZeroRows = 16;
 
+// Minimum-cost perfect assignment of the rows of an n x n integer cost
+// matrix (row-major, entries below 2^28) to distinct columns: the Hungarian
+// method with row and column potentials and shortest augmenting paths,
+// O(n^3).  Writes col_of_row[0..n).
+void assign_min_cost(const int* cost, int n, int* col_of_row);
+
 // Order the edges inside each piece (slot j of lane l) for the rule above:
 // per wave and slot, the permutation of bank groups over the 16 lane classes
 // (lane mod 16) that the most lanes can follow (an assignment problem,
