@@ -36,6 +36,21 @@ def test_path_selection():
     assert sgr.recurrence_path(make_graph(big), 32) == "per_microstep"
 
 
+def test_largest_resident_graph():
+    """At the node limit, 9,184 nodes, a workgroup's LDS holds the state plane
+    with its 16 zero rows and the partial sums in all but a few hundred of the
+    CU's 160 KiB: the resident kernels still match the oracle there, and one
+    node more takes the per-microstep kernels."""
+    rng = np.random.default_rng(9184)
+    w = synthetic.random_graph(rng, 9184, 120_000, 64, B=8, T=2, M=2, v_scale=0.2)
+    g = make_graph(w)
+    assert sgr.recurrence_path(g, 8) == "resident"
+    log("parity: largest resident graph, N=9184 E=120000 B=8")
+    compare_all(run_gpu(w, graph=g), run_oracle(w))
+    w2 = synthetic.random_graph(np.random.default_rng(9185), 9185, 1000, 4, B=1, T=1, M=1)
+    assert sgr.recurrence_path(make_graph(w2), 8) == "per_microstep"
+
+
 def test_failed_wait_poisons_every_output():
     """With every wait of the resident kernels forced to give up at once
     (CK_RESIDENT_SPIN_LIMIT=-1 at creation; the kernels still run to their
