@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
   const int rank = res_join(p.c, xcc, &s_rank);
   if (rank < 0) return;
   const int N = p.c.N, B = p.c.B;
-  float4* plane = sm;             // [N + 1]
+  float4* plane = sm;             // [N + kResZeroRows]
   float4* part = sm + (N + kResZeroRows);  // [kResLanes]
   const int r0 = p.c.rank_rows[rank], r1 = p.c.rank_rows[rank + 1];
   Piece<D> pc;
