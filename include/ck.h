@@ -28,8 +28,13 @@
  *   - Sizes: num_nodes and num_edges must be below 2^31, and num_nodes times
  *     the padded batch width (B rounded up to a multiple of 4) must be below
  *     2^30 (one state plane under 4 GiB); otherwise CK_ERR_TOO_LARGE.
- *   - A graph handle is immutable after creation and may be used from several
- *     streams at once provided each call has its own `saved` and `workspace`.
+ *   - A graph handle is immutable after creation.  On the per-microstep path
+ *     (ck_recurrence_path) it may be used from several streams at once
+ *     provided each call has its own `saved` and `workspace`.  An XCD-resident
+ *     call occupies every compute unit and its workgroups wait for one
+ *     another: issue resident calls on one stream, with no other device work
+ *     running beside them (a call that cannot finish its waits sets its
+ *     outputs to NaN and ck_recurrence_status reports CK_ERR_WAIT).
  *   - Calls that share a `saved` or `workspace` buffer must be ordered on one
  *     stream (or otherwise synchronised) by the caller.
  */
@@ -57,7 +62,8 @@ typedef enum {
   CK_ERR_WORKSPACE = 6,   /* workspace_bytes below what ck_recurrence_sizes reports */
   CK_ERR_NOMEM = 7,       /* device or host allocation failed */
   CK_ERR_HIP = 8,         /* a HIP runtime call failed; see ck_last_error() */
-  CK_ERR_BAD_HANDLE = 9   /* NULL or destroyed graph handle */
+  CK_ERR_BAD_HANDLE = 9,  /* NULL or destroyed graph handle */
+  CK_ERR_WAIT = 10        /* a wait inside an XCD-resident kernel gave up (ck_recurrence_status) */
 } ck_status;
 
 /*
@@ -112,7 +118,8 @@ ck_status ck_graph_export(ck_graph_t g, int32_t* row_ptr, int32_t* col_idx, int3
  *                    2 * T * M * N * Bp * 4 bytes with Bp = B rounded up to a
  *                    multiple of 4 (= 2*T*M*N*B*4 when B % 4 == 0); on the
  *                    XCD-resident path N is first rounded up to a multiple of
- *                    8.  Its layout is internal.
+ *                    8 and 256 bytes follow (the forward's status word).  Its
+ *                    layout is internal.
  *   workspace_bytes  scratch needed by either forward or backward.
  */
 ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int64_t microsteps,
@@ -133,7 +140,9 @@ ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int64_t micros
  * launch holds one workgroup on every compute unit and its workgroups wait
  * for one another, so it must not run concurrently with other kernels on the
  * device.  A wait that does not end within about a second raises an internal
- * error flag; the call's outputs (or all five gradients) are then NaN.  (The
+ * error flag; the call's outputs (or all five gradients) are then NaN, a
+ * backward given the saved arena of such a forward also writes NaN, and
+ * ck_recurrence_status reports CK_ERR_WAIT.  (The
  * poll limit of those waits is read from CK_RESIDENT_SPIN_LIMIT at graph
  * creation, default 1048576; a negative value fails every wait at once and
  * exists to test that failure path.)
@@ -181,6 +190,19 @@ ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_values, const f
                                  float* grad_edge_values, float* grad_leak, float* grad_bias,
                                  float* grad_drives, float* grad_state0, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Status of the last forward or backward call that used `workspace` (same
+ * graph, T, B and microsteps).  Synchronises `stream`, then returns CK_OK, or
+ * CK_ERR_WAIT if that call ran the XCD-resident kernels and one of their
+ * bounded waits gave up -- typically because other device work ran beside
+ * the call -- or if the call was a backward whose saved arena came from such
+ * a failed forward.  In both cases every output of that call was set to NaN.
+ * The per-microstep kernels have no waits: CK_OK.
+ */
+ck_status ck_recurrence_status(ck_graph_t g, int64_t T, int64_t B, int64_t microsteps,
+                               const void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /*
  * Measurement hook (changes no result).  While enabled (process-wide),

@@ -33,12 +33,12 @@ LIB_PATH = os.path.join(_PKG, "libck_hip.so")
 STATUS_NAMES = {
     0: "CK_OK", 1: "CK_ERR_NULL_ARG", 2: "CK_ERR_BAD_SIZE", 3: "CK_ERR_INDEX_RANGE",
     4: "CK_ERR_DUP_INPUT", 5: "CK_ERR_TOO_LARGE", 6: "CK_ERR_WORKSPACE", 7: "CK_ERR_NOMEM",
-    8: "CK_ERR_HIP", 9: "CK_ERR_BAD_HANDLE",
+    8: "CK_ERR_HIP", 9: "CK_ERR_BAD_HANDLE", 10: "CK_ERR_WAIT",
 }
 
 EXPORTED = ("ck_graph_create", "ck_graph_destroy", "ck_graph_sizes", "ck_graph_export",
             "ck_recurrence_sizes", "ck_recurrence_path", "ck_recurrence_forward",
-            "ck_recurrence_backward",
+            "ck_recurrence_backward", "ck_recurrence_status",
             "ck_profile_enable", "ck_profile_collect", "ck_status_string", "ck_last_error")
 
 
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
         L.ck_recurrence_path.argtypes = [p, i64, ctypes.POINTER(ctypes.c_int)]
         L.ck_recurrence_forward.argtypes = [p, p, p, p, p, p, i64, i64, i64, p, p, p, sz, p]
         L.ck_recurrence_backward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p, p, p, p, p, p, sz, p]
+        L.ck_recurrence_status.argtypes = [p, i64, i64, i64, p, sz, p]
         L.ck_profile_enable.argtypes = [ctypes.c_int]
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(i64)
@@ -246,6 +247,16 @@ def recurrence_backward(graph: SparseGraph, edge_values, leak, state0, microstep
     return grads
 
 
+def recurrence_status(graph: SparseGraph, T: int, B: int, microsteps: int, workspace,
+                      stream=None):
+    """Synchronise the stream and raise CkError (CK_ERR_WAIT) if the last call
+    that used `workspace` failed inside the XCD-resident kernels (its outputs
+    were then set to NaN); see ``ck_recurrence_status``."""
+    _check(lib().ck_recurrence_status(graph.handle, int(T), int(B), int(microsteps),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+
+
 def profile_enable(enable: bool = True):
     """Turn the library's per-launch HIP-event timing on or off (process-wide)."""
     _check(lib().ck_profile_enable(1 if enable else 0))
@@ -264,29 +275,45 @@ def profile_collect() -> dict:
 
 class _SparseRecurrence(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, edge_values, leak, bias, drives, state0, graph, microsteps):
+    def forward(ctx, edge_values, leak, bias, drives, state0, graph, microsteps, check):
         ev, lk, bs = edge_values.contiguous(), leak.contiguous(), bias.contiguous()
         dr, st = drives.contiguous(), state0.contiguous()
-        out, saved, _ = recurrence_forward(graph, ev, lk, bs, dr, st, microsteps)
-        ctx.graph, ctx.microsteps = graph, microsteps
+        out, saved, ws = recurrence_forward(graph, ev, lk, bs, dr, st, microsteps)
+        if check:
+            recurrence_status(graph, dr.shape[0], st.shape[0], microsteps, ws)
+        ctx.graph, ctx.microsteps, ctx.check = graph, microsteps, check
         ctx.save_for_backward(ev, lk, st, saved)
         return out
 
     @staticmethod
     def backward(ctx, grad_out):
         ev, lk, st, saved = ctx.saved_tensors
-        g = recurrence_backward(ctx.graph, ev, lk, st, ctx.microsteps, saved,
-                                grad_out.contiguous().float())
-        return g["g_edge_values"], g["g_leak"], g["g_bias"], g["g_drives"], g["g_state0"], None, None
+        G = grad_out.contiguous().float()
+        T, B = G.shape[0], G.shape[1]
+        sb, wb = recurrence_sizes(ctx.graph, T, B, ctx.microsteps)
+        ws = _byte_buffer(wb, G.device)
+        g = recurrence_backward(ctx.graph, ev, lk, st, ctx.microsteps, saved, G, workspace=ws)
+        if ctx.check:
+            recurrence_status(ctx.graph, T, B, ctx.microsteps, ws)
+        return (g["g_edge_values"], g["g_leak"], g["g_bias"], g["g_drives"], g["g_state0"],
+                None, None, None)
 
 
 def sparse_recurrence(edge_values, leak, bias, drives, state0, graph: SparseGraph,
-                      microsteps: int = 2) -> torch.Tensor:
-    """out [T, B, N]: node states after each input step; differentiable in the
-    five tensor arguments (one autograd node for the whole window)."""
-    return _SparseRecurrence.apply(edge_values, leak, bias, drives, state0, graph, int(microsteps))
+                      microsteps: int = 2, check: bool = True) -> torch.Tensor:
+    """Run the recurrence over the whole window as one autograd node
+    (connectome-kernels README, "Use": argument names and shapes).
+
+    Returns the node states at the end of every input step, shaped
+    [T, B, N]; gradients reach all five tensor arguments.  With check=True
+    (the default) the forward and the backward each synchronise their stream
+    once and raise CkError (CK_ERR_WAIT) if the XCD-resident kernels failed
+    (their outputs are then NaN); check=False skips that synchronisation, e.g.
+    under HIP graph capture."""
+    return _SparseRecurrence.apply(edge_values, leak, bias, drives, state0, graph,
+                                   int(microsteps), bool(check))
 
 
 __all__ = ["SparseGraph", "sparse_recurrence", "recurrence_forward", "recurrence_backward",
-           "recurrence_sizes", "profile_enable", "profile_collect", "CkError", "CkLibraryMissing",
+           "recurrence_sizes", "recurrence_status", "recurrence_path", "profile_enable", "profile_collect", "CkError", "CkLibraryMissing",
            "lib", "LIB_PATH", "EXPORTED"]

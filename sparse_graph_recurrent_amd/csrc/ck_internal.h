@@ -146,6 +146,10 @@ struct ResWs {
 ck_status res_prepare();
 ResWs res_ws_layout(const ck_graph* g, const ResDims& d);
 size_t res_saved_bytes(const ResDims& d);
+// Reads the error flag of the last resident call that used `workspace`
+// (synchronises `stream`).
+ck_status res_status(const ck_graph* g, const ResDims& d, const void* workspace,
+                     hipStream_t stream, unsigned* err);
 ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_values,
                       const float* leak, const float* bias, const float* drives,
                       const float* state0, float* out, void* saved, void* workspace,

@@ -630,6 +630,7 @@ extern "C" const char* ck_status_string(ck_status s) {
     case CK_ERR_NOMEM: return "CK_ERR_NOMEM";
     case CK_ERR_HIP: return "CK_ERR_HIP";
     case CK_ERR_BAD_HANDLE: return "CK_ERR_BAD_HANDLE";
+    case CK_ERR_WAIT: return "CK_ERR_WAIT";
   }
   return "CK_ERR_UNKNOWN";
 }

@@ -877,7 +877,10 @@ ck_status make_dims(const ck_graph* g, int64_t T, int64_t B, int64_t M, Dims* d)
   d->slots_f = g->fwd[d->wide].slots;
   d->slots_b = g->bwd[d->wide].slots;
   d->plane = (size_t)g->N * Bp;
-  d->resident = g->res_ok != 0;
+  // the resident kernels address the [T][n_in][B] drives and the [B][N]
+  // upstream-gradient and initial-state tensors of one step with 32-bit byte
+  // offsets below 2^31 (range-checked buffer accesses)
+  d->resident = g->res_ok != 0 && std::max(g->N, g->n_in) * B * 4 < (1LL << 31);
   d->rd = ResDims{g->N, (g->N + 7) / 8 * 8, B, Bp / 4, g->n_in, T, M, T * M};
   return CK_OK;
 }
@@ -1120,6 +1123,38 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
     }
   }
 #endif
+  return CK_OK;
+}
+
+extern "C" ck_status ck_recurrence_status(ck_graph_t g, int64_t T, int64_t B,
+                                          int64_t microsteps, const void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  ck_status rc = check_graph(g);
+  if (rc != CK_OK) return rc;
+  Dims d;
+  rc = make_dims(g, T, B, microsteps, &d);
+  if (rc != CK_OK) return rc;
+  if (!d.resident) return CK_OK;  // the per-microstep kernels have no waits
+  if (!workspace) {
+    set_error("workspace is NULL");
+    return CK_ERR_NULL_ARG;
+  }
+  const size_t need = res_ws_layout(g, d.rd).total;
+  if (workspace_bytes < need) {
+    set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+    return CK_ERR_WORKSPACE;
+  }
+  unsigned err = 0;
+  rc = res_status(g, d.rd, workspace, stream, &err);
+  if (rc != CK_OK) return rc;
+  if (err != 0u) {
+    set_error("the last resident call on this workspace failed (flag 0x%x: %s%s%s); its outputs "
+              "were set to NaN", err, (err & 1u) ? "unexpected workgroup grouping " : "",
+              (err & 2u) ? "a wait between XCD workgroups gave up " : "",
+              (err & 4u) ? "the saved arena came from a failed forward" : "");
+    return CK_ERR_WAIT;
+  }
   return CK_OK;
 }
 

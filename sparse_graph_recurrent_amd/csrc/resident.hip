@@ -46,6 +46,9 @@ namespace {
 constexpr int kCtlTicket = 0;
 constexpr int kCtlCount = 256;
 constexpr int kCtlErr = 512;
+// bits of the error flag: a workgroup found an unexpected grouping (1), a wait
+// gave up (2), the saved arena came from a forward that failed (4)
+constexpr unsigned kErrForward = 4u;
 constexpr int kCtlWords = 1024;
 constexpr int kCtlStride = 32;
 
@@ -596,11 +599,13 @@ __global__ void res_prologue(const float* __restrict__ values, const int32_t* __
 }
 
 // out[t][b][i] = h^((t+1) M)[b / 4][i][b % 4], or NaN everywhere if the
-// resident kernel raised its error flag.
+// resident kernel raised its error flag.  The flag is also copied into the
+// saved arena's status word, so that a backward given this arena knows.
 __global__ void res_out(const float* __restrict__ hplanes, size_t psz, size_t gsz, int M,
                         int64_t T, int N, int B, int G, const unsigned* __restrict__ ctl,
-                        float* __restrict__ out) {
+                        float* __restrict__ out, unsigned* __restrict__ saved_status) {
   const bool bad = ctl[kCtlErr] != 0u;
+  if (blockIdx.x == 0 && threadIdx.x == 0) saved_status[0] = ctl[kCtlErr];
   const int64_t n = T * G * (int64_t)N;
   for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n;
        k += (int64_t)gridDim.x * blockDim.x) {
@@ -618,14 +623,20 @@ __global__ void res_out(const float* __restrict__ hplanes, size_t psz, size_t gs
 
 // After the resident backward: edge gradients to caller order and the leak /
 // bias gradients, each summed over the column groups in group order; NaN in
-// every gradient if the resident kernel raised its error flag.
+// every gradient if the resident kernel raised its error flag or the forward
+// that wrote the saved arena did (its status word; then kErrForward is added
+// to the error flag, so that the call's status reports it).
 __global__ void res_bwd_finish(const float* __restrict__ gvpart, int G, const int32_t* __restrict__ pperm,
                                int64_t slots, float* __restrict__ gv, const float* __restrict__ glpart,
                                const float* __restrict__ gbpart, int N, float* __restrict__ gleak,
-                               float* __restrict__ gbias, const unsigned* __restrict__ ctl,
+                               float* __restrict__ gbias, unsigned* __restrict__ ctl,
+                               const unsigned* __restrict__ saved_status,
                                float* __restrict__ gdrives, int64_t nd, float* __restrict__ gstate0,
                                int64_t ns) {
-  const bool bad = ctl[kCtlErr] != 0u;
+  const bool fwd_bad = saved_status[0] != 0u;
+  const bool bad = fwd_bad || ctl[kCtlErr] != 0u;
+  if (fwd_bad && blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_fetch_or(&ctl[kCtlErr], kErrForward, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int64_t n = std::max<int64_t>(std::max<int64_t>(slots, N), bad ? std::max(nd, ns) : 0);
   for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n;
        k += (int64_t)gridDim.x * blockDim.x) {
@@ -741,7 +752,25 @@ ResWs res_ws_layout(const ck_graph* g, const ResDims& d) {
   return w;
 }
 
-size_t res_saved_bytes(const ResDims& d) { return 2 * (size_t)d.S * d.G * d.Np * 16; }
+// the h and a planes, then a 256-byte trailer whose first word is the
+// forward's error flag
+size_t res_saved_bytes(const ResDims& d) { return 2 * (size_t)d.S * d.G * d.Np * 16 + 256; }
+
+static unsigned* saved_status(void* saved, const ResDims& d) {
+  return reinterpret_cast<unsigned*>(static_cast<char*>(saved) + 2 * (size_t)d.S * d.G * d.Np * 16);
+}
+
+ck_status res_status(const ck_graph* g, const ResDims& d, const void* workspace,
+                     hipStream_t stream, unsigned* err) {
+  const ResWs ws = res_ws_layout(g, d);
+  const unsigned* ctl =
+      reinterpret_cast<const unsigned*>(static_cast<const char*>(workspace) + ws.ctl);
+  unsigned v = 0;
+  CK_HIP_TRY(hipMemcpyAsync(&v, ctl + kCtlErr, sizeof(unsigned), hipMemcpyDeviceToHost, stream));
+  CK_HIP_TRY(hipStreamSynchronize(stream));
+  *err = v;
+  return CK_OK;
+}
 
 ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_values,
                       const float* leak, const float* bias, const float* drives,
@@ -776,7 +805,8 @@ ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_val
   if (rc != CK_OK) return rc;
   const size_t gsz = (size_t)d.Np * 4, psz = gsz * d.G;
   res_out<<<res_grid(d.T * d.G * d.N), 256, 0, stream>>>(a.hplanes, psz, gsz, (int)d.M, d.T,
-                                                         (int)d.N, (int)d.B, (int)d.G, ctl, out);
+                                                         (int)d.N, (int)d.B, (int)d.G, ctl, out,
+                                                         saved_status(saved, d));
   CK_HIP_TRY(hipGetLastError());
   return CK_OK;
 }
@@ -821,7 +851,8 @@ ck_status res_backward(const ck_graph* g, const ResDims& d, const float* edge_va
   const int64_t nd = d.T * d.n_in * d.B, ns = d.B * d.N;
   res_bwd_finish<<<res_grid(std::max<int64_t>({r.slots, d.N, nd, ns})), 256, 0, stream>>>(
       a.gvpart, (int)d.G, r.pperm, r.slots, grad_edge_values, a.glpart, a.gbpart, (int)d.N,
-      grad_leak, grad_bias, ctl, grad_drives, nd, grad_state0, ns);
+      grad_leak, grad_bias, ctl, saved_status(const_cast<void*>(saved), d), grad_drives, nd,
+      grad_state0, ns);
   CK_HIP_TRY(hipGetLastError());
   return CK_OK;
 }

@@ -54,16 +54,43 @@ def test_largest_resident_graph():
 def test_failed_wait_poisons_every_output():
     """With every wait of the resident kernels forced to give up at once
     (CK_RESIDENT_SPIN_LIMIT=-1 at creation; the kernels still run to their
-    end), forward and backward report the failure as NaN in every output.
-    A graph created afterwards computes correctly again."""
+    end), forward and backward report the failure as NaN in every output and
+    as CK_ERR_WAIT from ck_recurrence_status; a backward on a healthy graph
+    given the saved arena of the failed forward does too (the arena carries
+    the forward's status), and so does the autograd wrapper.  A graph created
+    afterwards computes correctly again."""
     w = synthetic.make("tiny")
     log("resident failure path: all waits give up")
     g = make_graph(w, "resident", env={"CK_RESIDENT_SPIN_LIMIT": "-1"})
     bad = run_gpu(w, graph=g)
     for k, v in bad.items():
         assert np.isnan(v).all(), k
+    ev, lk, bs, dr, st, G = (to_dev(x) for x in (w.edge_values, w.leak, w.bias, w.drives,
+                                                  w.state0, w.grad_out))
+    out, saved, ws = sgr.recurrence_forward(g, ev, lk, bs, dr, st, w.microsteps)
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.recurrence_status(g, w.T, w.B, w.microsteps, ws)
+    assert ei.value.status == 10
+    log("resident failure path: healthy backward given the failed forward's arena")
+    good = make_graph(w, "resident")
+    ws2 = torch.empty(sgr.recurrence_sizes(good, w.T, w.B, w.microsteps)[1], dtype=torch.uint8,
+                      device="cuda")
+    grads = sgr.recurrence_backward(good, ev, lk, st, w.microsteps, saved, G, workspace=ws2)
+    for k, v in grads.items():
+        assert torch.isnan(v).all().item(), k
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.recurrence_status(good, w.T, w.B, w.microsteps, ws2)
+    assert ei.value.status == 10
+    log("resident failure path: autograd wrapper raises")
+    ins = [x.clone().requires_grad_() for x in (ev, lk, bs, dr, st)]
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.sparse_recurrence(*ins, g, microsteps=w.microsteps)
+    assert ei.value.status == 10
     log("resident failure path: healthy graph afterwards")
-    compare_all(run_gpu(w, path="resident"), run_oracle(w))
+    res = run_gpu(w, graph=good)
+    compare_all(res, run_oracle(w))
+    out, saved, ws = sgr.recurrence_forward(good, ev, lk, bs, dr, st, w.microsteps)
+    sgr.recurrence_status(good, w.T, w.B, w.microsteps, ws)
 
 
 def test_paths_agree_on_flygpt():

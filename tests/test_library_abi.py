@@ -71,6 +71,7 @@ def test_null_handles_are_rejected(L):
     assert L.ck_graph_sizes(None, ctypes.byref(n), None, None) == 9
     s = ctypes.c_size_t()
     assert L.ck_recurrence_sizes(None, 1, 1, 1, ctypes.byref(s), ctypes.byref(s)) == 9
+    assert L.ck_recurrence_status(None, 1, 1, 1, None, 0, None) == 9
     assert L.ck_recurrence_forward(None, *([None] * 5), 1, 1, 1, None, None, None, 0, None) == 9
     assert L.ck_recurrence_backward(None, None, None, None, 1, 1, 1, *([None] * 8), 0, None) == 9
     assert "handle" in L.ck_last_error().decode()
