@@ -170,6 +170,30 @@ ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_values, const fl
                                 hipStream_t stream);
 
 /*
+ * Allocation-free variant of ck_recurrence_forward, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): same arguments without the workspace, same
+ * kernels and the same results.  Its scratch (the packed edge slots, the
+ * initial state in the kernels' layout and, on the XCD-resident path, the
+ * control block) lives in a fixed device array of 64 MiB that the library
+ * holds on every GPU it runs on until the process ends; its device address is
+ * resolved when a graph is created on that GPU.  The call allocates nothing,
+ * records no profiling events and returns CK_ERR_TOO_LARGE when the forward
+ * needs more than 64 MiB of scratch (e.g. graphs of tens of millions of
+ * edges).  Every call on one GPU shares that array and leaves its contents
+ * behind (each call rewrites what it reads): calls that overlap in time on
+ * one GPU race and must be ordered by the caller (one stream).  `saved` is
+ * the caller's, as for ck_recurrence_forward, and serves ck_recurrence_backward
+ * unchanged.  ck_recurrence_status does not apply (the control block is not
+ * in a caller workspace).
+ */
+ck_status ck_recurrence_forward_noalloc(ck_graph_t g, const float* edge_values,
+                                        const float* leak, const float* bias, const float* drives,
+                                        const float* state0, int64_t T, int64_t B,
+                                        int64_t microsteps, float* out, void* saved,
+                                        hipStream_t stream);
+
+/*
  * Gradient of L given grad_out = dL/dout, for all five inputs
  * (connectome-kernels README, introduction and "Design notes": elementwise
  * gradients with per-node leak/bias reductions, the transposed sparse product

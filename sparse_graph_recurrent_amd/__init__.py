@@ -38,7 +38,7 @@ STATUS_NAMES = {
 
 EXPORTED = ("ck_graph_create", "ck_graph_destroy", "ck_graph_sizes", "ck_graph_export",
             "ck_recurrence_sizes", "ck_recurrence_path", "ck_recurrence_forward",
-            "ck_recurrence_backward", "ck_recurrence_status",
+            "ck_recurrence_backward", "ck_recurrence_status", "ck_recurrence_forward_noalloc",
             "ck_profile_enable", "ck_profile_collect", "ck_status_string", "ck_last_error")
 
 
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.ck_recurrence_forward.argtypes = [p, p, p, p, p, p, i64, i64, i64, p, p, p, sz, p]
         L.ck_recurrence_backward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p, p, p, p, p, p, sz, p]
         L.ck_recurrence_status.argtypes = [p, i64, i64, i64, p, sz, p]
+        L.ck_recurrence_forward_noalloc.argtypes = [p, p, p, p, p, p, i64, i64, i64, p, p, p]
         L.ck_profile_enable.argtypes = [ctypes.c_int]
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(i64)
@@ -220,6 +221,28 @@ def recurrence_forward(graph: SparseGraph, edge_values, leak, bias, drives, stat
     return out, saved, workspace
 
 
+def recurrence_forward_noalloc(graph: SparseGraph, edge_values, leak, bias, drives, state0,
+                               microsteps: int, out, saved, stream=None):
+    """Run ``ck_recurrence_forward_noalloc`` into the caller's `out` and `saved`
+    (no workspace: the library's fixed device scratch is used)."""
+    N, E, n_in = graph.num_nodes, graph.num_edges, graph.num_inputs
+    B = state0.shape[0]
+    T = drives.shape[0]
+    _dev(edge_values, "edge_values", torch.float32, (E,))
+    _dev(leak, "leak", torch.float32, (N,))
+    _dev(bias, "bias", torch.float32, (N,))
+    _dev(drives, "drives", torch.float32, (T, n_in, B))
+    _dev(state0, "state0", torch.float32, (B, N))
+    _dev(out, "out", torch.float32, (T, B, N))
+    sb, _ = recurrence_sizes(graph, T, B, microsteps)
+    if saved.numel() * saved.element_size() < sb:
+        raise ValueError("saved buffer too small")
+    _check(lib().ck_recurrence_forward_noalloc(
+        graph.handle, _ptr(edge_values), _ptr(leak), _ptr(bias), _ptr(drives), _ptr(state0),
+        T, B, int(microsteps), _ptr(out), _ptr(saved), _stream(stream)))
+    return out, saved
+
+
 def recurrence_backward(graph: SparseGraph, edge_values, leak, state0, microsteps: int, saved,
                         grad_out, workspace=None, grads=None, stream=None) -> dict:
     """Run ``ck_recurrence_backward``; returns the five gradients (overwritten)."""
@@ -315,5 +338,6 @@ def sparse_recurrence(edge_values, leak, bias, drives, state0, graph: SparseGrap
 
 
 __all__ = ["SparseGraph", "sparse_recurrence", "recurrence_forward", "recurrence_backward",
+           "recurrence_forward_noalloc",
            "recurrence_sizes", "recurrence_status", "recurrence_path", "profile_enable", "profile_collect", "CkError", "CkLibraryMissing",
            "lib", "LIB_PATH", "EXPORTED"]

@@ -150,10 +150,17 @@ size_t res_saved_bytes(const ResDims& d);
 // (synchronises `stream`).
 ck_status res_status(const ck_graph* g, const ResDims& d, const void* workspace,
                      hipStream_t stream, unsigned* err);
+// Leading bytes of the workspace a resident forward uses.
+size_t res_forward_ws_bytes(const ck_graph* g, const ResDims& d);
+// profile: record the measurement hook's events around the main launch.
 ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_values,
                       const float* leak, const float* bias, const float* drives,
                       const float* state0, float* out, void* saved, void* workspace,
-                      hipStream_t stream);
+                      hipStream_t stream, bool profile);
+// Resolves, once per device, the device address of the allocation-free
+// forward's fixed scratch array (called at graph creation, with `device`
+// current).
+ck_status scratch_prepare(int device);
 ck_status res_backward(const ck_graph* g, const ResDims& d, const float* edge_values,
                        const float* leak, const float* state0, const void* saved,
                        const float* grad_out, float* grad_edge_values, float* grad_leak,

@@ -568,6 +568,10 @@ extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int
   }
   (void)hipFree(flags);
   (void)hipFree(seen);
+  flags = nullptr;
+  seen = nullptr;
+  rc = scratch_prepare(g->device);
+  if (rc != CK_OK) return fail(rc);
   g->magic = kGraphMagic;
   *out = g;
   return CK_OK;

@@ -24,6 +24,7 @@
 // No floating-point atomics: every output element has exactly one owner, and
 // every sum is taken in a fixed order, so results are bitwise reproducible.
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "ck_internal.h"
@@ -32,6 +33,37 @@
 namespace ckhip {
 
 Profile g_profile;
+
+// Device scratch of the allocation-free forward (ck_recurrence_forward_noalloc):
+// one fixed array per GPU the library runs on, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in); it uses the device address resolved by scratch_prepare.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kScratchDevices] = {};
+
+ck_status scratch_prepare(int device) {
+  if (device < 0 || device >= kScratchDevices) {
+    set_error("device %d is beyond the %d devices the scratch table covers", device,
+              kScratchDevices);
+    return CK_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* ptr = nullptr;
+    CK_HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    g_scratch_ptr[device] = ptr;
+  }
+  return CK_OK;
+}
+
+static void* scratch_ptr(int device) {
+  if (device < 0 || device >= kScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 namespace {
 
@@ -919,37 +951,42 @@ extern "C" ck_status ck_recurrence_path(ck_graph_t g, int64_t B, int* resident) 
   return CK_OK;
 }
 
-extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_values,
-                                           const float* leak, const float* bias,
-                                           const float* drives, const float* state0, int64_t T,
-                                           int64_t B, int64_t microsteps, float* out, void* saved,
-                                           void* workspace, size_t workspace_bytes,
-                                           hipStream_t stream) {
-  clear_error();
+namespace {
+
+// Bytes of the workspace a forward call touches (its leading part: the
+// backward's regions follow it).
+size_t forward_ws_bytes(const ck_graph* g, const Dims& d) {
+  return d.resident ? res_forward_ws_bytes(g, d.rd) : ws_layout(d).gh;
+}
+
+// Argument checks shared by both forward entry points.
+ck_status forward_checks(ck_graph_t g, const float* edge_values, const float* leak,
+                         const float* bias, const float* drives, const float* state0, int64_t T,
+                         int64_t B, int64_t microsteps, float* out, void* saved, Dims* d) {
   ck_status rc = check_graph(g);
   if (rc != CK_OK) return rc;
-  Dims d;
-  rc = make_dims(g, T, B, microsteps, &d);
+  rc = make_dims(g, T, B, microsteps, d);
   if (rc != CK_OK) return rc;
-  if ((d.E > 0 && !edge_values) || !leak || !bias || (d.n_in > 0 && !drives) || !state0 ||
-      !out || !saved || !workspace) {
+  if ((d->E > 0 && !edge_values) || !leak || !bias || (d->n_in > 0 && !drives) || !state0 ||
+      !out || !saved) {
     set_error("NULL pointer for a non-empty tensor in forward");
     return CK_ERR_NULL_ARG;
   }
-  if (d.resident) {
-    const size_t need = res_ws_layout(g, d.rd).total;
-    if (workspace_bytes < need) {
-      set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, need);
-      return CK_ERR_WORKSPACE;
-    }
+  return CK_OK;
+}
+
+// The forward once its arguments are checked; `workspace` holds at least
+// forward_ws_bytes(g, d) bytes.
+// `profile`: false keeps the measurement hook's events out of the call.
+ck_status forward_body(const ck_graph* g, const Dims& d, const float* edge_values,
+                       const float* leak, const float* bias, const float* drives,
+                       const float* state0, float* out, void* saved, void* workspace,
+                       hipStream_t stream, bool profile) {
+  if (d.resident)
     return res_forward(g, d.rd, edge_values, leak, bias, drives, state0, out, saved, workspace,
-                       stream);
-  }
+                       stream, profile);
+  ck_status rc = CK_OK;
   const WsLayout ws = ws_layout(d);
-  if (workspace_bytes < ws.total) {
-    set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, ws.total);
-    return CK_ERR_WORKSPACE;
-  }
   char* wsb = static_cast<char*>(workspace);
   int2* pedge = reinterpret_cast<int2*>(wsb + ws.v);
   float* h0 = reinterpret_cast<float*>(wsb + ws.h0);
@@ -979,8 +1016,11 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
     a.h_prev = s == 1 ? h0 : hplanes + (size_t)(s - 2) * d.plane;
     a.h_next = hplanes + (size_t)(s - 1) * d.plane;
     a.a_next = aplanes + (size_t)(s - 1) * d.plane;
-    rc = timed_launch(g_profile.fwd, stream,
-                      [&] { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); });
+    if (profile)
+      rc = timed_launch(g_profile.fwd, stream,
+                        [&] { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); });
+    else
+      hipLaunchKernelGGL(kern, grid, block, 0, stream, a);
     if (rc != CK_OK) return rc;
   }
   // out[t] = the state after the last microstep of step t, in [B][N]
@@ -1004,6 +1044,57 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
   }
 #endif
   return CK_OK;
+}
+
+}  // namespace
+
+extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_values,
+                                           const float* leak, const float* bias,
+                                           const float* drives, const float* state0, int64_t T,
+                                           int64_t B, int64_t microsteps, float* out, void* saved,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  clear_error();
+  Dims d;
+  ck_status rc = forward_checks(g, edge_values, leak, bias, drives, state0, T, B, microsteps, out,
+                                saved, &d);
+  if (rc != CK_OK) return rc;
+  if (!workspace) {
+    set_error("NULL workspace in forward");
+    return CK_ERR_NULL_ARG;
+  }
+  const size_t need = d.resident ? res_ws_layout(g, d.rd).total : ws_layout(d).total;
+  if (workspace_bytes < need) {
+    set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+    return CK_ERR_WORKSPACE;
+  }
+  return forward_body(g, d, edge_values, leak, bias, drives, state0, out, saved, workspace,
+                      stream, true);
+}
+
+extern "C" ck_status ck_recurrence_forward_noalloc(ck_graph_t g, const float* edge_values,
+                                                   const float* leak, const float* bias,
+                                                   const float* drives, const float* state0,
+                                                   int64_t T, int64_t B, int64_t microsteps,
+                                                   float* out, void* saved, hipStream_t stream) {
+  clear_error();
+  Dims d;
+  ck_status rc = forward_checks(g, edge_values, leak, bias, drives, state0, T, B, microsteps, out,
+                                saved, &d);
+  if (rc != CK_OK) return rc;
+  const size_t need = forward_ws_bytes(g, d);
+  if (need > kScratchBytes) {
+    set_error("this forward needs %zu bytes of scratch, above the %zu of the allocation-free "
+              "entry point; use ck_recurrence_forward with a workspace", need, kScratchBytes);
+    return CK_ERR_TOO_LARGE;
+  }
+  void* ws = scratch_ptr(g->device);
+  if (ws == nullptr) {
+    set_error("device scratch of device %d was not resolved at graph creation", g->device);
+    return CK_ERR_HIP;
+  }
+  return forward_body(g, d, edge_values, leak, bias, drives, state0, out, saved, ws, stream,
+                      false);
 }
 
 extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_values,

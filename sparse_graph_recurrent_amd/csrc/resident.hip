@@ -772,10 +772,14 @@ ck_status res_status(const ck_graph* g, const ResDims& d, const void* workspace,
   return CK_OK;
 }
 
+size_t res_forward_ws_bytes(const ck_graph* g, const ResDims& d) {
+  return res_ws_layout(g, d).ga;  // the edge slots, the initial state and the control block
+}
+
 ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_values,
                       const float* leak, const float* bias, const float* drives,
                       const float* state0, float* out, void* saved, void* workspace,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool profile) {
   const Resident& r = g->res_fwd;
   const ResFwdFn kern = fwd_kernel(r.D, d.G > kResXcds);
   if (!kern) {
@@ -799,9 +803,13 @@ ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_val
   a.aplanes = a.hplanes + (size_t)d.S * d.G * d.Np * 4;
   const size_t lds = res_lds_bytes((int)d.N);
   const unsigned wgs = (unsigned)(r.ranks * kResXcds);
-  ck_status rc = timed_launch(g_profile.fwd, stream, [&] {
+  ck_status rc = CK_OK;
+  if (profile)
+    rc = timed_launch(g_profile.fwd, stream, [&] {
+      hipLaunchKernelGGL(kern, dim3(wgs), dim3(kResLanes), lds, stream, a);
+    });
+  else
     hipLaunchKernelGGL(kern, dim3(wgs), dim3(kResLanes), lds, stream, a);
-  });
   if (rc != CK_OK) return rc;
   const size_t gsz = (size_t)d.Np * 4, psz = gsz * d.G;
   res_out<<<res_grid(d.T * d.G * d.N), 256, 0, stream>>>(a.hplanes, psz, gsz, (int)d.M, d.T,
