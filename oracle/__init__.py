@@ -20,8 +20,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# "f64" is the oracle; "f32" is the same code evaluated in fp32, used only to
-# measure the fp32 rounding floor of the method (never as a parity reference).
+# "f64" is the oracle; "f32" is the same code evaluated in fp32: the rounding
+# floor of the method, to which the GPU parity tests hold a tensor only where
+# some element misses the stated bound against the fp64 oracle.
 _LIB_PATHS = {"f64": os.path.join(_HERE, "libckoracle.so"),
               "f32": os.path.join(_HERE, "libckoracle_f32.so")}
 _libs = {}
@@ -101,16 +102,42 @@ def build_graph(src, dst, num_nodes: int, input_nodes):
     return res
 
 
+def edge_order(src, dst, order):
+    """Permutation p of the caller's edges giving the order in which the
+    oracle visits them: None = caller order, "sorted" = by (dst, src, caller
+    index) (the order of the rows of the CSR by destination), an int = a
+    random order drawn with that seed."""
+    src, dst = _i64(src), _i64(dst)
+    if order is None:
+        return np.arange(src.size)
+    if order == "sorted":
+        return np.lexsort((np.arange(src.size), src, dst))
+    return np.random.default_rng(int(order)).permutation(src.size)
+
+
 def run(src, dst, num_nodes: int, input_nodes, edge_values, leak, bias, drives, state0,
-        microsteps: int, grad_out=None, nthreads: int = 0, precision: str = "f64"):
+        microsteps: int, grad_out=None, nthreads: int = 0, precision: str = "f64", order=None):
     """Forward (and, with grad_out, the gradient of sum(out * grad_out)).
 
     Shapes: edge_values[E] (caller order), leak[N], bias[N], drives[T, n_in, B],
     state0[B, N], grad_out[T, B, N].  Returns a dict with ``out`` [T, B, N] and,
     with grad_out, ``g_edge_values``, ``g_leak``, ``g_bias``, ``g_drives``,
     ``g_state0`` -- all float64.  precision="f32" evaluates the same steps in
-    fp32 (rounding-floor measurement only).
+    fp32 (rounding-floor measurement only).  order (see edge_order) sets the
+    order in which each node's incoming and outgoing edge terms are summed;
+    the result is the same definition whatever the order (only its rounding
+    differs), and g_edge_values is returned in the caller's edge order.
     """
+    if order is not None:
+        p = edge_order(src, dst, order)
+        res = run(_i64(src)[p], _i64(dst)[p], num_nodes, input_nodes, _f64(edge_values)[p], leak,
+                  bias, drives, state0, microsteps, grad_out=grad_out, nthreads=nthreads,
+                  precision=precision)
+        if "g_edge_values" in res:
+            gv = np.empty_like(res["g_edge_values"])
+            gv[p] = res["g_edge_values"]
+            res["g_edge_values"] = gv
+        return res
     src, dst, inp = _i64(src), _i64(dst), _i64(input_nodes)
     v, lk, bs = _f64(edge_values), _f64(leak), _f64(bias)
     st0 = _f64(state0)

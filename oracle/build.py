@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "ck_oracle.c")
 LIB = os.path.join(HERE, "libckoracle.so")
-# Same source evaluated in fp32: measures the method's fp32 rounding floor only.
+# Same source evaluated in fp32: the method's fp32 rounding floor.
 LIB_F32 = os.path.join(HERE, "libckoracle_f32.so")
 
 

@@ -41,8 +41,9 @@
  *
  * The working precision is `real`: double by default.  Built with
  * -DOR_REAL=float the same code evaluates every step in fp32 (inputs rounded
- * to fp32); that build only measures the fp32 rounding floor of the method
- * and is never a parity reference.
+ * to fp32); that build measures the fp32 rounding floor of the method (the
+ * parity tests fall back to it only where an element misses the stated bound
+ * against the fp64 build).
  *
  * The graph builder orders edges by (dst, src, caller index) for the CSR and by
  * (src, dst, caller index) for the transposed CSR; both are total orders, so the

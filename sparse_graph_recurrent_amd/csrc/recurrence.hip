@@ -97,6 +97,22 @@ __device__ __forceinline__ float4 sum_slots(float4 v, int sub) {
   }
 }
 
+// sum_slots for the forward's fp64 row sums (same order)
+template <int L>
+__device__ __forceinline__ double4 sum_slots_d(double4 v, int sub) {
+  constexpr int P = Geom<L>::P;
+  if constexpr (is_pow2(L)) {
+#pragma unroll
+    for (int m = L; m < 64; m <<= 1) v = add4d(v, shfl_xor4d(v, m));
+    return v;
+  } else {
+    double4 s = shfl4d(v, sub);
+#pragma unroll
+    for (int p = 1; p < P; ++p) s = add4d(s, shfl4d(v, p * L + sub));
+    return s;
+  }
+}
+
 // Sum over the L lanes of this lane's slot; every lane of the slot gets it.
 template <int L>
 __device__ __forceinline__ float sum_in_slot(float x, int slot) {
@@ -232,6 +248,9 @@ __device__ __forceinline__ T ld_row(const T* base, size_t i, size_t n, int site)
 __device__ __forceinline__ float pick4(float4 v, int q) {
   return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
 }
+__device__ __forceinline__ double pick4d(double4 v, int q) {
+  return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+}
 
 // Lane roles shared by both kernels.  In the gather loop lane = slot * L + sub
 // holds columns [col, col + 4) of one gathered row.  In the per-row epilogue
@@ -361,13 +380,14 @@ __device__ __forceinline__ FwdEpi fwd_epi_load(const FwdArgs& p, const Lanes& ln
   return e;
 }
 
-// a = (W h)[row] + drive + bias;  h' = (1 - leak) h + leak tanh(a)
+// a = (W h)[row] + drive + bias (summed in fp64, rounded once);
+// h' = (1 - leak) h + leak tanh(a)
 __device__ __forceinline__ void fwd_epilogue(const FwdArgs& p, const Lanes& ln, int row,
-                                             float4 acc, const FwdEpi& e) {
+                                             double4 acc, const FwdEpi& e) {
   if (!ln.eok) return;
   const int c = ln.ecol;
   const size_t off = (size_t)row * p.Bp + c;
-  const float a = pick4(acc, ln.slot) + e.dv + e.bi;
+  const float a = (float)(pick4d(acc, ln.slot) + (double)e.dv + (double)e.bi);
   const float h = (1.0f - e.lam) * e.hp + e.lam * tanhf(a);
   [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
   CK_AT(p.h_next, off, NBp, 5) = h;
@@ -381,7 +401,7 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
   constexpr int W = waves_for_lanes(L);
   constexpr int P = Gm::P, I = Gm::I, EB = Gm::EB;
   constexpr int NSUB = Pp::NSUB, NU = Pp::NU, TU = Pp::TU, TE = Pp::TE;
-  __shared__ float4 red[2 * W][16];  // partial sums of pieces, by piece number
+  __shared__ double4 red[2 * W][16];  // partial sums of pieces, by piece number
   const Lanes ln = lanes<L>(p.Bp);
   const int wave = __builtin_amdgcn_readfirstlane(ln.wave);
   const uint32_t colb = (uint32_t)(ln.ok ? ln.col : 0) * 4u;  // this lane's columns, in bytes
@@ -394,7 +414,7 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
   const int first_info = p.KB > 0 ? CK_AT(bt, 0, p.KB, 10).w : 0;
   const uint32_t pbytes = (uint32_t)NBp * 4u;
   const __amdgpu_buffer_rsrc_t hsrc = plane_rsrc(p.h_prev, pbytes);
-  float4 acc = f4(0.f);
+  double4 acc = d4(0.0);  // the row sums are formed in fp64
   FwdEpi eo{0.f, 0.f, 0.f, 0.f};
   for (int g0 = 0; g0 < p.KB; g0 += kFwdGroup) {
     const int4 ent = (ln.lane < kFwdGroup && g0 + ln.lane < p.KB)
@@ -437,24 +457,24 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
                 wj[j] = lane_or(__shfl(wb[q], e & 63), e, 0.f);
               }
 #pragma unroll
-              for (int j = 0; j < I; ++j) acc = fma4(wj[j], hv[uc % TU][j], acc);
+              for (int j = 0; j < I; ++j) acc = fma4d(wj[j], hv[uc % TU][j], acc);
             } else {
 #pragma unroll
               for (int j = 0; j < I; ++j) {
                 if (sb * EB + j * P >= d.z) break;  // past the batch's last edge (uniform)
                 const int e = sb * EB + j * P + ln.slot;
-                acc = fma4(lane_or(__shfl(wb[q], e & 63), e, 0.f), hv[uc % TU][j], acc);
+                acc = fma4d(lane_or(__shfl(wb[q], e & 63), e, 0.f), hv[uc % TU][j], acc);
               }
             }
           }
           if (sb == NSUB - 1 && (d.w & kInfoLastBit)) {  // the row (or piece) is complete
-            acc = sum_slots<L>(acc, ln.sub);
+            acc = sum_slots_d<L>(acc, ln.sub);
             if (d.w & kInfoPieceBit) {
               if (ln.slot == 0) red[piece_slot<W>(d.w)][ln.sub] = acc;
             } else {
               fwd_epilogue(p, ln, d.x, acc, eo);
             }
-            acc = f4(0.f);
+            acc = d4(0.0);
           }
         }
       }
@@ -492,8 +512,8 @@ __global__ __launch_bounds__(waves_for_lanes(L) * 64) void fwd_step(FwdArgs p) {
     if (combine) {
       int q0, q1;
       piece_range<W>(d0.w, q0, q1);
-      float4 a = red[q0][ln.sub];
-      for (int q = q0 + 1; q <= q1; ++q) a = add4(a, red[q][ln.sub]);
+      double4 a = red[q0][ln.sub];
+      for (int q = q0 + 1; q <= q1; ++q) a = add4d(a, red[q][ln.sub]);
       fwd_epilogue(p, ln, d0.x, a, ce);
     }
   }

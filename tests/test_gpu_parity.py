@@ -1,11 +1,13 @@
 """GPU parity of the HIP path (through the C ABI) against the CPU oracle.
 
 Graph arrays must be bit-exact; outputs must match to rtol 1e-5 (atol 1e-6)
-and all five gradients to rtol 1e-4 (atol 1e-6), per element.  Large
-workloads run the GPU at the full launch configuration and compare against the
-oracle on sampled batch columns: columns are independent through the whole
-recurrence, so with grad_out zero outside those columns the column-sampled
-oracle gives every gradient exactly.
+and all five gradients to rtol 1e-4 (atol 1e-6), per element, or be no less
+accurate than the oracle's fp32 evaluation in the kernels' summation order
+where that evaluation itself misses the bound (gpu_helpers.compare).  Large
+workloads run the GPU at the full launch configuration; their outputs are
+compared on every batch column and their gradients on sampled columns:
+columns are independent through the whole recurrence, so with grad_out zero
+outside those columns the column-sampled oracle gives every gradient exactly.
 """
 import numpy as np
 import pytest
@@ -14,8 +16,8 @@ import torch
 import oracle
 import sparse_graph_recurrent_amd as sgr
 import synthetic
-from gpu_helpers import (PATHS, column_masked_grad, compare_all, compare_floor,
-                         compare_with_fp32_floor, log, make_graph, run_gpu, run_oracle, to_dev)
+from gpu_helpers import (PATHS, check_outputs_all_columns, check_parity, column_masked_grad, log,
+                         make_graph, run_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,7 +107,7 @@ def test_graph_validation_agrees_with_oracle(case):
 def test_tiny_workload_full_parity(path):
     w = synthetic.make("tiny")
     log(f"parity: tiny workload, {path} kernels")
-    compare_all(run_gpu(w, path=path), run_oracle(w))
+    check_parity(run_gpu(w, path=path), w)
 
 
 def _mixed_graph(seed, B, T, M, N=400, E=9000, n_in=9):
@@ -130,7 +132,7 @@ def _mixed_graph(seed, B, T, M, N=400, E=9000, n_in=9):
 def test_batch_widths_parity(B, path):
     w = _mixed_graph(100 + B, B=B, T=3, M=2)
     log(f"parity: mixed graph B={B} E={w.num_edges}, {path} kernels")
-    compare_all(run_gpu(w, path=path), run_oracle(w))
+    check_parity(run_gpu(w, path=path), w)
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -138,7 +140,7 @@ def test_batch_widths_parity(B, path):
 def test_microsteps_parity(M, path):
     w = _mixed_graph(200 + M, B=32, T=4, M=M)
     log(f"parity: mixed graph M={M}, {path} kernels")
-    compare_all(run_gpu(w, path=path), run_oracle(w))
+    check_parity(run_gpu(w, path=path), w)
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -154,7 +156,7 @@ def test_degenerate_graphs_parity(kind, path):
     w.grad_out = rng2.standard_normal((T, B, w.num_nodes)).astype(np.float32)
     w.microsteps = M
     log(f"parity: degenerate {kind} N={w.num_nodes} E={w.num_edges}, {path} kernels")
-    compare_all(run_gpu(w, path=path), run_oracle(w))
+    check_parity(run_gpu(w, path=path), w)
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -166,7 +168,7 @@ def test_saturated_preactivations(path):
     w.bias = np.where(i % 3 == 0, np.where(i % 2 == 0, 6.0, -6.0), w.bias).astype(np.float32)
     w.drives = (6.0 * w.drives).astype(np.float32)
     log(f"parity: saturated pre-activations, {path} kernels")
-    compare_all(run_gpu(w, path=path), run_oracle(w))
+    check_parity(run_gpu(w, path=path), w)
 
 
 # ---------------------------------------------------------------- parity, full size
@@ -174,54 +176,64 @@ def test_saturated_preactivations(path):
 def test_flygpt_full_parity(path):
     w = synthetic.make("flygpt")
     log(f"parity: flygpt launch shape, all columns, {path} kernels")
-    gpu, ref = run_gpu(w, path=path), run_oracle(w)
-    compare_all(gpu, ref)
-    compare_floor(gpu, ref, run_oracle(w, precision="f32"))
+    check_parity(run_gpu(w, path=path), w)
 
 
 @pytest.mark.parametrize("path", PATHS)
 def test_edge_cases_full_parity(path):
     w = synthetic.make("edge_cases")
     log(f"parity: edge-cases workload, all columns, {path} kernels")
-    gpu, ref = run_gpu(w, path=path), run_oracle(w)
-    compare_all(gpu, ref)
-    compare_floor(gpu, ref, run_oracle(w, precision="f32"))
+    check_parity(run_gpu(w, path=path), w)
 
 
-def test_mid_scale_sampled_parity():
+def test_mid_scale_parity():
+    """Outputs on all 64 batch columns; gradients on columns 0, 37, 63."""
     w = synthetic.make("mid_scale")
     cols = [0, 37, 63]
     G = column_masked_grad(w, cols)
-    log("parity: mid-scale workload, columns 0, 37, 63")
-    gpu, ref = run_gpu(w, G=G), run_oracle(w, G=G, cols=cols)
-    compare_all(gpu, ref, cols=cols)
-    compare_floor(gpu, ref, run_oracle(w, G=G, cols=cols, precision="f32"), cols=cols)
+    log("parity: mid-scale workload, gradients on columns 0, 37, 63")
+    gpu = run_gpu(w, G=G)
+    check_parity(gpu, w, G=G, cols=cols)
+    log("parity: mid-scale workload, outputs on all columns")
+    check_outputs_all_columns(gpu["out"], w)
+
+
+def _connectome_parity(w, label):
+    cols = [0, 31]
+    G = column_masked_grad(w, cols)
+    log(f"parity: {label}, gradients on columns 0, 31")
+    gpu = run_gpu(w, G=G)
+    check_parity(gpu, w, G=G, cols=cols)
+    log(f"parity: {label}, outputs on all columns")
+    check_outputs_all_columns(gpu["out"], w)
 
 
 @pytest.mark.slow
-def test_connectome_sampled_parity():
-    """Whole-connectome shape (hubs of in-degree up to 20,000, 80 % positive
-    weights, 64 microsteps).  This workload is ill-conditioned for fp32: two
-    fp32 evaluations of the definition that differ only in summation order
-    (the C oracle's fp32 build in caller edge order, and a float32 sparse
-    product evaluation in sorted order) differ several-fold in error, and the
-    first already misses the per-element bound on a few elements.  So each
-    GPU element must be within the bound or within twice the worst error of
-    those fp32 evaluations on its tensor."""
+def test_connectome_parity():
+    """Whole-connectome shape: hubs of in-degree up to 20,000, 80 % positive
+    weights, 64 microsteps.  fp32 evaluations of the definition miss the
+    stated bound on thousands of gradient entries here, by amounts that vary
+    several-fold with summation order; the per-microstep forward forms its
+    row sums in fp64 and stays within the bound on all but a few dozen."""
     w = synthetic.make("connectome")
-    cols = [0, 31]
-    G = column_masked_grad(w, cols)
-    log("parity: whole-connectome workload, columns 0, 31")
-    gpu, ref = run_gpu(w, G=G), run_oracle(w, G=G, cols=cols)
-    refs32 = [run_oracle(w, G=G, cols=cols, precision="f32"),
-              run_oracle(w, G=G, cols=cols, precision="f32sorted")]
-    compare_with_fp32_floor(gpu, ref, refs32, cols=cols)
+    _connectome_parity(w, "whole-connectome workload")
     log("graph build: connectome")
     g = make_graph(w)
     got = {k: v.cpu().numpy() for k, v in g.export().items()}
     ref = oracle.build_graph(w.src, w.dst, w.num_nodes, w.input_nodes)
     for k in GRAPH_KEYS:
         np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+
+
+@pytest.mark.slow
+def test_connectome_zero_mean_weights_parity():
+    """Control: the same graph with zero-mean signed weights (signs +-1 with
+    equal probability), where the summation order moves fp32 results little."""
+    w = synthetic.make("connectome")
+    rng = np.random.default_rng(55)
+    w.edge_values = (np.abs(w.edge_values) * np.where(rng.random(w.num_edges) < 0.5, 1, -1)
+                     ).astype(np.float32)
+    _connectome_parity(w, "whole-connectome graph, zero-mean weights")
 
 
 # ---------------------------------------------------------------- properties

@@ -10,7 +10,7 @@ import torch
 
 import sparse_graph_recurrent_amd as sgr
 import synthetic
-from gpu_helpers import compare_all, log, make_graph, run_gpu, run_oracle, to_dev
+from gpu_helpers import check_parity, log, make_graph, run_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,7 @@ def test_largest_resident_graph():
     g = make_graph(w)
     assert sgr.recurrence_path(g, 8) == "resident"
     log("parity: largest resident graph, N=9184 E=120000 B=8")
-    compare_all(run_gpu(w, graph=g), run_oracle(w))
+    check_parity(run_gpu(w, graph=g), w)
     w2 = synthetic.random_graph(np.random.default_rng(9185), 9185, 1000, 4, B=1, T=1, M=1)
     assert sgr.recurrence_path(make_graph(w2), 8) == "per_microstep"
 
@@ -87,8 +87,7 @@ def test_failed_wait_poisons_every_output():
         sgr.sparse_recurrence(*ins, g, microsteps=w.microsteps)
     assert ei.value.status == 10
     log("resident failure path: healthy graph afterwards")
-    res = run_gpu(w, graph=good)
-    compare_all(res, run_oracle(w))
+    check_parity(run_gpu(w, graph=good), w)
     out, saved, ws = sgr.recurrence_forward(good, ev, lk, bs, dr, st, w.microsteps)
     sgr.recurrence_status(good, w.T, w.B, w.microsteps, ws)
 
