@@ -12,12 +12,20 @@ torch.cuda.CUDAGraph on the stream the library launches on) and the graph is
 replayed; --no-graph launches them directly.
 Prints one JSON line with:
   value        edge-visits/s = S * E * B / t_step  (S = T * M microsteps)
-  ms_per_step  mean time of one step over the K timed steps (HIP events)
+  ms_per_step  mean time of one step over the K timed steps (HIP events);
+               ms_per_step_median / ms_per_step_min from an event pair
+               around each of the K steps
   roofline     the dominant kernel's algorithmic bytes per launch / its mean
                launch duration (HIP events around each launch, recorded by the
                library's measurement hook on the stream the kernels run on)
                against the MI355X HBM peak of 8 TB/s
-  cpu_baseline the CPU oracle's rate on the same workload (host cores)
+               (achieved); with the committed rocprofv3 counter summary of
+               that kernel, also its measured HBM bytes per launch (traffic)
+               over the same duration (measured_GBps, measured_frac)
+  cpu_baseline the CPU oracle's rate on the same workload (host cores), the
+               host CPU model, and one-thread oracle times of whole
+               forward+backward windows of the tiny, edge-case and FlyGPT
+               workloads
 """
 from __future__ import annotations
 
@@ -80,6 +88,33 @@ def measured_traffic(kernel: str):
     return int(v) if v else None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def one_thread_times():
+    """Seconds of one whole forward+backward window of the oracle on one
+    thread, for the tiny, edge-case and FlyGPT workloads."""
+    import oracle
+    import synthetic
+    res = {}
+    for name in ("tiny", "edge_cases", "flygpt"):
+        w = synthetic.make(name)
+        t0 = time.perf_counter()
+        oracle.run(w.src, w.dst, w.num_nodes, w.input_nodes, w.edge_values, w.leak, w.bias,
+                   w.drives, w.state0, w.microsteps, grad_out=w.grad_out, nthreads=1)
+        res[name] = round(time.perf_counter() - t0, 4)
+    return res
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The CPU oracle (fp64, OpenMP over all host cores) on the same workload:
     whole forward+backward windows, repeated until at least budget_s seconds
@@ -98,7 +133,9 @@ def cpu_baseline(w, budget_s: float = 12.0):
     return {"value": S * E * B / per, "unit": "edge-visits/s", "cores": threads, "kind": "oracle",
             "sample": f"{runs} full forward+backward window(s) of the benchmark workload "
                       f"(all {B} batch columns, {S} microsteps), fp64, {per:.2f} s each, "
-                      f"{total:.1f} s in all"}
+                      f"{total:.1f} s in all",
+            "ms_per_step": 1e3 * per, "cpu_model": cpu_model(),
+            "one_thread_s_per_window": one_thread_times()}
 
 
 def main():
@@ -113,6 +150,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's plain device copy of MIB MiB three times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--read-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch's sum over MIB MiB three times (a kernel that "
+                         "reads MIB MiB and writes almost nothing)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the recurrence would "
@@ -135,6 +175,14 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n * 4}), flush=True)
+        return
+    if args.read_calibration:
+        n = args.read_calibration * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            t = x.sum()
+        torch.cuda.synchronize()
+        print(json.dumps({"read_calibration_bytes": n * 4, "sum": float(t)}), flush=True)
         return
     w = synthetic.make(args.workload)
     N, E, n_in, B, T, M = w.num_nodes, w.num_edges, w.n_in, w.B, w.T, w.microsteps
@@ -180,6 +228,16 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    # the same K steps again, each between its own event pair
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
+    for k in range(args.steps):
+        run()
+        marks[k + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
 
     # per-launch kernel durations: HIP events around every per-microstep launch
     sgr.profile_collect()
@@ -203,9 +261,12 @@ def main():
     for kname, per_b, us in ((("res_fwd" if resident else "fwd_step"), fwd_b * S / fwd_n, fwd_us),
                              (("res_bwd" if resident else "bwd_step"), bwd_b * S / bwd_n, bwd_us)):
         a = per_b / (us * 1e-6) / 1e9
+        tr = measured_traffic(kname)
+        m = None if tr is None else tr / (us * 1e-6) / 1e9
         per_kernel[kname] = {"achieved": a, "frac": a / HBM_PEAK_GBS, "launch_us": us,
-                             "algorithmic_bytes_per_launch": per_b,
-                             "traffic": measured_traffic(kname)}
+                             "algorithmic_bytes_per_launch": per_b, "traffic": tr,
+                             "measured_GBps": m,
+                             "measured_frac": None if m is None else m / HBM_PEAK_GBS}
     # the dominant kernel is the one with the larger share of the step's time
     name = list(per_kernel)[1] if prof["bwd_ms"] >= prof["fwd_ms"] else list(per_kernel)[0]
     achieved = per_kernel[name]["achieved"]
@@ -218,6 +279,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": ms_median,
+        "ms_per_step_min": per_step[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -232,7 +295,9 @@ def main():
                     "fwd_launches_per_step": fwd_n, "bwd_launches_per_step": bwd_n},
         "roofline": {"bound": "hbm", "kernel": name, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": per_kernel[name]["traffic"]},
+                     "traffic": per_kernel[name]["traffic"],
+                     "measured_GBps": per_kernel[name]["measured_GBps"],
+                     "measured_frac": per_kernel[name]["measured_frac"]},
         "roofline_by_kernel": per_kernel,
     }
     if not args.no_cpu:
