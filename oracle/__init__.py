@@ -165,3 +165,59 @@ def run(src, dst, num_nodes: int, input_nodes, edge_values, leak, bias, drives, 
     if rc:
         raise OracleError(rc)
     return res
+
+
+# ---------------------------------------------------------------- LIF forward
+# Integer fixed-point leaky integrate-and-fire forward (lif_oracle.c; soup-connectome
+# page, "Runtime contract").
+_LIF_PATH = os.path.join(_HERE, "libliforacle.so")
+_lif = None
+LIF_OVERFLOW = 11   # the run was rejected: a potential left the int32 range
+LIF_BAD_VALUE = 12  # a delay, decay shift or refractory count out of range
+
+
+def _load_lif():
+    global _lif
+    if _lif is None:
+        if not os.path.exists(_LIF_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIF_PATH)
+        i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        lib.lifor_run.restype = ctypes.c_int
+        lib.lifor_run.argtypes = [i64, i64, p, p, p, p, i32, i32, i32, i32, p, p, i64, p, p, p]
+        _lif = lib
+    return _lif
+
+
+class LifOverflow(OracleError):
+    def __init__(self, step: int):
+        super().__init__(LIF_OVERFLOW)
+        self.step = step
+
+
+def lif_run(src, dst, num_nodes: int, impulses, delays, v0, T: int, threshold: int, reset: int,
+            refractory_steps: int, decay_shifts):
+    """Spikes uint8 [T, N] and potentials int32 [T, N] (after each step) of the
+    fixed-point LIF forward.  impulses int16 [E] and delays int32 [E] are in the
+    caller's edge order.  Raises LifOverflow (with .step) if a potential leaves
+    the int32 range, OracleError for invalid arguments."""
+    src, dst = _i64(src), _i64(dst)
+    w = np.ascontiguousarray(np.asarray(impulses, np.int16))
+    d = np.ascontiguousarray(np.asarray(delays, np.int32))
+    v = np.ascontiguousarray(np.asarray(v0, np.int32))
+    sh = np.ascontiguousarray(np.asarray(list(decay_shifts), np.int32))
+    N, E = int(num_nodes), src.size
+    if dst.size != E or w.size != E or d.size != E or v.size != N:
+        raise OracleError(2)
+    spikes = np.zeros((int(T), N), np.uint8)
+    pot = np.zeros((int(T), N), np.int32)
+    step = ctypes.c_int64(-1)
+    rc = _load_lif().lifor_run(N, E, _ptr(src), _ptr(dst), _ptr(w), _ptr(d), int(threshold),
+                               int(reset), int(refractory_steps), sh.size, _ptr(sh) if sh.size else None,
+                               _ptr(v), int(T), _ptr(spikes), _ptr(pot), ctypes.byref(step))
+    if rc == LIF_OVERFLOW:
+        raise LifOverflow(step.value)
+    if rc:
+        raise OracleError(rc)
+    return spikes, pot

@@ -14,6 +14,11 @@ LIB = os.path.join(HERE, "libckoracle.so")
 LIB_F32 = os.path.join(HERE, "libckoracle_f32.so")
 
 
+# Integer fixed-point LIF forward (a second workload on the same graph class).
+LIF_SRC = os.path.join(HERE, "lif_oracle.c")
+LIF_LIB = os.path.join(HERE, "libliforacle.so")
+
+
 def build(verbose: bool = False) -> str:
     for out, extra in ((LIB, []), (LIB_F32, ["-DOR_REAL=float"])):
         cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
@@ -21,6 +26,10 @@ def build(verbose: bool = False) -> str:
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-o", LIF_LIB, LIF_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
     return LIB
 
 
