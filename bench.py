@@ -138,6 +138,79 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "one_thread_s_per_window": one_thread_times()}
 
 
+# The active LIF run: threshold 40, reset 0, decay_shifts [2], refractory 2
+# (the soup-connectome page's standard parameters with a threshold low enough
+# for sustained activity), initial potentials uniform in [0, 60), delays 1..4.
+LIF_RUN = dict(T=16, threshold=40, reset=0, refractory_steps=2, decay_shifts=[2])
+
+
+def lif_bench(args, torch, sgr, synthetic, np):
+    """One LIF forward = T timesteps on the synthetic whole-connectome graph.
+    value = edge-visits/s = E * T / t_forward; roofline of the per-step gather
+    kernel against HBM: algorithmic bytes per launch = 12 E (8-byte edge record
+    and 4-byte destination per CSR position) + 9 N (the spike row read, the
+    64-bit accumulators written) over its mean launch time."""
+    w = synthetic.make_lif("connectome", max_delay=4, v0_range=(0, 60))
+    N, E, T = w.num_nodes, w.src.size, LIF_RUN["T"]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    g = sgr.SparseGraph(dev(w.src), dev(w.dst), N, dev(w.input_nodes))
+    imp, dl, v0 = dev(w.impulses), dev(w.delays), dev(w.v0)
+    kw = {k: v for k, v in LIF_RUN.items() if k != "T"}
+    ws = torch.empty(1, dtype=torch.uint8, device="cuda")
+    import ctypes
+    wb = ctypes.c_size_t()
+    sgr.lib().ck_lif_workspace_size(g.handle, ctypes.byref(wb))
+    ws = torch.empty(wb.value, dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        sgr.lif_forward(g, imp, dl, v0, T, workspace=ws, **kw)
+    times = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        spikes, _ = sgr.lif_forward(g, imp, dl, v0, T, workspace=ws, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sum(times) / len(times)
+    sgr.profile_collect_lif()
+    sgr.profile_enable(True)
+    for _ in range(args.steps):
+        sgr.lif_forward(g, imp, dl, v0, T, workspace=ws, **kw)
+    sgr.profile_enable(False)
+    prof = sgr.profile_collect_lif()
+    gather_us = 1e3 * prof["gather_ms"] / max(1, prof["gather_launches"])
+    update_us = 1e3 * prof["update_ms"] / max(1, prof["update_launches"])
+    per_launch = 12 * E + 9 * N
+    ach = per_launch / (gather_us * 1e-6) / 1e9
+    res = {"metric": "LIF forward: ms per timestep & edge-visits/s, synthetic whole-connectome "
+                     "graph N=211,577 E=24,678,466; HBM GB/s",
+           "value": E * T / (ms * 1e-3), "unit": "edge-visits/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_forward": ms,
+           "ms_per_timestep": ms / T, "ms_per_forward_min": min(times),
+           "higher_is_better": True, "vs_baseline": None, "dtype": "int32/int16",
+           "data": "synthetic",
+           "config": {"workload": f"lif connectome: N={N} E={E} T={T} delays 1..4 "
+                                  f"threshold {kw['threshold']} decay_shifts {kw['decay_shifts']} "
+                                  f"refractory {kw['refractory_steps']}",
+                      "spikes_per_step": spikes.sum(dim=1).tolist()},
+           "kernels": {"gather_launch_us": gather_us, "update_launch_us": update_us,
+                       "gather_launches_per_forward": prof["gather_launches"] // args.steps,
+                       "update_launches_per_forward": prof["update_launches"] // args.steps},
+           "roofline": {"bound": "hbm", "kernel": "lif_gather", "achieved": ach,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                        "traffic": None}}
+    if not args.no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.lif_run(w.src, w.dst, N, w.impulses, w.delays, w.v0, T, **kw)
+        sec = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": E * T / sec, "unit": "edge-visits/s", "cores": 1,
+                               "kind": "oracle", "cpu_model": cpu_model(),
+                               "sample": f"one whole {T}-step run of the same workload, "
+                                         f"{sec:.2f} s (the LIF oracle is single-threaded)"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +220,9 @@ def main():
                     help="launch every step directly instead of replaying a captured HIP graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--workload", default="flygpt")
+    ap.add_argument("--lif", action="store_true",
+                    help="measure the fixed-point LIF forward instead (active run on the "
+                         "synthetic whole-connectome graph, 16 timesteps)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's plain device copy of MIB MiB three times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -183,6 +259,9 @@ def main():
             t = x.sum()
         torch.cuda.synchronize()
         print(json.dumps({"read_calibration_bytes": n * 4, "sum": float(t)}), flush=True)
+        return
+    if args.lif:
+        print(json.dumps(lif_bench(args, torch, sgr, synthetic, np)), flush=True)
         return
     w = synthetic.make(args.workload)
     N, E, n_in, B, T, M = w.num_nodes, w.num_edges, w.n_in, w.B, w.T, w.microsteps

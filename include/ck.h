@@ -63,7 +63,9 @@ typedef enum {
   CK_ERR_NOMEM = 7,       /* device or host allocation failed */
   CK_ERR_HIP = 8,         /* a HIP runtime call failed; see ck_last_error() */
   CK_ERR_BAD_HANDLE = 9,  /* NULL or destroyed graph handle */
-  CK_ERR_WAIT = 10        /* a wait inside an XCD-resident kernel gave up (ck_recurrence_status) */
+  CK_ERR_WAIT = 10,       /* a wait inside an XCD-resident kernel gave up (ck_recurrence_status) */
+  CK_ERR_OVERFLOW = 11,   /* LIF forward: a membrane potential left the int32 range (run rejected) */
+  CK_ERR_BAD_VALUE = 12   /* a parameter or per-edge value outside its documented range */
 } ck_status;
 
 /*
@@ -241,6 +243,65 @@ ck_status ck_recurrence_status(ck_graph_t g, int64_t T, int64_t B, int64_t micro
 ck_status ck_profile_enable(int enable);
 ck_status ck_profile_collect(double* fwd_ms, int64_t* fwd_launches, double* bwd_ms,
                              int64_t* bwd_launches);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Fixed-point leaky integrate-and-fire (LIF) forward on the same graph handle
+ * (soup-connectome page, "Runtime contract": signed int32 membrane potentials,
+ * signed int16 synaptic impulses, positive integer timestep delays, checked
+ * arithmetic with rejected overflow, the arithmetic-shift leak
+ * V := V - (V >> k); "Full-scale benchmark": a run's threshold, reset,
+ * decay_shifts and refractory_steps).  The page fixes the representation,
+ * not the update order; this library's reading, per timestep t and neuron i:
+ *
+ *   I = sum of w[e] over the in-edges e of i whose source spiked at t - d[e]
+ *       (exact; impulses whose arrival step precedes the run never exist)
+ *   if i is refractory (count r > 0): r -= 1, I is dropped, V is kept, no spike
+ *   else: for each k in decay_shifts in order, V := V - (V >> k) (arithmetic
+ *         shift, i.e. floor(V / 2^k)); V := V + I, rejected if it leaves the
+ *         int32 range; if V >= threshold: spike, V := reset, r := refractory_steps
+ *   spikes[t][i] = spike, potentials[t][i] = V.
+ *
+ * The graph's input_nodes play no part.  Integer arithmetic is exact: results
+ * are bit-identical to any correct evaluation.
+ */
+typedef struct {
+  int32_t threshold;         /* a neuron spikes when its potential reaches this value */
+  int32_t reset;             /* potential right after a spike */
+  int32_t refractory_steps;  /* >= 0: steps after a spike that ignore input */
+  int32_t num_decay_shifts;  /* 0..8 */
+  int32_t decay_shifts[8];   /* each in [0, 31]: V := V - (V >> k), applied in order */
+} ck_lif_params;
+
+/* Workspace bytes of ck_lif_forward on this graph. */
+ck_status ck_lif_workspace_size(ck_graph_t g, size_t* workspace_bytes);
+
+/*
+ *   impulses     int16[E]  device, caller edge order: the impulse edge e delivers
+ *   delays       int32[E]  device, caller edge order: steps until it arrives, 1..32767
+ *   params       host pointer (above)
+ *   v0           int32[N]  device: potentials before step 0 (refractory counts start at 0)
+ *   T            timesteps, 1..2^31-1
+ *   spikes       uint8[T][N]  device, written (1 = spike)
+ *   potentials   int32[T][N]  device, written: V after each step
+ *   overflow_step  host, may be NULL: -1, or the first step whose update left
+ *                  the int32 range
+ * Runs on `stream` and synchronises it before returning (the overflow and
+ * value checks are read back).  Returns CK_ERR_OVERFLOW if a potential left
+ * the int32 range (outputs of that step and later are unspecified),
+ * CK_ERR_BAD_VALUE for a delay outside [1, 32767], more than 8 decay shifts, a
+ * shift outside [0, 31] or a negative refractory count.
+ */
+ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const int32_t* delays,
+                         const ck_lif_params* params, const int32_t* v0, int64_t T,
+                         uint8_t* spikes, int32_t* potentials, int64_t* overflow_step,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Measurement hook for the LIF forward: summed durations (ms) and counts of
+ * the per-step gather and update launches recorded while ck_profile_enable
+ * is on, since the last collect (synchronises the device). */
+ck_status ck_profile_collect_lif(double* gather_ms, int64_t* gather_launches, double* update_ms,
+                                 int64_t* update_launches);
 
 /* Static name of a status value. */
 const char* ck_status_string(ck_status s);

@@ -33,17 +33,26 @@ LIB_PATH = os.path.join(_PKG, "libck_hip.so")
 STATUS_NAMES = {
     0: "CK_OK", 1: "CK_ERR_NULL_ARG", 2: "CK_ERR_BAD_SIZE", 3: "CK_ERR_INDEX_RANGE",
     4: "CK_ERR_DUP_INPUT", 5: "CK_ERR_TOO_LARGE", 6: "CK_ERR_WORKSPACE", 7: "CK_ERR_NOMEM",
-    8: "CK_ERR_HIP", 9: "CK_ERR_BAD_HANDLE", 10: "CK_ERR_WAIT",
+    8: "CK_ERR_HIP", 9: "CK_ERR_BAD_HANDLE", 10: "CK_ERR_WAIT", 11: "CK_ERR_OVERFLOW",
+    12: "CK_ERR_BAD_VALUE",
 }
 
 EXPORTED = ("ck_graph_create", "ck_graph_destroy", "ck_graph_sizes", "ck_graph_export",
             "ck_recurrence_sizes", "ck_recurrence_path", "ck_recurrence_forward",
             "ck_recurrence_backward", "ck_recurrence_status", "ck_recurrence_forward_noalloc",
+            "ck_lif_workspace_size", "ck_lif_forward", "ck_profile_collect_lif",
             "ck_profile_enable", "ck_profile_collect", "ck_status_string", "ck_last_error")
 
 
 class CkLibraryMissing(RuntimeError):
     pass
+
+
+class LifParams(ctypes.Structure):
+    """ck_lif_params of include/ck.h."""
+    _fields_ = [("threshold", ctypes.c_int32), ("reset", ctypes.c_int32),
+                ("refractory_steps", ctypes.c_int32), ("num_decay_shifts", ctypes.c_int32),
+                ("decay_shifts", ctypes.c_int32 * 8)]
 
 
 class CkError(RuntimeError):
@@ -75,10 +84,14 @@ def lib() -> ctypes.CDLL:
         L.ck_recurrence_backward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p, p, p, p, p, p, sz, p]
         L.ck_recurrence_status.argtypes = [p, i64, i64, i64, p, sz, p]
         L.ck_recurrence_forward_noalloc.argtypes = [p, p, p, p, p, p, i64, i64, i64, p, p, p]
+        L.ck_lif_workspace_size.argtypes = [p, ctypes.POINTER(sz)]
+        L.ck_lif_forward.argtypes = [p, p, p, ctypes.POINTER(LifParams), p, i64, p, p,
+                                     ctypes.POINTER(i64), p, sz, p]
         L.ck_profile_enable.argtypes = [ctypes.c_int]
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(i64)
         L.ck_profile_collect.argtypes = [dp, ip, dp, ip]
+        L.ck_profile_collect_lif.argtypes = [dp, ip, dp, ip]
         for name in EXPORTED[:-2]:
             getattr(L, name).restype = ctypes.c_int
         L.ck_status_string.argtypes = [ctypes.c_int]
@@ -296,6 +309,50 @@ def profile_collect() -> dict:
             "bwd_launches": bn.value}
 
 
+def lif_forward(graph: SparseGraph, impulses, delays, v0, T: int, threshold: int, reset: int,
+                refractory_steps: int, decay_shifts=(), workspace=None, stream=None):
+    """Run ``ck_lif_forward`` (fixed-point leaky integrate-and-fire on the
+    graph): impulses int16 [E] and delays int32 [E] in the caller's edge
+    order, v0 int32 [N].  Returns (spikes uint8 [T, N], potentials int32
+    [T, N]).  Synchronises the stream; raises CkError with status
+    CK_ERR_OVERFLOW (and .step, the first overflowing timestep) if a
+    potential left the int32 range."""
+    N, E = graph.num_nodes, graph.num_edges
+    _dev(impulses, "impulses", torch.int16, (E,))
+    _dev(delays, "delays", torch.int32, (E,))
+    _dev(v0, "v0", torch.int32, (N,))
+    shifts = list(decay_shifts)
+    if len(shifts) > 8:
+        raise ValueError("at most 8 decay shifts")
+    prm = LifParams(int(threshold), int(reset), int(refractory_steps), len(shifts),
+                    (ctypes.c_int32 * 8)(*shifts))
+    wb = ctypes.c_size_t()
+    _check(lib().ck_lif_workspace_size(graph.handle, ctypes.byref(wb)))
+    workspace = _byte_buffer(wb.value, v0.device) if workspace is None else workspace
+    spikes = torch.empty((int(T), N), dtype=torch.uint8, device=v0.device)
+    pot = torch.empty((int(T), N), dtype=torch.int32, device=v0.device)
+    step = ctypes.c_int64(-1)
+    st = lib().ck_lif_forward(graph.handle, _ptr(impulses), _ptr(delays), ctypes.byref(prm),
+                              _ptr(v0), int(T), _ptr(spikes), _ptr(pot), ctypes.byref(step),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream))
+    if st != 0:
+        err = CkError(st, lib().ck_last_error().decode())
+        err.step = step.value
+        raise err
+    return spikes, pot
+
+
+def profile_collect_lif() -> dict:
+    """LIF kernel milliseconds and launch counts recorded since the last collect."""
+    gm, um = ctypes.c_double(), ctypes.c_double()
+    gn, un = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ck_profile_collect_lif(ctypes.byref(gm), ctypes.byref(gn), ctypes.byref(um),
+                                        ctypes.byref(un)))
+    return {"gather_ms": gm.value, "gather_launches": gn.value, "update_ms": um.value,
+            "update_launches": un.value}
+
+
 class _SparseRecurrence(torch.autograd.Function):
     @staticmethod
     def forward(ctx, edge_values, leak, bias, drives, state0, graph, microsteps, check):
@@ -338,6 +395,6 @@ def sparse_recurrence(edge_values, leak, bias, drives, state0, graph: SparseGrap
 
 
 __all__ = ["SparseGraph", "sparse_recurrence", "recurrence_forward", "recurrence_backward",
-           "recurrence_forward_noalloc",
+           "recurrence_forward_noalloc", "lif_forward", "profile_collect_lif", "LifParams",
            "recurrence_sizes", "recurrence_status", "recurrence_path", "profile_enable", "profile_collect", "CkError", "CkLibraryMissing",
            "lib", "LIB_PATH", "EXPORTED"]

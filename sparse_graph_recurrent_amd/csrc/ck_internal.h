@@ -104,7 +104,7 @@ namespace ckhip {
 // Measurement hook state: HIP event pairs around the main kernel launches.
 struct Profile {
   bool enabled = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> fwd, bwd;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> fwd, bwd, lif_gather, lif_update;
 };
 extern Profile g_profile;
 

@@ -635,6 +635,8 @@ extern "C" const char* ck_status_string(ck_status s) {
     case CK_ERR_HIP: return "CK_ERR_HIP";
     case CK_ERR_BAD_HANDLE: return "CK_ERR_BAD_HANDLE";
     case CK_ERR_WAIT: return "CK_ERR_WAIT";
+    case CK_ERR_OVERFLOW: return "CK_ERR_OVERFLOW";
+    case CK_ERR_BAD_VALUE: return "CK_ERR_BAD_VALUE";
   }
   return "CK_ERR_UNKNOWN";
 }

@@ -1302,5 +1302,37 @@ extern "C" ck_status ck_profile_collect(double* fwd_ms, int64_t* fwd_launches, d
   };
   drain(g_profile.fwd, fwd_ms, fwd_launches);
   drain(g_profile.bwd, bwd_ms, bwd_launches);
+  drain(g_profile.lif_gather, nullptr, nullptr);
+  drain(g_profile.lif_update, nullptr, nullptr);
+  return rc;
+}
+
+extern "C" ck_status ck_profile_collect_lif(double* gather_ms, int64_t* gather_launches,
+                                            double* update_ms, int64_t* update_launches) {
+  clear_error();
+  ck_status rc = CK_OK;
+  if (!g_profile.lif_gather.empty() || !g_profile.lif_update.empty())
+    CK_HIP_TRY(hipDeviceSynchronize());
+  auto drain = [&](std::vector<std::pair<hipEvent_t, hipEvent_t>>& log, double* ms,
+                   int64_t* n) {
+    double total = 0.0;
+    for (auto& e : log) {
+      float t = 0.f;
+      hipError_t err = hipEventSynchronize(e.second);
+      if (err == hipSuccess) err = hipEventElapsedTime(&t, e.first, e.second);
+      if (err != hipSuccess && rc == CK_OK) {
+        set_error("profiling event failed: %s", hipGetErrorString(err));
+        rc = CK_ERR_HIP;
+      }
+      total += t;
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
+    }
+    if (ms) *ms = total;
+    if (n) *n = (int64_t)log.size();
+    log.clear();
+  };
+  drain(g_profile.lif_gather, gather_ms, gather_launches);
+  drain(g_profile.lif_update, update_ms, update_launches);
   return rc;
 }

@@ -266,3 +266,34 @@ def random_graph(rng: np.random.Generator, N: int, E: int, n_in: int, B: int, T:
     grad_out = rng.standard_normal((T, B, N)).astype(f32)
     return Workload("random", -1, N, src.astype(np.int64), dst.astype(np.int64), inputs, v, leak,
                     bias, drives, state0, grad_out, M)
+
+
+@dataclasses.dataclass
+class LifWorkload:
+    """Inputs of the fixed-point LIF forward on a workload's graph."""
+    name: str
+    num_nodes: int
+    src: np.ndarray        # int64 [E], caller order
+    dst: np.ndarray        # int64 [E]
+    input_nodes: np.ndarray
+    impulses: np.ndarray   # int16 [E]
+    delays: np.ndarray     # int32 [E]
+    v0: np.ndarray         # int32 [N]
+
+
+def make_lif(name: str = "connectome", seed: int = 7, max_delay: int = 1,
+             v0_range=(0, 1)) -> LifWorkload:
+    """The graph of workload `name` with integer LIF inputs: each edge's
+    impulse is sign * synapse count, sign +1 with p=0.8 (else -1) and count
+    = 1 + floor(lognormal(1.5, 1.0)) capped at 32767; delays uniform in
+    1..max_delay (the soup-connectome page's runs fix none; 1 reproduces a
+    one-step delay line); initial potentials uniform in v0_range."""
+    w = make(name, B=1, T=1)
+    rng = np.random.default_rng([seed, 2])
+    E = w.num_edges
+    count = np.minimum(1 + np.floor(rng.lognormal(1.5, 1.0, E)), 32767).astype(np.int64)
+    sign = np.where(rng.random(E) < 0.8, 1, -1)
+    impulses = (sign * count).astype(np.int16)
+    delays = rng.integers(1, max_delay + 1, E).astype(np.int32)
+    v0 = rng.integers(v0_range[0], v0_range[1], w.num_nodes).astype(np.int32)
+    return LifWorkload(name, w.num_nodes, w.src, w.dst, w.input_nodes, impulses, delays, v0)

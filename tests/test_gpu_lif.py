@@ -1,0 +1,141 @@
+"""GPU parity of the fixed-point LIF forward (ck_lif_forward, through the C
+ABI) against the LIF oracle (oracle/lif_oracle.c): integer arithmetic, so
+spikes and potentials must be bit-exact, and a rejected overflow must be
+reported at the same timestep.  Workloads: the hand-worked timeline, small
+random graphs with delays up to 9 steps, the soup-connectome page's standard
+and stress runs re-read on the synthetic whole-connectome graph, and an
+active run on that graph (hubs of in-degree up to 20,000, delays 1..4)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_graph_recurrent_amd as sgr
+import synthetic
+from gpu_helpers import log, to_dev
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+I32_MAX = 2**31 - 1
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sgr.lib()
+
+
+def _graph(src, dst, N):
+    return sgr.SparseGraph(to_dev(np.asarray(src, np.int64)), to_dev(np.asarray(dst, np.int64)), N,
+                           to_dev(np.zeros(0, np.int64)))
+
+
+def _both(src, dst, N, w, d, v0, T, thr, reset, refr, shifts, graph=None):
+    g = _graph(src, dst, N) if graph is None else graph
+    s, p = sgr.lif_forward(g, to_dev(np.asarray(w, np.int16)), to_dev(np.asarray(d, np.int32)),
+                           to_dev(np.asarray(v0, np.int32)), T, thr, reset, refr, shifts)
+    s, p = s.cpu().numpy(), p.cpu().numpy()
+    s2, p2 = oracle.lif_run(src, dst, N, w, d, v0, T, thr, reset, refr, shifts)
+    np.testing.assert_array_equal(s, s2)
+    np.testing.assert_array_equal(p, p2)
+    return s
+
+
+def test_hand_worked_timeline():
+    g = json.load(open(os.path.join(HERE, "golden", "lif_timeline.json")))
+    log("LIF: hand-worked timeline")
+    s = _both(g["src"], g["dst"], g["num_nodes"], g["impulse"], g["delay"], g["v0"], g["T"],
+              g["threshold"], g["reset"], g["refractory_steps"], g["decay_shifts"])
+    np.testing.assert_array_equal(s, np.array(g["spikes"], np.uint8))
+
+
+@pytest.mark.parametrize("seed,N,E,max_delay,refr,shifts,active", [
+    (1, 50, 900, 1, 0, [2], True), (2, 300, 9000, 9, 2, [1, 4], True),
+    (3, 1000, 4000, 3, 1, [], True), (4, 129, 5000, 5, 3, [0], False),
+    (5, 2000, 60000, 7, 2, [3, 31], True)])
+def test_random_graphs(seed, N, E, max_delay, refr, shifts, active):
+    """(shift 0 zeroes every potential before the impulses arrive: no neuron
+    ever reaches the threshold there.)"""
+    rng = np.random.default_rng(seed)
+    src, dst = rng.integers(0, N, E), rng.integers(0, N, E)   # parallel edges, self-loops
+    w = (np.where(rng.random(E) < 0.8, 1, -1) * rng.integers(1, 120, E)).astype(np.int16)
+    d = rng.integers(1, max_delay + 1, E).astype(np.int32)
+    v0 = rng.integers(-200, 600, N).astype(np.int32)
+    log(f"LIF: random graph N={N} E={E} delays<={max_delay}")
+    s = _both(src, dst, N, w, d, v0, 20, 100, -20, refr, shifts)
+    assert (s[10:].sum() > 0) == active
+
+
+@pytest.fixture(scope="module")
+def connectome():
+    w = synthetic.make_lif("connectome")
+    g = _graph(w.src, w.dst, w.num_nodes)
+    return w, g
+
+
+def test_pages_standard_run_on_connectome(connectome):
+    """threshold 20000, reset 0, decay_shifts [2], refractory 2, 4 steps,
+    neuron 0 seeded at 30000 (soup-connectome, "Full-scale benchmark")."""
+    w, g = connectome
+    v0 = np.zeros(w.num_nodes, np.int32)
+    v0[0] = 30000
+    log("LIF: the page's standard run on the synthetic connectome")
+    s = _both(w.src, w.dst, w.num_nodes, w.impulses, w.delays, v0, 4, 20000, 0, 2, [2], graph=g)
+    assert s.sum(axis=1).tolist() == [1, 0, 0, 0]
+
+
+def test_pages_stress_run_on_connectome(connectome):
+    """threshold 1, reset 0, decay_shifts [31], refractory 0, 2 steps (the
+    page's active stress configuration)."""
+    w, g = connectome
+    v0 = np.zeros(w.num_nodes, np.int32)
+    v0[0] = 30000
+    log("LIF: the page's stress run on the synthetic connectome")
+    s = _both(w.src, w.dst, w.num_nodes, w.impulses, w.delays, v0, 2, 1, 0, 0, [31], graph=g)
+    log(f"  spike counts {s.sum(axis=1).tolist()}")
+    assert s[0].sum() == 1 and s[1].sum() > 0
+
+
+def test_active_run_on_connectome():
+    """A run that stays active: 12-48 % of the 211,577 neurons spike per step,
+    delays 1..4, hubs of in-degree up to 20,000."""
+    w = synthetic.make_lif("connectome", max_delay=4, v0_range=(0, 60))
+    log("LIF: active run on the synthetic connectome, 16 steps")
+    s = _both(w.src, w.dst, w.num_nodes, w.impulses, w.delays, w.v0, 16, 40, 0, 2, [2])
+    log(f"  spike counts {s.sum(axis=1).tolist()}")
+    assert (s.sum(axis=1) > 1000).all()
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+def test_overflow_is_rejected_at_the_same_step(sign):
+    v0 = [I32_MAX, sign * (I32_MAX - 500), 5]
+    src, dst, w, d = [0, 0], [1, 2], [sign * 1000, 3], [3, 1]
+    with pytest.raises(oracle.LifOverflow) as eo:
+        oracle.lif_run(src, dst, 3, w, d, v0, 6, I32_MAX, 0, 0, [])
+    log(f"LIF: overflow ({'up' if sign > 0 else 'down'}) at step {eo.value.step}")
+    g = _graph(src, dst, 3)
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.lif_forward(g, to_dev(np.asarray(w, np.int16)), to_dev(np.asarray(d, np.int32)),
+                        to_dev(np.asarray(v0, np.int32)), 6, I32_MAX, 0, 0, [])
+    assert ei.value.status == 11 and ei.value.step == eo.value.step == 3
+
+
+def test_invalid_values_are_rejected():
+    g = _graph([0, 1], [1, 0], 2)
+    w = to_dev(np.array([5, 5], np.int16))
+    v0 = to_dev(np.zeros(2, np.int32))
+    for d, shifts, refr in (([0, 1], [2], 0), ([1, 40000], [2], 0), ([1, 1], [32], 0),
+                            ([1, 1], [2], -1), ([1, 1], list(range(9)), 0)):
+        with pytest.raises((sgr.CkError, ValueError)) as ei:
+            sgr.lif_forward(g, w, to_dev(np.asarray(d, np.int32)), v0, 3, 10, 0, refr, shifts)
+        if isinstance(ei.value, sgr.CkError):
+            assert ei.value.status == 12
+
+
+def test_graph_without_edges():
+    log("LIF: graph without edges")
+    _both([], [], 7, [], [], [0, 5, 10, 15, 20, -3, 99], 5, 12, 1, 1, [1])
