@@ -28,8 +28,8 @@
  *   - Sizes: num_nodes and num_edges must be below 2^31, and num_nodes times
  *     the padded batch width (B rounded up to a multiple of 4) must be below
  *     2^30 (one state plane under 4 GiB); otherwise CK_ERR_TOO_LARGE.
- *   - A graph handle is immutable after creation.  On the per-microstep path
- *     (ck_recurrence_path) it may be used from several streams at once
+ *   - A graph handle is immutable after creation.  On the per-microstep and
+ *     blocked paths (ck_recurrence_path) it may be used from several streams at once
  *     provided each call has its own `saved` and `workspace`.  An XCD-resident
  *     call occupies every compute unit and its workgroups wait for one
  *     another: issue resident calls on one stream, with no other device work
@@ -85,6 +85,9 @@ typedef enum {
  * is at most 9184 and the environment variable CK_RESIDENT is not "0" at
  * creation, it also plans the XCD-resident kernels (see
  * ck_recurrence_path), which run a whole forward or backward in one launch.
+ * When the device's compute units are a multiple of 8 and num_nodes is at
+ * least 100000 (or the environment variable CK_BLOCKED is "1" at creation;
+ * "0" turns this off), it plans the blocked kernels (ck_recurrence_path).
  * The caller's edge order is kept for edge values and their gradient: the
  * permutation is invisible outside.  Validation failures return
  * CK_ERR_BAD_SIZE, CK_ERR_TOO_LARGE, CK_ERR_NULL_ARG, CK_ERR_INDEX_RANGE or
@@ -128,8 +131,10 @@ ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int64_t micros
                               size_t* saved_bytes, size_t* workspace_bytes);
 
 /*
- * Which kernels a call with batch B runs on this graph: *resident = 1 for the
- * XCD-resident kernels, 0 for the per-microstep kernels.
+ * Which kernels a call with batch B runs on this graph: *path = 1 for the
+ * XCD-resident kernels, 2 for the blocked kernels, 0 for the per-microstep
+ * kernels.  The resident kernels are taken whenever the graph has their
+ * plans; else the blocked kernels when the graph has theirs and 5 <= B <= 64.
  *
  * Per-microstep kernels: one fused launch per microstep and direction, the
  * rows of all batch columns spread over every compute unit.
@@ -148,9 +153,16 @@ ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int64_t micros
  * poll limit of those waits is read from CK_RESIDENT_SPIN_LIMIT at graph
  * creation, default 1048576; a negative value fails every wait at once and
  * exists to test that failure path.)
- * Both paths compute the same sums; results agree to rounding.
+ * Blocked kernels (graphs of at least 100000 nodes, or CK_BLOCKED set to
+ * "1" at creation; 5 <= B <= 64): two launches per microstep and direction.  The nodes
+ * whose rows are gathered are cut into 8 contiguous blocks, one per XCD, so
+ * each XCD gathers from a slice of the state plane that stays in its own L2;
+ * each row's edges into a block (at most 64 per work item) leave one partial
+ * row, and a second launch adds each row's partials in a fixed order and runs
+ * the elementwise update.
+ * All paths compute the same sums; results agree to rounding.
  */
-ck_status ck_recurrence_path(ck_graph_t g, int64_t B, int* resident);
+ck_status ck_recurrence_path(ck_graph_t g, int64_t B, int* path);
 
 /*
  * Forward over the whole window (connectome-kernels README, introduction and

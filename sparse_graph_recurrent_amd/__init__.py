@@ -195,13 +195,17 @@ def recurrence_sizes(graph: SparseGraph, T: int, B: int, microsteps: int):
     return s.value, w.value
 
 
+PATH_NAMES = {0: "per_microstep", 1: "resident", 2: "blocked"}
+
+
 def recurrence_path(graph: SparseGraph, B: int) -> str:
     """Kernels a call with batch B runs on this graph: "resident" (one launch
-    per call, each XCD computing one group of 4 batch columns) or
+    per call, each XCD computing one group of 4 batch columns), "blocked" (two
+    launches per microstep, each XCD gathering from its own block of nodes) or
     "per_microstep" (one launch per microstep)."""
     r = ctypes.c_int()
     _check(lib().ck_recurrence_path(graph.handle, int(B), ctypes.byref(r)))
-    return "resident" if r.value else "per_microstep"
+    return PATH_NAMES[r.value]
 
 
 def _byte_buffer(nbytes: int, device) -> torch.Tensor:

@@ -24,6 +24,22 @@ struct Schedule {
   int KB = 0;               // batch entries per wave (padded with row = -1)
 };
 
+// Device copy of a BlockedPlan (see schedule.h).
+struct Blocked {
+  int4* table = nullptr;         // [num_wgs * kBlkWaves][KB + kBlkPad] items {row, kbeg, count, id}
+  int32_t* row_items = nullptr;  // [N + 1]: row i's items are item_ids[row_items[i] ..]
+  int32_t* item_ids = nullptr;   // [items] partial row of each of a row's items
+  int32_t* pnode = nullptr;      // [E] gathered node of the edge at each blocked position
+  int32_t* pperm = nullptr;      // [E] caller index of that edge
+  int num_wgs = 0;
+  int KB = 0;
+  int64_t items = 0;
+};
+// Graphs of at least this many nodes get blocked plans at creation (unless
+// CK_BLOCKED is "0"; CK_BLOCKED=1 plans them for any graph).  Below it the
+// per-microstep kernels' gathers mostly hit the L2s already.
+constexpr int64_t kBlkMinN = 100000;
+
 // Largest node count of the XCD-resident kernels: one workgroup holds a
 // whole [N + kResZeroRows] x 16-byte state plane plus kResLanes 16-byte partial sums in
 // the 160 KiB of LDS of a gfx950 compute unit.
@@ -77,6 +93,11 @@ struct ck_graph {
   int res_spin_limit;
   ckhip::Resident res_fwd;  // rows of the CSR
   ckhip::Resident res_bwd;  // rows of the transposed CSR
+  // blocked per-microstep kernels: usable when blk_ok is set at creation
+  // (both orientations planned; see kBlkMinN and CK_BLOCKED)
+  int blk_ok;
+  ckhip::Blocked blk_fwd;   // rows of the CSR, items over source blocks
+  ckhip::Blocked blk_bwd;   // rows of the transposed CSR, items over destination blocks
 };
 
 namespace ckhip {
@@ -161,6 +182,37 @@ ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_val
 // forward's fixed scratch array (called at graph creation, with `device`
 // current).
 ck_status scratch_prepare(int device);
+// Sizes of one call of the blocked kernels (8 <= Bp <= 64, L = Bp / 4).
+struct BlkDims {
+  int64_t N, E, n_in, T, B, M, S, Bp;
+  int L;
+  size_t plane;  // floats per [N][Bp] plane
+};
+// Workspace of the blocked path, byte offsets; a forward uses [0, fwd_end).
+struct BlkWs {
+  size_t pe, part, h0, fwd_end, gv, gh, ga0, ga1, total;
+};
+BlkWs blk_ws_layout(const ck_graph* g, const BlkDims& d);
+// True when the graph has blocked plans and a call of Bp padded columns fits
+// them (8 <= Bp <= 64, buffer byte offsets below 2^32).
+bool blk_fits(const ck_graph* g, int64_t Bp);
+ck_status blk_forward(const ck_graph* g, const BlkDims& d, const float* edge_values,
+                      const float* leak, const float* bias, const float* drives,
+                      const float* state0, float* out, void* saved, void* workspace,
+                      hipStream_t stream, bool profile);
+ck_status blk_backward(const ck_graph* g, const BlkDims& d, const float* edge_values,
+                       const float* leak, const float* state0, const void* saved,
+                       const float* grad_out, float* grad_edge_values, float* grad_leak,
+                       float* grad_bias, float* grad_drives, float* grad_state0,
+                       void* workspace, hipStream_t stream);
+// Plan and upload the blocked items of one orientation (row pointers ptr;
+// gathered node col and caller index perm of each compressed edge, on the
+// device); *planned is false when the device shape allows no plan.
+ck_status build_blocked(const std::vector<int32_t>& ptr, int64_t N, const int32_t* col,
+                        const int32_t* perm, int num_cus, hipStream_t stream, Blocked* out,
+                        bool* planned);
+void free_blocked(Blocked* b);
+
 ck_status res_backward(const ck_graph* g, const ResDims& d, const float* edge_values,
                        const float* leak, const float* state0, const void* saved,
                        const float* grad_out, float* grad_edge_values, float* grad_leak,

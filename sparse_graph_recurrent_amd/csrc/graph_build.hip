@@ -429,6 +429,8 @@ void free_graph_arrays(ck_graph* g) {
     }
   free_resident(&g->res_fwd);
   free_resident(&g->res_bwd);
+  free_blocked(&g->blk_fwd);
+  free_blocked(&g->blk_bwd);
 }
 
 }  // namespace
@@ -563,6 +565,24 @@ extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int
       if (!g->res_ok) {
         free_resident(&g->res_fwd);
         free_resident(&g->res_bwd);
+      }
+    }
+  }
+  // blocked plans (optional: for graphs whose state plane dwarfs the L2s)
+  {
+    const char* env = getenv("CK_BLOCKED");
+    const bool wanted = env && env[0] ? (env[0] == '1' && env[1] == '\0') : N >= kBlkMinN;
+    if (wanted) {
+      bool pf = false, pb = false;
+      rc = build_blocked(hptr, N, g->col_idx, g->perm, num_cus, stream, &g->blk_fwd, &pf);
+      if (rc != CK_OK) return fail(rc);
+      if (pf)
+        rc = build_blocked(htptr, N, g->t_col_idx, g->t_perm, num_cus, stream, &g->blk_bwd, &pb);
+      if (rc != CK_OK) return fail(rc);
+      g->blk_ok = pf && pb ? 1 : 0;
+      if (!g->blk_ok) {
+        free_blocked(&g->blk_fwd);
+        free_blocked(&g->blk_bwd);
       }
     }
   }

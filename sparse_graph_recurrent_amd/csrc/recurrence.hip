@@ -878,7 +878,9 @@ struct Dims {
   int64_t slots_f, slots_b;  // padded edge slots of the forward / backward schedule
   size_t plane;  // floats per [N][Bp] plane
   bool resident;  // the call runs the XCD-resident kernels (one launch per call)
+  bool blocked;   // the call runs the blocked kernels (two launches per microstep)
   ResDims rd;
+  BlkDims bd;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -934,7 +936,16 @@ ck_status make_dims(const ck_graph* g, int64_t T, int64_t B, int64_t M, Dims* d)
   // offsets below 2^31 (range-checked buffer accesses)
   d->resident = g->res_ok != 0 && std::max(g->N, g->n_in) * B * 4 < (1LL << 31);
   d->rd = ResDims{g->N, (g->N + 7) / 8 * 8, B, Bp / 4, g->n_in, T, M, T * M};
+  d->blocked = !d->resident && blk_fits(g, Bp);
+  d->bd = BlkDims{g->N, g->E, g->n_in, T, B, M, T * M, Bp, (int)(Bp / 4), d->plane};
   return CK_OK;
+}
+
+// Workspace bytes of a call (either direction).
+size_t ws_total(const ck_graph* g, const Dims& d) {
+  if (d.resident) return res_ws_layout(g, d.rd).total;
+  if (d.blocked) return blk_ws_layout(g, d.bd).total;
+  return ws_layout(d).total;
 }
 
 }  // namespace
@@ -952,22 +963,22 @@ extern "C" ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int
   if (rc != CK_OK) return rc;
   if (saved_bytes)
     *saved_bytes = d.resident ? res_saved_bytes(d.rd) : 2 * (size_t)d.S * d.plane * sizeof(float);
-  if (workspace_bytes) *workspace_bytes = d.resident ? res_ws_layout(g, d.rd).total : ws_layout(d).total;
+  if (workspace_bytes) *workspace_bytes = ws_total(g, d);
   return CK_OK;
 }
 
-extern "C" ck_status ck_recurrence_path(ck_graph_t g, int64_t B, int* resident) {
+extern "C" ck_status ck_recurrence_path(ck_graph_t g, int64_t B, int* path) {
   clear_error();
   ck_status rc = check_graph(g);
   if (rc != CK_OK) return rc;
-  if (!resident) {
-    set_error("resident output pointer is NULL");
+  if (!path) {
+    set_error("path output pointer is NULL");
     return CK_ERR_NULL_ARG;
   }
   Dims d;
   rc = make_dims(g, 1, B, 1, &d);
   if (rc != CK_OK) return rc;
-  *resident = d.resident ? 1 : 0;
+  *path = d.resident ? 1 : d.blocked ? 2 : 0;
   return CK_OK;
 }
 
@@ -976,7 +987,9 @@ namespace {
 // Bytes of the workspace a forward call touches (its leading part: the
 // backward's regions follow it).
 size_t forward_ws_bytes(const ck_graph* g, const Dims& d) {
-  return d.resident ? res_forward_ws_bytes(g, d.rd) : ws_layout(d).gh;
+  if (d.resident) return res_forward_ws_bytes(g, d.rd);
+  if (d.blocked) return blk_ws_layout(g, d.bd).fwd_end;
+  return ws_layout(d).gh;
 }
 
 // Argument checks shared by both forward entry points.
@@ -1004,6 +1017,9 @@ ck_status forward_body(const ck_graph* g, const Dims& d, const float* edge_value
                        hipStream_t stream, bool profile) {
   if (d.resident)
     return res_forward(g, d.rd, edge_values, leak, bias, drives, state0, out, saved, workspace,
+                       stream, profile);
+  if (d.blocked)
+    return blk_forward(g, d.bd, edge_values, leak, bias, drives, state0, out, saved, workspace,
                        stream, profile);
   ck_status rc = CK_OK;
   const WsLayout ws = ws_layout(d);
@@ -1083,7 +1099,7 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
     set_error("NULL workspace in forward");
     return CK_ERR_NULL_ARG;
   }
-  const size_t need = d.resident ? res_ws_layout(g, d.rd).total : ws_layout(d).total;
+  const size_t need = ws_total(g, d);
   if (workspace_bytes < need) {
     set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, need);
     return CK_ERR_WORKSPACE;
@@ -1144,6 +1160,15 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
       return CK_ERR_WORKSPACE;
     }
     return res_backward(g, d.rd, edge_values, leak, state0, saved, grad_out, grad_edge_values,
+                        grad_leak, grad_bias, grad_drives, grad_state0, workspace, stream);
+  }
+  if (d.blocked) {
+    const size_t need = blk_ws_layout(g, d.bd).total;
+    if (workspace_bytes < need) {
+      set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, need);
+      return CK_ERR_WORKSPACE;
+    }
+    return blk_backward(g, d.bd, edge_values, leak, state0, saved, grad_out, grad_edge_values,
                         grad_leak, grad_bias, grad_drives, grad_state0, workspace, stream);
   }
   const WsLayout ws = ws_layout(d);

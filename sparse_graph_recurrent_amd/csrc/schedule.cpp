@@ -3,6 +3,7 @@
 #include "schedule.h"
 
 #include <algorithm>
+#include <climits>
 
 namespace ckhip {
 
@@ -383,6 +384,88 @@ void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out) {
         }
       }
     }
+}
+
+bool plan_blocked(const int32_t* ptr, const int32_t* col, int64_t N, int num_cus,
+                  BlockedPlan* out) {
+  if (num_cus <= 0 || num_cus % kBlkBlocks != 0 || N < 0) return false;
+  BlockedPlan& p = *out;
+  p = BlockedPlan();
+  p.num_wgs = num_cus;
+  const int64_t bs = std::max<int64_t>(1, (N + kBlkBlocks - 1) / kBlkBlocks);
+  // items, numbered row by row
+  std::vector<std::vector<BlkItem>> per(kBlkBlocks);
+  p.row_items.assign(N + 1, 0);
+  int64_t id = 0;
+  for (int64_t i = 0; i < N; ++i) {
+    p.row_items[i] = (int32_t)id;
+    int64_t k = ptr[i];
+    while (k < ptr[i + 1]) {
+      const int64_t x = col[k] / bs;
+      int64_t e = k;
+      while (e < ptr[i + 1] && col[e] / bs == x) ++e;
+      for (int64_t c = k; c < e; c += kBlkChunk) {
+        if (id >= (int64_t)INT32_MAX) return false;
+        per[x].push_back(BlkItem{(int32_t)i, (int32_t)c,
+                                 (int32_t)std::min<int64_t>(kBlkChunk, e - c), (int32_t)id++});
+      }
+      k = e;
+    }
+  }
+  p.row_items[N] = (int32_t)id;
+  p.items = id;
+  // deal each block's items to the waves of its workgroups
+  const int wgs_per = num_cus / kBlkBlocks;
+  const int nw = wgs_per * kBlkWaves;  // waves per block
+  std::vector<std::vector<std::vector<BlkItem>>> lists(kBlkBlocks);
+  size_t KB = 0;
+  for (int x = 0; x < kBlkBlocks; ++x) {
+    std::vector<BlkItem>& it = per[x];
+    std::stable_sort(it.begin(), it.end(),
+                     [](const BlkItem& a, const BlkItem& b) { return a.count > b.count; });
+    lists[x].assign(nw, {});
+    // min-heap of (cost so far, wave)
+    std::vector<std::pair<int64_t, int>> heap;
+    for (int w = 0; w < nw; ++w) heap.emplace_back(0, w);
+    auto later = [](const std::pair<int64_t, int>& a, const std::pair<int64_t, int>& b) {
+      return a > b;
+    };
+    std::make_heap(heap.begin(), heap.end(), later);
+    for (const BlkItem& item : it) {
+      std::pop_heap(heap.begin(), heap.end(), later);
+      auto& top = heap.back();
+      lists[x][top.second].push_back(item);
+      top.first += item.count + kBlkItemCost;
+      std::push_heap(heap.begin(), heap.end(), later);
+    }
+    for (const auto& l : lists[x]) KB = std::max(KB, l.size());
+  }
+  p.KB = (int)KB;
+  // wave v = b * kBlkWaves + w of workgroup b serves block b % kBlkBlocks as
+  // that block's wave (b / kBlkBlocks) * kBlkWaves + w
+  const size_t stride = KB + kBlkPad;
+  p.table.assign((size_t)num_cus * kBlkWaves * stride, BlkItem{-1, 0, 0, 0});
+  p.edge_order.assign(ptr[N], 0);
+  p.item_ids.assign(id, 0);
+  // Positions (of edges and of partial rows) go group by group of kBlkGroup
+  // items: all waves' first groups, then all waves' second groups, ... so the
+  // waves, which walk their lists at about the same pace, read and write
+  // nearby memory at any moment.
+  int64_t pos = 0, walk = 0;
+  for (size_t g0 = 0; g0 < KB; g0 += kBlkGroup)
+    for (int b = 0; b < num_cus; ++b)
+      for (int w = 0; w < kBlkWaves; ++w) {
+        const auto& l = lists[b % kBlkBlocks][(b / kBlkBlocks) * kBlkWaves + w];
+        BlkItem* t = &p.table[((size_t)b * kBlkWaves + w) * stride];
+        for (size_t q = g0; q < std::min(l.size(), g0 + kBlkGroup); ++q) {
+          t[q] = l[q];
+          t[q].kbeg = (int32_t)pos;
+          t[q].id = (int32_t)walk;
+          p.item_ids[l[q].id] = (int32_t)walk++;  // (l[q].id: the item's number row by row)
+          for (int32_t j = 0; j < l[q].count; ++j) p.edge_order[pos++] = l[q].kbeg + j;
+        }
+      }
+  return true;
 }
 
 }  // namespace ckhip

@@ -152,4 +152,62 @@ int64_t resident_conflict_cost(const int32_t* col, int64_t N, const ResidentPlan
 // than kResLanes pieces or rows).
 bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_lens, ResidentPlan* out);
 
+// ---------------------------------------------------------------------------
+// Blocked plan: the per-microstep kernels of graphs whose state plane is far
+// larger than the L2 caches.  The gathered nodes (the far end of each edge:
+// the source in the forward, the destination in the backward) are cut into
+// kBlkBlocks contiguous blocks of ceil(N / kBlkBlocks) nodes, one per XCD:
+// the workgroups of XCD x gather rows of block x only, so that block's slice
+// of the plane stays in that XCD's L2.  A row's edges into one block are one
+// contiguous run (each row's edges are sorted by gathered node); the run is
+// cut into work items of at most kBlkChunk edges.  An item leaves one partial
+// sum row; a second kernel adds each row's partials in item order.
+constexpr int kBlkBlocks = 8;
+constexpr int kBlkChunk = 64;
+constexpr int kBlkWaves = 16;  // waves per workgroup (one workgroup per CU)
+// Balancing cost of an item in edge units: its edges plus this much for
+// loading the item and storing its partial row.
+constexpr int kBlkItemCost = 8;
+// Padding entries (row = -1) after each wave's list: at least the widest pass
+// (64 items), so a wave may read the pass after its last one.
+constexpr int kBlkPad = 64;
+// Items per group of the blocked layout (see edge_order).
+constexpr int kBlkGroup = 8;
+
+// One work item: `count` edges of `row`, at positions [kbeg, kbeg + count)
+// of the blocked edge order (below); its partial row is number `id` (in the
+// same order as the edges).  The
+// same 16-byte layout as the int4 the kernels read; row = -1 pads a wave's
+// list.
+struct BlkItem {
+  int32_t row, kbeg, count, id;
+};
+
+struct BlockedPlan {
+  int num_wgs = 0;    // workgroup b serves block b % kBlkBlocks
+  int KB = 0;         // items of the longest wave list (shorter lists padded with row = -1)
+  int64_t items = 0;
+  // Row i's items, blocks ascending and chunks ascending, are entries
+  // [row_items[i], row_items[i+1]) of item_ids, which gives each one's id.
+  std::vector<int32_t> row_items;  // [N + 1]
+  std::vector<int32_t> item_ids;   // [items]
+  std::vector<BlkItem> table;      // [num_wgs * kBlkWaves][KB + kBlkPad]: wave v's items, largest first
+  // [E] the blocked edge order: position q holds compressed edge
+  // edge_order[q].  Items are laid out in groups of kBlkGroup consecutive
+  // items of one wave's list (their edges side by side), the first group of
+  // every wave, then the second group of every wave, and so on; item ids
+  // (partial rows) follow the same order.
+  std::vector<int32_t> edge_order;
+};
+
+// Plan the blocked schedule of a compressed row structure ptr[0..N] whose
+// edge k reads node col[k] (ascending within each row) for num_cus
+// workgroups of kBlkWaves waves.  Each block's items are dealt to the waves
+// of its workgroups largest first, each to the wave with the least cost so
+// far (edges plus kBlkItemCost per item); a wave walks its items largest
+// first, 64 / L at a time.  Returns false when num_cus is not a positive
+// multiple of kBlkBlocks or the ids would overflow 32 bits.
+bool plan_blocked(const int32_t* ptr, const int32_t* col, int64_t N, int num_cus,
+                  BlockedPlan* out);
+
 }  // namespace ckhip

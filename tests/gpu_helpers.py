@@ -41,19 +41,22 @@ def to_dev(a, dtype=None):
     return t.cuda()
 
 
-PATHS = ("resident", "per_microstep")
+PATHS = ("resident", "per_microstep", "blocked")
 
 
 def make_graph(w, path=None, env=None) -> sgr.SparseGraph:
     """The workload's graph.  path: None for the library's choice, or
-    "resident" / "per_microstep" to pin the kernels (CK_RESIDENT at creation;
-    a requested resident path must be the one taken at the workload's B).
-    env: extra environment variables set while the graph is created."""
+    "resident" / "per_microstep" / "blocked" to pin the kernels (CK_RESIDENT
+    and CK_BLOCKED at creation; the requested path must be the one taken at
+    the workload's B).  env: extra environment variables set while the graph
+    is created."""
     set_env = dict(env or {})
     if path == "per_microstep":
-        set_env["CK_RESIDENT"] = "0"
+        set_env.update(CK_RESIDENT="0", CK_BLOCKED="0")
     elif path == "resident":
         set_env["CK_RESIDENT"] = "1"
+    elif path == "blocked":
+        set_env.update(CK_RESIDENT="0", CK_BLOCKED="1")
     saved = {k: os.environ.get(k) for k in set_env}
     os.environ.update(set_env)
     try:

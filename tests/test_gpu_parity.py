@@ -128,7 +128,7 @@ def _mixed_graph(seed, B, T, M, N=400, E=9000, n_in=9):
 
 
 @pytest.mark.parametrize("B,path", [(b, p) for b in (1, 2, 3, 5, 8, 20, 31, 32, 33, 64, 65, 100)
-                                    for p in PATHS])
+                                    for p in PATHS if not (p == "blocked" and not 5 <= b <= 64)])
 def test_batch_widths_parity(B, path):
     w = _mixed_graph(100 + B, B=B, T=3, M=2)
     log(f"parity: mixed graph B={B} E={w.num_edges}, {path} kernels")
@@ -186,23 +186,24 @@ def test_edge_cases_full_parity(path):
     check_parity(run_gpu(w, path=path), w)
 
 
-def test_mid_scale_parity():
+@pytest.mark.parametrize("path", ["per_microstep", "blocked"])
+def test_mid_scale_parity(path):
     """Outputs on all 64 batch columns; gradients on columns 0, 37, 63."""
     w = synthetic.make("mid_scale")
     cols = [0, 37, 63]
     G = column_masked_grad(w, cols)
-    log("parity: mid-scale workload, gradients on columns 0, 37, 63")
-    gpu = run_gpu(w, G=G)
+    log(f"parity: mid-scale workload, gradients on columns 0, 37, 63, {path} kernels")
+    gpu = run_gpu(w, G=G, path=path)
     check_parity(gpu, w, G=G, cols=cols)
     log("parity: mid-scale workload, outputs on all columns")
     check_outputs_all_columns(gpu["out"], w)
 
 
-def _connectome_parity(w, label):
+def _connectome_parity(w, label, path=None):
     cols = [0, 31]
     G = column_masked_grad(w, cols)
-    log(f"parity: {label}, gradients on columns 0, 31")
-    gpu = run_gpu(w, G=G)
+    log(f"parity: {label}, gradients on columns 0, 31, {path or 'default'} kernels")
+    gpu = run_gpu(w, G=G, path=path)
     check_parity(gpu, w, G=G, cols=cols)
     log(f"parity: {label}, outputs on all columns")
     check_outputs_all_columns(gpu["out"], w)
@@ -211,11 +212,16 @@ def _connectome_parity(w, label):
 @pytest.mark.slow
 def test_connectome_parity():
     """Whole-connectome shape: hubs of in-degree up to 20,000, 80 % positive
-    weights, 64 microsteps.  fp32 evaluations of the definition miss the
-    stated bound on thousands of gradient entries here, by amounts that vary
-    several-fold with summation order; the per-microstep forward forms its
-    row sums in fp64 and stays within the bound on all but a few dozen."""
+    weights, 64 microsteps; the graph takes the blocked kernels.  fp32
+    evaluations of the definition miss the stated bound on thousands of
+    gradient entries here, by amounts that vary several-fold with summation
+    order; both forwards form their row sums in fp64 (the blocked one rounds
+    each item's sum to fp32 once) and stay within the bound on all but a few
+    dozen."""
     w = synthetic.make("connectome")
+    g = make_graph(w)
+    assert sgr.recurrence_path(g, w.B) == "blocked"
+    del g
     _connectome_parity(w, "whole-connectome workload")
     log("graph build: connectome")
     g = make_graph(w)
@@ -234,6 +240,13 @@ def test_connectome_zero_mean_weights_parity():
     w.edge_values = (np.abs(w.edge_values) * np.where(rng.random(w.num_edges) < 0.5, 1, -1)
                      ).astype(np.float32)
     _connectome_parity(w, "whole-connectome graph, zero-mean weights")
+
+
+@pytest.mark.slow
+def test_connectome_per_microstep_parity():
+    """The whole-connectome workload on the per-microstep kernels (pinned)."""
+    w = synthetic.make("connectome")
+    _connectome_parity(w, "whole-connectome workload", path="per_microstep")
 
 
 # ---------------------------------------------------------------- properties

@@ -24,8 +24,9 @@ def _need_gpu():
 def test_path_selection():
     """Graphs of up to 9184 nodes take the resident kernels at every batch
     width (beyond 32 columns each XCD computes several column groups in
-    turn), larger graphs the per-microstep kernels; CK_RESIDENT=0 at creation
-    turns the resident kernels off."""
+    turn), graphs of 100,000 nodes and more the blocked kernels from 5 to 64
+    columns, the rest the per-microstep kernels; CK_RESIDENT=0 and
+    CK_BLOCKED=0 at creation turn the first two off."""
     w = synthetic.make("flygpt", T=2)
     g = make_graph(w)
     log("path selection: flygpt graph")
@@ -34,6 +35,14 @@ def test_path_selection():
     big = synthetic.make("mid_scale", T=1)
     log("path selection: mid-scale graph")
     assert sgr.recurrence_path(make_graph(big), 32) == "per_microstep"
+    # graphs of 100,000 nodes and more take the blocked kernels from 5 to 64
+    # batch columns; CK_BLOCKED=0 at creation turns them off
+    huge = synthetic.random_graph(np.random.default_rng(5), 100_000, 200_000, 16, B=8, T=1, M=1)
+    log("path selection: 100,000-node graph")
+    gh = make_graph(huge)
+    assert ([sgr.recurrence_path(gh, B) for B in (4, 5, 32, 64, 65)]
+            == ["per_microstep"] + ["blocked"] * 3 + ["per_microstep"])
+    assert sgr.recurrence_path(make_graph(huge, env={"CK_BLOCKED": "0"}), 32) == "per_microstep"
 
 
 def test_largest_resident_graph():

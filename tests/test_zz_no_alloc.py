@@ -43,7 +43,7 @@ def _both(w, g):
         np.testing.assert_array_equal(gb[k].cpu().numpy(), ga[k].cpu().numpy(), err_msg=k)
 
 
-@pytest.mark.parametrize("path", ["resident", "per_microstep"])
+@pytest.mark.parametrize("path", ["resident", "per_microstep", "blocked"])
 def test_noalloc_forward_matches_workspace_forward(path):
     big = synthetic.make("flygpt", T=6)
     log(f"no-alloc forward: flygpt graph T=6 B=32, {path} kernels")
