@@ -63,6 +63,8 @@ CSRC = os.path.join(ROOT, "sparse_graph_recurrent_amd", "csrc")
 
 
 def kernel_source(kernel: str) -> str:
+    if kernel.startswith("blk_"):
+        return os.path.join(CSRC, "blocked.hip")
     return os.path.join(CSRC, "resident.hip" if kernel.startswith("res_") else "recurrence.hip")
 
 
@@ -334,11 +336,14 @@ def main():
     fwd_b, bwd_b, Q = algorithmic_bytes(N, E, n_in, B, T, M)
     # a step's S microsteps of forward (backward) bytes are spread over its
     # forward (backward) launches: S + 1 per-microstep backward launches (the
-    # first has no edge pass), or one resident launch per direction
-    resident = path == "resident"
+    # first has no edge pass), one resident launch per direction, or on the
+    # blocked path the part and epilogue launches of each microstep together
+    # (2 S forward, 2 S + 1 backward)
+    names = {"resident": ("res_fwd", "res_bwd"), "blocked": ("blk_fwd", "blk_bwd")}.get(
+        path, ("fwd_step", "bwd_step"))
     per_kernel = {}
-    for kname, per_b, us in ((("res_fwd" if resident else "fwd_step"), fwd_b * S / fwd_n, fwd_us),
-                             (("res_bwd" if resident else "bwd_step"), bwd_b * S / bwd_n, bwd_us)):
+    for kname, per_b, us in ((names[0], fwd_b * S / fwd_n, fwd_us),
+                             (names[1], bwd_b * S / bwd_n, bwd_us)):
         a = per_b / (us * 1e-6) / 1e9
         tr = measured_traffic(kname)
         m = None if tr is None else tr / (us * 1e-6) / 1e9

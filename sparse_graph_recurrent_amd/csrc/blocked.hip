@@ -716,7 +716,10 @@ ck_status blk_forward(const ck_graph* g, const BlkDims& d, const float* edge_val
     e.h_prev = a.src;
     e.h_next = hplanes + (size_t)(s - 1) * d.plane;
     e.a_next = aplanes + (size_t)(s - 1) * d.plane;
-    hipLaunchKernelGGL(epi, dim3(epi_blocks), dim3(256), 0, stream, e);
+    auto launch_epi = [&] { hipLaunchKernelGGL(epi, dim3(epi_blocks), dim3(256), 0, stream, e); };
+    if (profile) rc = timed_launch(g_profile.fwd, stream, launch_epi);
+    else launch_epi();
+    if (rc != CK_OK) return rc;
   }
   blk_from_planes<<<dim3(blocks_for(d.N, kT), (unsigned)((d.B + kT - 1) / kT),
                          (unsigned)std::min<int64_t>(d.T, 65535)),
@@ -806,7 +809,10 @@ ck_status blk_backward(const ck_graph* g, const BlkDims& d, const float* edge_va
       e.ga_out = nullptr;
       e.gdrives_t = nullptr;
     }
-    hipLaunchKernelGGL(epi, dim3(epi_blocks), dim3(256), 0, stream, e);
+    rc = timed_launch(g_profile.bwd, stream, [&] {
+      hipLaunchKernelGGL(epi, dim3(epi_blocks), dim3(256), 0, stream, e);
+    });
+    if (rc != CK_OK) return rc;
   }
   if (d.E > 0) {
     if (bb.KB > 0) {
