@@ -32,6 +32,11 @@ def test_path_selection():
     log("path selection: flygpt graph")
     assert [sgr.recurrence_path(g, B) for B in (1, 8, 20, 32, 33, 64, 100)] == ["resident"] * 7
     assert sgr.recurrence_path(make_graph(w, env={"CK_RESIDENT": "0"}), 32) == "per_microstep"
+    # the resident kernels address a step's [B][N] and [n_in][B] tensors with
+    # 32-bit byte offsets: a batch that puts N * B * 4 past 2^31 (while N * Bp
+    # stays below 2^30) takes the per-microstep kernels
+    assert 5000 * 110_000 * 4 >= 2**31 and 5000 * 110_000 < 2**30
+    assert sgr.recurrence_path(g, 110_000) == "per_microstep"
     big = synthetic.make("mid_scale", T=1)
     log("path selection: mid-scale graph")
     assert sgr.recurrence_path(make_graph(big), 32) == "per_microstep"
