@@ -298,10 +298,14 @@ ck_status ck_lif_workspace_size(ck_graph_t g, size_t* workspace_bytes);
  *   potentials   int32[T][N]  device, written: V after each step
  *   overflow_step  host, may be NULL: -1, or the first step whose update left
  *                  the int32 range
- * Runs on `stream` and synchronises it before returning (the overflow and
- * value checks are read back).  Returns CK_ERR_OVERFLOW if a potential left
- * the int32 range (outputs of that step and later are unspecified),
- * CK_ERR_BAD_VALUE for a delay outside [1, 32767], more than 8 decay shifts, a
+ * Runs on `stream` and synchronises it twice: once after the delays are
+ * validated (before any step runs; the largest delay picks the spike lookup:
+ * bit rows of the last max-delay steps held in LDS when max delay <= 16 and
+ * they fit 128 KB, else one byte read of `spikes` per edge; the environment
+ * variable CK_LIF_LDS set to "0" keeps the byte reads) and once at the end
+ * (the overflow check is read back).  Returns CK_ERR_OVERFLOW if a potential left the int32
+ * range (outputs of that step and later are unspecified), CK_ERR_BAD_VALUE for
+ * a delay outside [1, 32767] (no step is run), more than 8 decay shifts, a
  * shift outside [0, 31] or a negative refractory count.
  */
 ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const int32_t* delays,

@@ -17,13 +17,21 @@
 //                of positions of one row, then one 64-bit integer atomic add
 //                per run into I[row].  Integer sums are exact and associative,
 //                so the result does not depend on the order of the atomics.
+//                When the bit rows of the steps the delays reach fit in LDS
+//                (lif_gather_lds), each workgroup first copies them there and
+//                looks the spikes up in LDS instead of one scattered byte
+//                read per edge, and sums the runs with DPP prefix sums.
 //   lif_update   one thread per neuron: the state update above; writes the
-//                step's spikes and potentials, clears I.
+//                step's spikes and potentials (and the step's spike bits into
+//                a ring of kLifRing bit rows), clears I.
 // A per-call prologue packs {source, impulse, delay} into 8-byte records in
-// CSR order (the caller's edge order stays invisible) with each position's
-// destination beside it, and validates the delays.
+// CSR order (the caller's edge order stays invisible: impulse and delay are
+// first packed into one word per caller edge, so the permutation costs one
+// scattered read per position), writes each position's destination beside
+// it, and validates the delays.
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
 
 #include "ck_internal.h"
 
@@ -32,10 +40,19 @@ namespace {
 
 // flags[0]: first timestep whose update left the int32 range (INT_MAX: none)
 // flags[1]: set when a delay is outside [1, 32767]
+// flags[2]: the largest delay
 constexpr int kLifFlags = 64;
+// Spike bit rows kept for the LDS lookups: step t's row is slot t % R of the
+// ring, R = the largest delay (at most kLifRing); a workgroup holds the
+// R rows in LDS, at most kLifLdsBytes.
+constexpr int kLifRing = 16;
+constexpr int kLifLdsBytes = 128 * 1024;
+
+// Words between two bit rows: one bit per neuron, rounded up to 16 bytes.
+inline int64_t lif_row_words(int64_t N) { return ((N + 31) / 32 + 3) & ~int64_t(3); }
 
 struct LifWs {
-  size_t rec, dst, acc, v, r, flags, total;
+  size_t rec, dst, acc, v, r, bits, flags, total;
 };
 
 LifWs lif_layout(int64_t N, int64_t E) {
@@ -47,6 +64,7 @@ LifWs lif_layout(int64_t N, int64_t E) {
   w.acc = o;   o = al(o + (size_t)N * 8);
   w.v = o;     o = al(o + (size_t)N * 4);
   w.r = o;     o = al(o + (size_t)N * 4);
+  w.bits = o;  o = al(o + (size_t)kLifRing * lif_row_words(N) * 4);
   w.flags = o; o = al(o + kLifFlags * 4);
   w.total = o;
   return w;
@@ -64,31 +82,56 @@ __global__ void lif_init(const int32_t* __restrict__ v0, int64_t N, int32_t* __r
   if (i == 0) {
     flags[0] = INT_MAX;
     flags[1] = 0;
+    flags[2] = 0;
   }
 }
 
-// Record k of the CSR: {source node, impulse (low 16 bits) | delay << 16} and
-// the destination of position k (the row whose range holds k).
-__global__ void lif_pack(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-                         const int32_t* __restrict__ perm, const int16_t* __restrict__ impulses,
-                         const int32_t* __restrict__ delays, int64_t N, int64_t E,
-                         int2* __restrict__ rec, int32_t* __restrict__ dst,
-                         int32_t* __restrict__ flags) {
-  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= E) return;
-  const int32_t e = perm[k];
-  const int32_t d = delays[e];
-  if (d < 1 || d > 32767) atomicOr(&flags[1], 1);
-  const uint32_t w = (uint16_t)impulses[e];
-  rec[k] = make_int2(col_idx[k], (int)(w | ((uint32_t)(d & 0x7FFF) << 16)));
-  // last row whose start is <= k (rows without edges share their start)
-  int64_t lo = 0, hi = N;  // invariant: row_ptr[lo] <= k < row_ptr[hi]
-  while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (row_ptr[mid] <= k) lo = mid;
-    else hi = mid;
+// The impulse and delay of every edge in the caller's order packed into one
+// word, impulse (low 16 bits) | delay << 16, with the delays validated and the
+// largest one found.  Grid-stride, so the largest delay costs one atomic per
+// workgroup.
+__global__ __launch_bounds__(256) void lif_words(const int16_t* __restrict__ impulses,
+                                                 const int32_t* __restrict__ delays, int64_t E,
+                                                 uint32_t* __restrict__ words,
+                                                 int32_t* __restrict__ flags) {
+  __shared__ int32_t s_max[4];
+  int32_t dmax = 0;
+  bool bad = false;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < E;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t d = delays[e];
+    bad |= d < 1 || d > 32767;
+    dmax = max(dmax, d);
+    words[e] = (uint32_t)(uint16_t)impulses[e] | ((uint32_t)(d & 0x7FFF) << 16);
   }
-  dst[k] = (int32_t)lo;
+  if (bad) atomicOr(&flags[1], 1);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) dmax = max(dmax, __shfl_xor(dmax, off));
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = dmax;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(&flags[2], max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3])));
+}
+
+// Record k of the CSR: {source node, the word of its caller edge}: one
+// scattered 4-byte read per position.
+__global__ __launch_bounds__(256) void lif_pack(const int32_t* __restrict__ col_idx,
+                                                const int32_t* __restrict__ perm,
+                                                const uint32_t* __restrict__ words, int64_t E,
+                                                int2* __restrict__ rec) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < E) rec[k] = make_int2(col_idx[k], (int)words[perm[k]]);
+}
+
+// The destination of every CSR position: one wave per row writes the row's
+// index over its range [row_ptr[i], row_ptr[i + 1]).
+__global__ __launch_bounds__(256) void lif_rows(const int32_t* __restrict__ row_ptr, int64_t N,
+                                                int32_t* __restrict__ dst) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (i >= N) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t b = row_ptr[i], e = row_ptr[i + 1];
+  for (int32_t k = b + lane; k < e; k += 64) dst[k] = (int32_t)i;
 }
 
 __global__ __launch_bounds__(256) void lif_gather(const int2* __restrict__ rec,
@@ -120,45 +163,181 @@ __global__ __launch_bounds__(256) void lif_gather(const int2* __restrict__ rec,
     atomicAdd(reinterpret_cast<unsigned long long*>(&acc[row]), (unsigned long long)c);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts within
+// each row of 16 lanes, then the totals of the earlier rows added.
+__device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
+// lif_gather with the spike lookups in LDS: the R bit rows of steps
+// t - 1 .. t - R (zero before step 0) are copied into LDS, row d - 1 for
+// delay d, then each position tests its source's bit.  Bit rows are `ws`
+// words apart (a multiple of 4), so the copy moves 16-byte words, at most
+// kLifCopy of them per lane, all loads in flight together.  Grid-stride over
+// the positions in chunks of kLifU * 1024, each chunk's records loaded while
+// the previous chunk is summed.  Per wave and position group: the run starts
+// (lane 0 and every row change) as a ballot, the impulses summed by a prefix
+// sum (one wave's run holds at most 64 impulses, |impulse| < 2^15, so 32 bits
+// are exact), and the last lane of each run adds its run's total (the prefix
+// at the lane minus the prefix before the run's first lane) with one 64-bit
+// atomic.  Each stage runs over a lane's kLifU positions at once, so their
+// LDS reads, prefix sums and shuffles overlap.
+constexpr int kLifU = 6;
+constexpr int kLifCopy = kLifLdsBytes / 16 / 1024;
+
+__global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ rec,
+                                                      const int32_t* __restrict__ dst,
+                                                      int64_t E, int ws, int t, int R,
+                                                      const uint4* __restrict__ bits,
+                                                      long long* __restrict__ acc) {
+  extern __shared__ uint4 sb4[];  // [R][ws / 4]
+  const uint32_t* sb = reinterpret_cast<const uint32_t*>(sb4);
+  {
+    const int w4 = ws / 4, n4 = R * w4;
+    uint4 tmp[kLifCopy];
+#pragma unroll
+    for (int j = 0; j < kLifCopy; ++j) {
+      const int i = min((int)threadIdx.x + j * 1024, n4 - 1);
+      const int d = i / w4 + 1;
+      tmp[j] = bits[(size_t)((t - d + R) % R) * w4 + (i - (d - 1) * w4)];
+    }
+#pragma unroll
+    for (int j = 0; j < kLifCopy; ++j) {
+      const int i = (int)threadIdx.x + j * 1024;
+      if (i < n4) sb4[i] = t >= i / w4 + 1 ? tmp[j] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t chunk = (int64_t)kLifU * blockDim.x;
+  const int64_t stride = (int64_t)gridDim.x * chunk;
+  int2 x[kLifU];
+  int row[kLifU];
+  int64_t base = (int64_t)blockIdx.x * chunk;
+#pragma unroll
+  for (int j = 0; j < kLifU; ++j) {
+    const int64_t k = std::min<int64_t>(base + j * blockDim.x + threadIdx.x, E - 1);
+    x[j] = rec[k];
+    row[j] = dst[k];
+  }
+  for (; base < E; base += stride) {
+    // the next chunk's records (clamped into range: the loads are unconditional)
+    int2 xn[kLifU];
+    int rn[kLifU];
+#pragma unroll
+    for (int j = 0; j < kLifU; ++j) {
+      const int64_t k = std::min<int64_t>(base + stride + j * blockDim.x + threadIdx.x, E - 1);
+      xn[j] = rec[k];
+      rn[j] = dst[k];
+    }
+    bool live[kLifU];
+    int c[kLifU], rj[kLifU], prev[kLifU], P[kLifU], first[kLifU], before[kLifU];
+    uint32_t w[kLifU];
+    unsigned long long B[kLifU];
+#pragma unroll
+    for (int j = 0; j < kLifU; ++j) {
+      live[j] = base + j * blockDim.x + threadIdx.x < E;
+      rj[j] = live[j] ? row[j] : -1;
+      const uint32_t y = (uint32_t)x[j].y, src = (uint32_t)x[j].x;
+      w[j] = sb[(int)(y >> 16) * ws - ws + (int)(src >> 5)];
+    }
+#pragma unroll
+    for (int j = 0; j < kLifU; ++j) {
+      const uint32_t src = (uint32_t)x[j].x;
+      c[j] = live[j] && ((w[j] >> (src & 31)) & 1u) ? (int)(int16_t)(x[j].y & 0xFFFF) : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kLifU; ++j) prev[j] = __shfl_up(rj[j], 1);
+#pragma unroll
+    for (int j = 0; j < kLifU; ++j) P[j] = wave_prefix_sum(c[j], lane);
+#pragma unroll
+    for (int j = 0; j < kLifU; ++j) {
+      B[j] = __ballot(lane == 0 || prev[j] != rj[j]);  // run starts
+      first[j] = 63 - __clzll(B[j] & (~0ull >> (63 - lane)));
+    }
+#pragma unroll
+    for (int j = 0; j < kLifU; ++j) before[j] = __shfl(P[j], first[j] > 0 ? first[j] - 1 : 0);
+#pragma unroll
+    for (int j = 0; j < kLifU; ++j) {
+      const int sum = P[j] - (first[j] > 0 ? before[j] : 0);
+      const bool last = lane == 63 || (((B[j] >> lane) >> 1) & 1ull) != 0;
+      if (rj[j] >= 0 && last && sum != 0)
+        atomicAdd(reinterpret_cast<unsigned long long*>(&acc[rj[j]]),
+                  (unsigned long long)(long long)sum);
+    }
+#pragma unroll
+    for (int j = 0; j < kLifU; ++j) {
+      x[j] = xn[j];
+      row[j] = rn[j];
+    }
+  }
+}
+
 struct LifParams {
   int32_t threshold, reset, refractory, nshift;
   int32_t shift[8];
 };
 
+// With bits set (the LDS lookups are in use), the step's spikes also go into
+// slot t % R of the bit ring (slots ws words apart): one ballot per wave, bit
+// i % 32 of word i / 32 for neuron i.  Every lane takes part in the ballot, so no lane returns early.
 __global__ __launch_bounds__(256) void lif_update(int64_t N, int t, LifParams p,
                                                   long long* __restrict__ acc,
                                                   int32_t* __restrict__ v, int32_t* __restrict__ r,
                                                   uint8_t* __restrict__ spikes,
                                                   int32_t* __restrict__ potentials,
-                                                  int32_t* __restrict__ flags) {
+                                                  uint32_t* __restrict__ bits, int64_t ws,
+                                                  int R, int32_t* __restrict__ flags) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= N) return;
-  const long long in = acc[i];
-  acc[i] = 0;
-  int32_t vi = v[i];
-  int32_t ri = r[i];
   uint8_t s = 0;
-  if (ri > 0) {
-    ri -= 1;  // refractory: the arriving impulses are dropped
-  } else {
-    // arithmetic right shift of a signed int32 = floor division by 2^k
-    for (int j = 0; j < p.nshift; ++j) vi -= vi >> p.shift[j];
-    const long long x = (long long)vi + in;
-    if (x < INT_MIN || x > INT_MAX) atomicMin(&flags[0], t);
-    vi = (int32_t)x;
-    if (vi >= p.threshold) {
-      s = 1;
-      vi = p.reset;
-      ri = p.refractory;
+  if (i < N) {
+    const long long in = acc[i];
+    acc[i] = 0;
+    int32_t vi = v[i];
+    int32_t ri = r[i];
+    if (ri > 0) {
+      ri -= 1;  // refractory: the arriving impulses are dropped
+    } else {
+      // arithmetic right shift of a signed int32 = floor division by 2^k
+      for (int j = 0; j < p.nshift; ++j) vi -= vi >> p.shift[j];
+      const long long x = (long long)vi + in;
+      if (x < INT_MIN || x > INT_MAX) atomicMin(&flags[0], t);
+      vi = (int32_t)x;
+      if (vi >= p.threshold) {
+        s = 1;
+        vi = p.reset;
+        ri = p.refractory;
+      }
     }
+    v[i] = vi;
+    r[i] = ri;
+    spikes[(size_t)t * N + i] = s;
+    potentials[(size_t)t * N + i] = vi;
   }
-  v[i] = vi;
-  r[i] = ri;
-  spikes[(size_t)t * N + i] = s;
-  potentials[(size_t)t * N + i] = vi;
+  if (bits != nullptr) {
+    const unsigned long long m = __ballot(s != 0);
+    const int lane = threadIdx.x & 63;
+    const int64_t wd = i >> 5;  // lanes 0 and 32 start a word
+    if ((lane & 31) == 0 && wd < (N + 31) / 32)
+      bits[(size_t)(t % R) * ws + wd] = (uint32_t)(lane != 0 ? (m >> 32) : m);
+  }
 }
 
 inline unsigned blocks(int64_t n) { return (unsigned)std::max<int64_t>(1, (n + 255) / 256); }
+
+// CK_LIF_LDS=0 in the environment keeps the byte lookups (lif_gather) for
+// every run; read on each call.
+bool lif_lds_enabled() {
+  const char* e = std::getenv("CK_LIF_LDS");
+  return !(e && e[0] == '0' && e[1] == 0);
+}
 
 }  // namespace
 }  // namespace ckhip
@@ -224,30 +403,64 @@ extern "C" ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const
   int32_t* v = reinterpret_cast<int32_t*>(wsb + ws.v);
   int32_t* r = reinterpret_cast<int32_t*>(wsb + ws.r);
   int32_t* flags = reinterpret_cast<int32_t*>(wsb + ws.flags);
+  uint32_t* bitring = reinterpret_cast<uint32_t*>(wsb + ws.bits);
   lif_init<<<blocks(N), 256, 0, stream>>>(v0, N, v, r, acc, flags);
-  if (E > 0)
-    lif_pack<<<blocks(E), 256, 0, stream>>>(g->row_ptr, g->col_idx, g->perm, impulses, delays, N,
-                                            E, rec, dst, flags);
+  // The delays are validated, and the largest one read back, before the
+  // first step: it picks the lookup (LDS bit rows when they fit).
+  int R = 0;
+  if (E > 0) {
+    // the caller-order words live in dst's region until lif_rows fills it
+    uint32_t* words = reinterpret_cast<uint32_t*>(dst);
+    lif_words<<<std::min(blocks(E), 4096u), 256, 0, stream>>>(impulses, delays, E, words, flags);
+    lif_pack<<<blocks(E), 256, 0, stream>>>(g->col_idx, g->perm, words, E, rec);
+    lif_rows<<<blocks(N * 64), 256, 0, stream>>>(g->row_ptr, N, dst);
+    CK_HIP_TRY(hipGetLastError());
+    int32_t fl[3] = {0, 0, 0};
+    CK_HIP_TRY(hipMemcpyAsync(fl, flags, sizeof(fl), hipMemcpyDeviceToHost, stream));
+    CK_HIP_TRY(hipStreamSynchronize(stream));
+    if (fl[1]) {
+      set_error("an edge delay is outside [1, 32767]");
+      return CK_ERR_BAD_VALUE;
+    }
+    if (fl[2] >= 1 && fl[2] <= kLifRing && (int64_t)fl[2] * lif_row_words(N) * 4 <= kLifLdsBytes &&
+        lif_lds_enabled())
+      R = fl[2];
+  }
+  const int64_t wsw = lif_row_words(N);
+  const int lds = R > 0 ? (int)(R * wsw * 4) : 0;
+  unsigned lds_grid = 0;
+  if (R > 0) {
+    CK_HIP_TRY(hipFuncSetAttribute((const void*)lif_gather_lds,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+    int cus = 0;
+    CK_HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, g->device));
+    const int per_cu = lds <= 80 * 1024 ? 2 : 1;  // workgroups whose LDS fits a 160 KB CU
+    const int64_t chunks = (E + (int64_t)kLifU * 1024 - 1) / ((int64_t)kLifU * 1024);
+    lds_grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((int64_t)cus * per_cu, chunks));
+  }
   for (int64_t t = 0; t < T; ++t) {
     if (t >= 1 && E > 0) {
       rc = timed_launch(g_profile.lif_gather, stream, [&] {
-        lif_gather<<<blocks(E), 256, 0, stream>>>(rec, dst, E, N, (int)t, spikes, acc);
+        if (R > 0)
+          lif_gather_lds<<<lds_grid, 1024, lds, stream>>>(rec, dst, E, (int)wsw, (int)t, R,
+                                                          reinterpret_cast<const uint4*>(bitring),
+                                                          acc);
+        else
+          lif_gather<<<blocks(E), 256, 0, stream>>>(rec, dst, E, N, (int)t, spikes, acc);
       });
       if (rc != CK_OK) return rc;
     }
     rc = timed_launch(g_profile.lif_update, stream, [&] {
-      lif_update<<<blocks(N), 256, 0, stream>>>(N, (int)t, p, acc, v, r, spikes, potentials, flags);
+      lif_update<<<blocks(N), 256, 0, stream>>>(N, (int)t, p, acc, v, r, spikes, potentials,
+                                               R > 0 ? bitring : nullptr, wsw, std::max(R, 1),
+                                               flags);
     });
     if (rc != CK_OK) return rc;
   }
   CK_HIP_TRY(hipGetLastError());
-  int32_t fl[2] = {0, 0};
+  int32_t fl[1] = {0};
   CK_HIP_TRY(hipMemcpyAsync(fl, flags, sizeof(fl), hipMemcpyDeviceToHost, stream));
   CK_HIP_TRY(hipStreamSynchronize(stream));
-  if (fl[1]) {
-    set_error("an edge delay is outside [1, 32767]");
-    return CK_ERR_BAD_VALUE;
-  }
   if (fl[0] != INT_MAX) {
     if (overflow_step) *overflow_step = fl[0];
     set_error("a membrane potential left the int32 range at timestep %d; the run is rejected "

@@ -70,6 +70,60 @@ def test_random_graphs(seed, N, E, max_delay, refr, shifts, active):
     assert (s[10:].sum() > 0) == active
 
 
+def _random_case(seed, N, E, max_delay, T=20, refr=2, shifts=(2,)):
+    rng = np.random.default_rng(seed)
+    src, dst = rng.integers(0, N, E), rng.integers(0, N, E)
+    w = (np.where(rng.random(E) < 0.8, 1, -1) * rng.integers(1, 120, E)).astype(np.int16)
+    d = rng.integers(1, max_delay + 1, E).astype(np.int32)
+    v0 = rng.integers(-200, 600, N).astype(np.int32)
+    return _both(src, dst, N, w, d, v0, T, 100, -20, refr, list(shifts))
+
+
+@pytest.mark.parametrize("seed,N,E,max_delay", [
+    (11, 33, 700, 2), (12, 65, 2000, 16), (13, 300, 9000, 9), (14, 2000, 60000, 7)])
+def test_byte_lookups_match(seed, N, E, max_delay, monkeypatch):
+    """The same runs with the spike lookups forced to one byte read of the
+    spike history per edge (CK_LIF_LDS=0) instead of LDS bit rows."""
+    monkeypatch.setenv("CK_LIF_LDS", "0")
+    log(f"LIF: byte lookups, N={N} E={E} delays<={max_delay}")
+    s = _random_case(seed, N, E, max_delay)
+    assert s[10:].sum() > 0
+
+
+@pytest.mark.parametrize("seed,N,E,max_delay,T", [
+    (21, 33, 700, 2, 20),          # ragged last ballot word (N = 32 + 1)
+    (22, 65, 2000, 16, 40),        # the longest delay the bit ring holds
+    (23, 400, 8000, 17, 40),       # one step past it: byte lookups
+    (24, 600, 9000, 40, 60),       # delays far past it
+    (25, 262144, 1000000, 4, 8),   # 4 bit rows of 8,192 words: exactly 128 KB of LDS
+    (26, 262176, 1000000, 4, 8)])  # one word more per row: byte lookups
+def test_lookup_boundaries(seed, N, E, max_delay, T):
+    """Cases on both sides of the limits that pick the spike lookup (largest
+    delay 16, 128 KB of bit rows), bit-exact against the oracle."""
+    log(f"LIF: lookup boundary N={N} E={E} delays<={max_delay} T={T}")
+    s = _random_case(seed, N, E, max_delay, T=T)
+    assert s[1:].sum() > 0
+
+
+@pytest.mark.parametrize("gap", [2, 63, 4096])
+def test_empty_row_gaps(gap):
+    """In-edges into rows 0, gap, 2 gap, 2 gap + 2 and 3 gap + 2 only: long
+    runs of rows without edges between the rows whose runs a wave sums."""
+    rng = np.random.default_rng(gap)
+    rows = np.array([0, gap, 2 * gap, 2 * gap + 2, 3 * gap + 2], np.int64)
+    N = int(rows[-1]) + 10
+    E = 5000
+    dst = rows[rng.integers(0, rows.size, E)]
+    src = np.concatenate([rows, rng.integers(0, N, E - rows.size)])
+    w = (np.where(rng.random(E) < 0.8, 1, -1) * rng.integers(1, 120, E)).astype(np.int16)
+    d = rng.integers(1, 5, E).astype(np.int32)
+    v0 = rng.integers(-200, 600, N).astype(np.int32)
+    v0[rows] = 500
+    log(f"LIF: empty-row gap {gap}")
+    s = _both(src, dst, N, w, d, v0, 12, 100, -20, 1, [2])
+    assert s[1:, rows].sum() > 0
+
+
 @pytest.fixture(scope="module")
 def connectome():
     w = synthetic.make_lif("connectome")
