@@ -150,8 +150,10 @@ def lif_bench(args, torch, sgr, synthetic, np):
     """One LIF forward = T timesteps on the synthetic whole-connectome graph.
     value = edge-visits/s = E * T / t_forward; roofline of the per-step gather
     kernel against HBM: algorithmic bytes per launch = 12 E (8-byte edge record
-    and 4-byte destination per CSR position) + 9 N (the spike row read, the
-    64-bit accumulators written) over its mean launch time."""
+    and 4-byte destination per CSR position) + 8 N (the 64-bit accumulators
+    written) + the spike lookups (the R = 4 bit rows of ceil(N / 32) words the
+    delays reach on the LDS path, one byte row of N otherwise) over its mean
+    launch time."""
     w = synthetic.make_lif("connectome", max_delay=4, v0_range=(0, 60))
     N, E, T = w.num_nodes, w.src.size, LIF_RUN["T"]
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -182,7 +184,10 @@ def lif_bench(args, torch, sgr, synthetic, np):
     prof = sgr.profile_collect_lif()
     gather_us = 1e3 * prof["gather_ms"] / max(1, prof["gather_launches"])
     update_us = 1e3 * prof["update_ms"] / max(1, prof["update_launches"])
-    per_launch = 12 * E + 9 * N
+    maxd = int(w.delays.max())
+    row_words = ((N + 31) // 32 + 3) // 4 * 4
+    lds_path = maxd <= 16 and maxd * row_words * 4 <= 128 * 1024 and os.environ.get("CK_LIF_LDS") != "0"
+    per_launch = 12 * E + 8 * N + (maxd * row_words * 4 if lds_path else N)
     ach = per_launch / (gather_us * 1e-6) / 1e9
     res = {"metric": "LIF forward: ms per timestep & edge-visits/s, synthetic whole-connectome "
                      "graph N=211,577 E=24,678,466; HBM GB/s",
@@ -198,7 +203,8 @@ def lif_bench(args, torch, sgr, synthetic, np):
            "kernels": {"gather_launch_us": gather_us, "update_launch_us": update_us,
                        "gather_launches_per_forward": prof["gather_launches"] // args.steps,
                        "update_launches_per_forward": prof["update_launches"] // args.steps},
-           "roofline": {"bound": "hbm", "kernel": "lif_gather", "achieved": ach,
+           "roofline": {"bound": "hbm", "kernel": "lif_gather_lds" if lds_path else "lif_gather",
+                        "achieved": ach,
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                         "traffic": None}}
     if not args.no_cpu:
