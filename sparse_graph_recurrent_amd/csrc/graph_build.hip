@@ -105,28 +105,104 @@ __global__ __launch_bounds__(kRsThreads) void rs_histogram(const uint64_t* __res
   if (threadIdx.x < kRsRadix) hist[threadIdx.x * nblocks + blockIdx.x] = cnt[threadIdx.x];
 }
 
-// Exclusive scan of m uint32 values in place; one workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void exclusive_scan_u32(uint32_t* __restrict__ data, int64_t m) {
-  __shared__ uint32_t part[1024];
+// Exclusive scan of m uint32 values in place, in tiles of kScanTile values
+// (256 threads x 16 consecutive values): scan_tile_sums writes each tile's
+// total, scan_small scans those totals in one workgroup, scan_tiles scans
+// every tile from its total's prefix.  Every load is of 16 consecutive values.
+constexpr int kScanPer = 16;
+constexpr int kScanTile = 256 * kScanPer;
+
+__device__ __forceinline__ void scan_load(const uint32_t* data, int64_t m, int64_t b,
+                                          uint32_t (&x)[kScanPer]) {
+  if (b + kScanPer <= m) {
+    const uint4* q = reinterpret_cast<const uint4*>(data + b);
+#pragma unroll
+    for (int i = 0; i < kScanPer / 4; ++i) {
+      const uint4 v = q[i];
+      x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) x[i] = b + i < m ? data[b + i] : 0u;
+  }
+}
+
+// Exclusive scan over the 256 threads of a workgroup of one value each.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh) {
   const int t = threadIdx.x;
-  const int64_t chunk = (m + 1023) / 1024;
-  const int64_t b = std::min<int64_t>(m, (int64_t)t * chunk);
-  const int64_t e = std::min<int64_t>(m, b + chunk);
-  uint32_t s = 0;
-  for (int64_t i = b; i < e; ++i) s += data[i];
-  part[t] = s;
+  sh[t] = v;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    uint32_t add = t >= off ? part[t - off] : 0u;
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t add = t >= off ? sh[t - off] : 0u;
     __syncthreads();
-    part[t] += add;
+    sh[t] += add;
     __syncthreads();
   }
-  uint32_t run = t ? part[t - 1] : 0u;
+  const uint32_t r = t ? sh[t - 1] : 0u;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void scan_tile_sums(const uint32_t* __restrict__ data,
+                                                      int64_t m, uint32_t* __restrict__ sums) {
+  __shared__ uint32_t sh[256];
+  const int64_t b = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanPer;
+  uint32_t x[kScanPer];
+  scan_load(data, m, b, x);
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) s += x[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) sh[threadIdx.x] += sh[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sums[blockIdx.x] = sh[0];
+}
+
+// Exclusive scan of n values in one workgroup of 256 threads (n up to a few
+// thousand: each thread takes a contiguous run).
+__global__ __launch_bounds__(256) void scan_small(uint32_t* __restrict__ v, int64_t n) {
+  __shared__ uint32_t sh[256];
+  const int64_t chunk = (n + 255) / 256;
+  const int64_t b = std::min<int64_t>(n, (int64_t)threadIdx.x * chunk);
+  const int64_t e = std::min<int64_t>(n, b + chunk);
+  uint32_t s = 0;
+  for (int64_t i = b; i < e; ++i) s += v[i];
+  uint32_t run = block_exclusive_scan(s, sh);
   for (int64_t i = b; i < e; ++i) {
-    uint32_t x = data[i];
-    data[i] = run;
+    const uint32_t x = v[i];
+    v[i] = run;
     run += x;
+  }
+}
+
+__global__ __launch_bounds__(256) void scan_tiles(uint32_t* __restrict__ data, int64_t m,
+                                                  const uint32_t* __restrict__ sums) {
+  __shared__ uint32_t sh[256];
+  const int64_t b = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanPer;
+  uint32_t x[kScanPer];
+  scan_load(data, m, b, x);
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) s += x[i];
+  uint32_t run = sums[blockIdx.x] + block_exclusive_scan(s, sh);
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    const uint32_t c = x[i];
+    x[i] = run;
+    run += c;
+  }
+  if (b + kScanPer <= m) {
+    uint4* q = reinterpret_cast<uint4*>(data + b);
+#pragma unroll
+    for (int i = 0; i < kScanPer / 4; ++i)
+      q[i] = make_uint4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i)
+      if (b + i < m) data[b + i] = x[i];
   }
 }
 
@@ -231,25 +307,30 @@ ck_status build_compressed(const int64_t* major, const int64_t* minor, int64_t E
   uint64_t *k0 = nullptr, *k1 = nullptr;
   int32_t *v0 = nullptr, *v1 = nullptr;
   uint32_t* hist = nullptr;
+  // the histogram (digit-major, nblocks per digit) and its tile totals
+  const int64_t ntiles = (nblocks * kRsRadix + kScanTile - 1) / kScanTile;
   auto cleanup = [&]() {
     (void)hipFree(k0); (void)hipFree(k1); (void)hipFree(v0); (void)hipFree(v1);
     (void)hipFree(hist);
   };
   if (hipMalloc(&k0, E * 8) != hipSuccess || hipMalloc(&k1, E * 8) != hipSuccess ||
       hipMalloc(&v0, E * 4) != hipSuccess || hipMalloc(&v1, E * 4) != hipSuccess ||
-      hipMalloc(&hist, nblocks * kRsRadix * 4) != hipSuccess) {
+      hipMalloc(&hist, (nblocks * kRsRadix + ntiles) * 4) != hipSuccess) {
     cleanup();
     (void)hipGetLastError();
     set_error("device allocation of %lld bytes of sort scratch failed", (long long)(E * 24));
     return CK_ERR_NOMEM;
   }
+  uint32_t* tsum = hist + nblocks * kRsRadix;
   make_keys<<<grid_for(E, 256), 256, 0, st>>>(major, minor, E, N, k0, v0);
   const uint64_t maxkey = (uint64_t)N * (uint64_t)N - 1;
   int bits = 0;
   while (bits < 64 && (maxkey >> bits) != 0) ++bits;
   for (int shift = 0; shift < bits; shift += 4) {
     rs_histogram<<<(unsigned)nblocks, kRsThreads, 0, st>>>(k0, E, shift, hist, nblocks);
-    exclusive_scan_u32<<<1, 1024, 0, st>>>(hist, nblocks * kRsRadix);
+    scan_tile_sums<<<(unsigned)ntiles, 256, 0, st>>>(hist, nblocks * kRsRadix, tsum);
+    scan_small<<<1, 256, 0, st>>>(tsum, ntiles);
+    scan_tiles<<<(unsigned)ntiles, 256, 0, st>>>(hist, nblocks * kRsRadix, tsum);
     rs_scatter<<<(unsigned)nblocks, kRsThreads, 0, st>>>(k0, v0, k1, v1, E, shift, hist, nblocks);
     std::swap(k0, k1);
     std::swap(v0, v1);
