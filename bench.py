@@ -149,11 +149,11 @@ LIF_RUN = dict(T=16, threshold=40, reset=0, refractory_steps=2, decay_shifts=[2]
 def lif_bench(args, torch, sgr, synthetic, np):
     """One LIF forward = T timesteps on the synthetic whole-connectome graph.
     value = edge-visits/s = E * T / t_forward; roofline of the per-step gather
-    kernel against HBM: algorithmic bytes per launch = 12 E (8-byte edge record
-    and 4-byte destination per CSR position) + 8 N (the 64-bit accumulators
-    written) + the spike lookups (the R = 4 bit rows of ceil(N / 32) words the
-    delays reach on the LDS path, one byte row of N otherwise) over its mean
-    launch time."""
+    kernel against HBM: algorithmic bytes per launch, over its mean launch
+    time = on the LDS-lookup path 8 E (the 8-byte record of every CSR position,
+    its row inside) + 8 N (the 64-bit accumulators written) + the R = 4 bit
+    rows of ceil(N / 32) words the delays reach; on the byte-lookup path 12 E
+    (record and 4-byte destination) + 8 N + one byte row of N."""
     w = synthetic.make_lif("connectome", max_delay=4, v0_range=(0, 60))
     N, E, T = w.num_nodes, w.src.size, LIF_RUN["T"]
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -187,7 +187,7 @@ def lif_bench(args, torch, sgr, synthetic, np):
     maxd = int(w.delays.max())
     row_words = ((N + 31) // 32 + 3) // 4 * 4
     lds_path = maxd <= 16 and maxd * row_words * 4 <= 128 * 1024 and os.environ.get("CK_LIF_LDS") != "0"
-    per_launch = 12 * E + 8 * N + (maxd * row_words * 4 if lds_path else N)
+    per_launch = (8 * E + 8 * N + maxd * row_words * 4) if lds_path else (12 * E + 9 * N)
     ach = per_launch / (gather_us * 1e-6) / 1e9
     res = {"metric": "LIF forward: ms per timestep & edge-visits/s, synthetic whole-connectome "
                      "graph N=211,577 E=24,678,466; HBM GB/s",

@@ -20,15 +20,17 @@
 //                When the bit rows of the steps the delays reach fit in LDS
 //                (lif_gather_lds), each workgroup first copies them there and
 //                looks the spikes up in LDS instead of one scattered byte
-//                read per edge, and sums the runs with DPP prefix sums.
+//                read per edge, reads 8-byte records that carry the row
+//                (no separate destination), and sums the runs with DPP
+//                prefix sums.
 //   lif_update   one thread per neuron: the state update above; writes the
 //                step's spikes and potentials (and the step's spike bits into
 //                a ring of kLifRing bit rows), clears I.
-// A per-call prologue packs {source, impulse, delay} into 8-byte records in
-// CSR order (the caller's edge order stays invisible: impulse and delay are
-// first packed into one word per caller edge, so the permutation costs one
-// scattered read per position), writes each position's destination beside
-// it, and validates the delays.
+// A per-call prologue validates the delays, writes each position's
+// destination, and packs {source, impulse, delay} (and, for the LDS lookups,
+// the destination) into 8-byte records in CSR order (the caller's edge order
+// stays invisible: impulse and delay are first packed into one word per
+// caller edge, so the permutation costs one scattered read per position).
 #include <algorithm>
 #include <climits>
 #include <cstdlib>
@@ -52,7 +54,7 @@ constexpr int kLifLdsBytes = 128 * 1024;
 inline int64_t lif_row_words(int64_t N) { return ((N + 31) / 32 + 3) & ~int64_t(3); }
 
 struct LifWs {
-  size_t rec, dst, acc, v, r, bits, flags, total;
+  size_t rec, dst, words, acc, v, r, bits, flags, total;
 };
 
 LifWs lif_layout(int64_t N, int64_t E) {
@@ -61,6 +63,7 @@ LifWs lif_layout(int64_t N, int64_t E) {
   size_t o = 0;
   w.rec = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 8);
   w.dst = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 4);
+  w.words = o; o = al(o + (size_t)std::max<int64_t>(E, 1) * 4);
   w.acc = o;   o = al(o + (size_t)N * 8);
   w.v = o;     o = al(o + (size_t)N * 4);
   w.r = o;     o = al(o + (size_t)N * 4);
@@ -121,6 +124,24 @@ __global__ __launch_bounds__(256) void lif_pack(const int32_t* __restrict__ col_
                                                 int2* __restrict__ rec) {
   const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k < E) rec[k] = make_int2(col_idx[k], (int)words[perm[k]]);
+}
+
+// The records of the LDS-lookup path (every such graph has N <= 2^20 nodes:
+// its bit rows fit 128 KB, and the largest delay is at most 16), with the
+// destination inside: x = source (bits 0-19) | row bits 0-11 (bits 20-31),
+// y = impulse (bits 0-15) | delay - 1 (bits 16-19) | row bits 12-23 (bits
+// 20-31).  The per-step gather then reads 8 bytes per position.
+__global__ __launch_bounds__(256) void lif_pack_lds(const int32_t* __restrict__ col_idx,
+                                                    const int32_t* __restrict__ perm,
+                                                    const uint32_t* __restrict__ words,
+                                                    const int32_t* __restrict__ dst, int64_t E,
+                                                    int2* __restrict__ rec) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= E) return;
+  const uint32_t w = words[perm[k]], row = (uint32_t)dst[k];
+  const uint32_t x = (uint32_t)col_idx[k] | (row & 0xFFFu) << 20;
+  const uint32_t y = (w & 0xFFFFu) | ((w >> 16) - 1u) << 16 | (row >> 12) << 20;
+  rec[k] = make_int2((int)x, (int)y);
 }
 
 // The destination of every CSR position: one wave per row writes the row's
@@ -193,7 +214,6 @@ constexpr int kLifU = 6;
 constexpr int kLifCopy = kLifLdsBytes / 16 / 1024;
 
 __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ rec,
-                                                      const int32_t* __restrict__ dst,
                                                       int64_t E, int ws, int t, int R,
                                                       const uint4* __restrict__ bits,
                                                       long long* __restrict__ acc) {
@@ -219,24 +239,16 @@ __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ 
   const int64_t chunk = (int64_t)kLifU * blockDim.x;
   const int64_t stride = (int64_t)gridDim.x * chunk;
   int2 x[kLifU];
-  int row[kLifU];
   int64_t base = (int64_t)blockIdx.x * chunk;
 #pragma unroll
-  for (int j = 0; j < kLifU; ++j) {
-    const int64_t k = std::min<int64_t>(base + j * blockDim.x + threadIdx.x, E - 1);
-    x[j] = rec[k];
-    row[j] = dst[k];
-  }
+  for (int j = 0; j < kLifU; ++j)
+    x[j] = rec[std::min<int64_t>(base + j * blockDim.x + threadIdx.x, E - 1)];
   for (; base < E; base += stride) {
     // the next chunk's records (clamped into range: the loads are unconditional)
     int2 xn[kLifU];
-    int rn[kLifU];
 #pragma unroll
-    for (int j = 0; j < kLifU; ++j) {
-      const int64_t k = std::min<int64_t>(base + stride + j * blockDim.x + threadIdx.x, E - 1);
-      xn[j] = rec[k];
-      rn[j] = dst[k];
-    }
+    for (int j = 0; j < kLifU; ++j)
+      xn[j] = rec[std::min<int64_t>(base + stride + j * blockDim.x + threadIdx.x, E - 1)];
     bool live[kLifU];
     int c[kLifU], rj[kLifU], prev[kLifU], P[kLifU], first[kLifU], before[kLifU];
     uint32_t w[kLifU];
@@ -244,13 +256,13 @@ __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ 
 #pragma unroll
     for (int j = 0; j < kLifU; ++j) {
       live[j] = base + j * blockDim.x + threadIdx.x < E;
-      rj[j] = live[j] ? row[j] : -1;
-      const uint32_t y = (uint32_t)x[j].y, src = (uint32_t)x[j].x;
-      w[j] = sb[(int)(y >> 16) * ws - ws + (int)(src >> 5)];
+      const uint32_t xx = (uint32_t)x[j].x, y = (uint32_t)x[j].y;
+      rj[j] = live[j] ? (int)((xx >> 20) | (y >> 20) << 12) : -1;
+      w[j] = sb[(int)((y >> 16) & 15u) * ws + (int)((xx & 0xFFFFFu) >> 5)];
     }
 #pragma unroll
     for (int j = 0; j < kLifU; ++j) {
-      const uint32_t src = (uint32_t)x[j].x;
+      const uint32_t src = (uint32_t)x[j].x;  // (bits 0-4 of the source)
       c[j] = live[j] && ((w[j] >> (src & 31)) & 1u) ? (int)(int16_t)(x[j].y & 0xFFFF) : 0;
     }
 #pragma unroll
@@ -273,10 +285,7 @@ __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ 
                   (unsigned long long)(long long)sum);
     }
 #pragma unroll
-    for (int j = 0; j < kLifU; ++j) {
-      x[j] = xn[j];
-      row[j] = rn[j];
-    }
+    for (int j = 0; j < kLifU; ++j) x[j] = xn[j];
   }
 }
 
@@ -399,6 +408,7 @@ extern "C" ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const
   char* wsb = static_cast<char*>(workspace);
   int2* rec = reinterpret_cast<int2*>(wsb + ws.rec);
   int32_t* dst = reinterpret_cast<int32_t*>(wsb + ws.dst);
+  uint32_t* words = reinterpret_cast<uint32_t*>(wsb + ws.words);
   long long* acc = reinterpret_cast<long long*>(wsb + ws.acc);
   int32_t* v = reinterpret_cast<int32_t*>(wsb + ws.v);
   int32_t* r = reinterpret_cast<int32_t*>(wsb + ws.r);
@@ -409,10 +419,7 @@ extern "C" ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const
   // first step: it picks the lookup (LDS bit rows when they fit).
   int R = 0;
   if (E > 0) {
-    // the caller-order words live in dst's region until lif_rows fills it
-    uint32_t* words = reinterpret_cast<uint32_t*>(dst);
     lif_words<<<std::min(blocks(E), 4096u), 256, 0, stream>>>(impulses, delays, E, words, flags);
-    lif_pack<<<blocks(E), 256, 0, stream>>>(g->col_idx, g->perm, words, E, rec);
     lif_rows<<<blocks(N * 64), 256, 0, stream>>>(g->row_ptr, N, dst);
     CK_HIP_TRY(hipGetLastError());
     int32_t fl[3] = {0, 0, 0};
@@ -422,9 +429,15 @@ extern "C" ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const
       set_error("an edge delay is outside [1, 32767]");
       return CK_ERR_BAD_VALUE;
     }
+    // (the 128 KB bound implies N <= 2^20, which the 20-bit sources and rows
+    // of lif_pack_lds need; it is checked on its own all the same)
     if (fl[2] >= 1 && fl[2] <= kLifRing && (int64_t)fl[2] * lif_row_words(N) * 4 <= kLifLdsBytes &&
-        lif_lds_enabled())
+        N <= (int64_t(1) << 20) && lif_lds_enabled())
       R = fl[2];
+    if (R > 0)
+      lif_pack_lds<<<blocks(E), 256, 0, stream>>>(g->col_idx, g->perm, words, dst, E, rec);
+    else
+      lif_pack<<<blocks(E), 256, 0, stream>>>(g->col_idx, g->perm, words, E, rec);
   }
   const int64_t wsw = lif_row_words(N);
   const int lds = R > 0 ? (int)(R * wsw * 4) : 0;
@@ -442,7 +455,7 @@ extern "C" ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const
     if (t >= 1 && E > 0) {
       rc = timed_launch(g_profile.lif_gather, stream, [&] {
         if (R > 0)
-          lif_gather_lds<<<lds_grid, 1024, lds, stream>>>(rec, dst, E, (int)wsw, (int)t, R,
+          lif_gather_lds<<<lds_grid, 1024, lds, stream>>>(rec, E, (int)wsw, (int)t, R,
                                                           reinterpret_cast<const uint4*>(bitring),
                                                           acc);
         else
