@@ -342,11 +342,12 @@ def main():
     fwd_b, bwd_b, Q = algorithmic_bytes(N, E, n_in, B, T, M)
     # a step's S microsteps of forward (backward) bytes are spread over its
     # forward (backward) launches: S + 1 per-microstep backward launches (the
-    # first has no edge pass), one resident launch per direction, or on the
-    # blocked path the part and epilogue launches of each microstep together
-    # (2 S forward, 2 S + 1 backward)
-    names = {"resident": ("res_fwd", "res_bwd"), "blocked": ("blk_fwd", "blk_bwd")}.get(
-        path, ("fwd_step", "bwd_step"))
+    # first has no edge pass), one resident launch per direction, or for the
+    # blocked kernels the part and epilogue launches of each microstep
+    # together (2 S forward, 2 S + 1 backward); the "blocked" path pairs the
+    # blocked forward with the per-microstep backward
+    names = {"resident": ("res_fwd", "res_bwd"), "blocked": ("blk_fwd", "bwd_step"),
+             "blocked_both": ("blk_fwd", "blk_bwd")}.get(path, ("fwd_step", "bwd_step"))
     per_kernel = {}
     for kname, per_b, us in ((names[0], fwd_b * S / fwd_n, fwd_us),
                              (names[1], bwd_b * S / bwd_n, bwd_us)):

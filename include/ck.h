@@ -87,7 +87,8 @@ typedef enum {
  * ck_recurrence_path), which run a whole forward or backward in one launch.
  * When the device's compute units are a multiple of 8 and num_nodes is at
  * least 100000 (or the environment variable CK_BLOCKED is "1" at creation;
- * "0" turns this off), it plans the blocked kernels (ck_recurrence_path).
+ * "0" turns this off), it plans the blocked forward kernels; with CK_BLOCKED
+ * "2" it plans the blocked kernels of both directions (ck_recurrence_path).
  * The caller's edge order is kept for edge values and their gradient: the
  * permutation is invisible outside.  Validation failures return
  * CK_ERR_BAD_SIZE, CK_ERR_TOO_LARGE, CK_ERR_NULL_ARG, CK_ERR_INDEX_RANGE or
@@ -132,9 +133,11 @@ ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int64_t micros
 
 /*
  * Which kernels a call with batch B runs on this graph: *path = 1 for the
- * XCD-resident kernels, 2 for the blocked kernels, 0 for the per-microstep
- * kernels.  The resident kernels are taken whenever the graph has their
- * plans; else the blocked kernels when the graph has theirs and 5 <= B <= 64.
+ * XCD-resident kernels, 2 for the blocked forward (with the per-microstep
+ * backward), 3 for the blocked kernels in both directions, 0 for the
+ * per-microstep kernels.  The resident kernels are taken whenever the graph
+ * has their plans; else the blocked kernels when the graph has theirs and
+ * 5 <= B <= 64.
  *
  * Per-microstep kernels: one fused launch per microstep and direction, the
  * rows of all batch columns spread over every compute unit.
@@ -154,7 +157,9 @@ ck_status ck_recurrence_sizes(ck_graph_t g, int64_t T, int64_t B, int64_t micros
  * creation, default 1048576; a negative value fails every wait at once and
  * exists to test that failure path.)
  * Blocked kernels (graphs of at least 100000 nodes, or CK_BLOCKED set to
- * "1" at creation; 5 <= B <= 64): two launches per microstep and direction.  The nodes
+ * "1" at creation; 5 <= B <= 64; *path 2): the forward runs two launches per
+ * microstep and the backward the per-microstep kernels; with CK_BLOCKED "2"
+ * at creation (*path 3) the backward is blocked as well.  The nodes
  * whose rows are gathered are cut into 8 contiguous blocks, one per XCD, so
  * each XCD gathers from a slice of the state plane that stays in its own L2;
  * each row's edges into a block (at most 64 per work item) leave one partial

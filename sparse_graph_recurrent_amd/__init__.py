@@ -195,14 +195,16 @@ def recurrence_sizes(graph: SparseGraph, T: int, B: int, microsteps: int):
     return s.value, w.value
 
 
-PATH_NAMES = {0: "per_microstep", 1: "resident", 2: "blocked"}
+PATH_NAMES = {0: "per_microstep", 1: "resident", 2: "blocked", 3: "blocked_both"}
 
 
 def recurrence_path(graph: SparseGraph, B: int) -> str:
     """Kernels a call with batch B runs on this graph: "resident" (one launch
-    per call, each XCD computing one group of 4 batch columns), "blocked" (two
-    launches per microstep, each XCD gathering from its own block of nodes) or
-    "per_microstep" (one launch per microstep)."""
+    per call, each XCD computing one group of 4 batch columns), "blocked" (a
+    forward of two launches per microstep, each XCD gathering from its own
+    block of nodes, and the per-microstep backward), "blocked_both" (blocked
+    kernels in both directions) or "per_microstep" (one launch per microstep
+    in both directions)."""
     r = ctypes.c_int()
     _check(lib().ck_recurrence_path(graph.handle, int(B), ctypes.byref(r)))
     return PATH_NAMES[r.value]

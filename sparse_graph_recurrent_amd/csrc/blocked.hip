@@ -654,7 +654,7 @@ BlkWs blk_ws_layout(const ck_graph* g, const BlkDims& d) {
 
 bool blk_fits(const ck_graph* g, int64_t Bp) {
   if (!g->blk_ok || Bp < 8 || Bp > 64) return false;
-  const int64_t items = std::max(g->blk_fwd.items, g->blk_bwd.items);
+  const int64_t items = std::max(g->blk_fwd.items, g->blk_bwd.items);  // (0 when not planned)
   const int64_t lim = (int64_t)kOut;  // buffer byte offsets stay below the out-of-range marker
   // nodes below the sentinel, whose gather offset (at least kBlkNoNode * 32
   // bytes) lies past the plane

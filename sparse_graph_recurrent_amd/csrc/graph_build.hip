@@ -652,19 +652,20 @@ extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int
   // blocked plans (optional: for graphs whose state plane dwarfs the L2s)
   {
     const char* env = getenv("CK_BLOCKED");
-    const bool wanted = env && env[0] ? (env[0] == '1' && env[1] == '\0') : N >= kBlkMinN;
+    const bool set = env && env[0] && env[1] == '\0';
+    const bool both = set && env[0] == '2';
+    const bool wanted = env && env[0] ? (set && (env[0] == '1' || both)) : N >= kBlkMinN;
     if (wanted) {
       bool pf = false, pb = false;
       rc = build_blocked(hptr, N, g->col_idx, g->perm, num_cus, stream, &g->blk_fwd, &pf);
       if (rc != CK_OK) return fail(rc);
-      if (pf)
+      if (pf && both)
         rc = build_blocked(htptr, N, g->t_col_idx, g->t_perm, num_cus, stream, &g->blk_bwd, &pb);
       if (rc != CK_OK) return fail(rc);
-      g->blk_ok = pf && pb ? 1 : 0;
-      if (!g->blk_ok) {
-        free_blocked(&g->blk_fwd);
-        free_blocked(&g->blk_bwd);
-      }
+      g->blk_ok = pf ? 1 : 0;
+      g->blk_bwd_ok = pf && pb ? 1 : 0;
+      if (!g->blk_ok) free_blocked(&g->blk_fwd);
+      if (!g->blk_bwd_ok) free_blocked(&g->blk_bwd);
     }
   }
   (void)hipFree(flags);

@@ -878,7 +878,8 @@ struct Dims {
   int64_t slots_f, slots_b;  // padded edge slots of the forward / backward schedule
   size_t plane;  // floats per [N][Bp] plane
   bool resident;  // the call runs the XCD-resident kernels (one launch per call)
-  bool blocked;   // the call runs the blocked kernels (two launches per microstep)
+  bool blocked;   // the forward runs the blocked kernels (two launches per microstep)
+  bool blocked_bwd;  // so does the backward (else it runs the per-microstep kernels)
   ResDims rd;
   BlkDims bd;
 };
@@ -937,6 +938,7 @@ ck_status make_dims(const ck_graph* g, int64_t T, int64_t B, int64_t M, Dims* d)
   d->resident = g->res_ok != 0 && std::max(g->N, g->n_in) * B * 4 < (1LL << 31);
   d->rd = ResDims{g->N, (g->N + 7) / 8 * 8, B, Bp / 4, g->n_in, T, M, T * M};
   d->blocked = !d->resident && blk_fits(g, Bp);
+  d->blocked_bwd = d->blocked && g->blk_bwd_ok != 0;
   d->bd = BlkDims{g->N, g->E, g->n_in, T, B, M, T * M, Bp, (int)(Bp / 4), d->plane};
   return CK_OK;
 }
@@ -944,7 +946,10 @@ ck_status make_dims(const ck_graph* g, int64_t T, int64_t B, int64_t M, Dims* d)
 // Workspace bytes of a call (either direction).
 size_t ws_total(const ck_graph* g, const Dims& d) {
   if (d.resident) return res_ws_layout(g, d.rd).total;
-  if (d.blocked) return blk_ws_layout(g, d.bd).total;
+  if (d.blocked_bwd) return blk_ws_layout(g, d.bd).total;
+  // a blocked forward's regions, then (from offset 0 again) the per-microstep
+  // backward's: the backward reads nothing the forward left in the workspace
+  if (d.blocked) return std::max(blk_ws_layout(g, d.bd).fwd_end, ws_layout(d).total);
   return ws_layout(d).total;
 }
 
@@ -978,7 +983,7 @@ extern "C" ck_status ck_recurrence_path(ck_graph_t g, int64_t B, int* path) {
   Dims d;
   rc = make_dims(g, 1, B, 1, &d);
   if (rc != CK_OK) return rc;
-  *path = d.resident ? 1 : d.blocked ? 2 : 0;
+  *path = d.resident ? 1 : d.blocked_bwd ? 3 : d.blocked ? 2 : 0;
   return CK_OK;
 }
 
@@ -1162,7 +1167,7 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
     return res_backward(g, d.rd, edge_values, leak, state0, saved, grad_out, grad_edge_values,
                         grad_leak, grad_bias, grad_drives, grad_state0, workspace, stream);
   }
-  if (d.blocked) {
+  if (d.blocked_bwd) {
     const size_t need = blk_ws_layout(g, d.bd).total;
     if (workspace_bytes < need) {
       set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, need);

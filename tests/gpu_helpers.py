@@ -41,13 +41,14 @@ def to_dev(a, dtype=None):
     return t.cuda()
 
 
-PATHS = ("resident", "per_microstep", "blocked")
+PATHS = ("resident", "per_microstep", "blocked", "blocked_both")
+BLOCKED = ("blocked", "blocked_both")  # paths that need 5 <= B <= 64
 
 
 def make_graph(w, path=None, env=None) -> sgr.SparseGraph:
     """The workload's graph.  path: None for the library's choice, or
-    "resident" / "per_microstep" / "blocked" to pin the kernels (CK_RESIDENT
-    and CK_BLOCKED at creation; the requested path must be the one taken at
+    "resident" / "per_microstep" / "blocked" / "blocked_both" to pin the
+    kernels (CK_RESIDENT and CK_BLOCKED at creation; the requested path must be the one taken at
     the workload's B).  env: extra environment variables set while the graph
     is created."""
     set_env = dict(env or {})
@@ -57,6 +58,8 @@ def make_graph(w, path=None, env=None) -> sgr.SparseGraph:
         set_env["CK_RESIDENT"] = "1"
     elif path == "blocked":
         set_env.update(CK_RESIDENT="0", CK_BLOCKED="1")
+    elif path == "blocked_both":
+        set_env.update(CK_RESIDENT="0", CK_BLOCKED="2")
     saved = {k: os.environ.get(k) for k in set_env}
     os.environ.update(set_env)
     try:

@@ -16,7 +16,7 @@ import torch
 import oracle
 import sparse_graph_recurrent_amd as sgr
 import synthetic
-from gpu_helpers import (PATHS, check_outputs_all_columns, check_parity, column_masked_grad, log,
+from gpu_helpers import (BLOCKED, PATHS, check_outputs_all_columns, check_parity, column_masked_grad, log,
                          make_graph, run_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -128,7 +128,7 @@ def _mixed_graph(seed, B, T, M, N=400, E=9000, n_in=9):
 
 
 @pytest.mark.parametrize("B,path", [(b, p) for b in (1, 2, 3, 5, 8, 20, 31, 32, 33, 64, 65, 100)
-                                    for p in PATHS if not (p == "blocked" and not 5 <= b <= 64)])
+                                    for p in PATHS if not (p in BLOCKED and not 5 <= b <= 64)])
 def test_batch_widths_parity(B, path):
     w = _mixed_graph(100 + B, B=B, T=3, M=2)
     log(f"parity: mixed graph B={B} E={w.num_edges}, {path} kernels")
@@ -186,7 +186,7 @@ def test_edge_cases_full_parity(path):
     check_parity(run_gpu(w, path=path), w)
 
 
-@pytest.mark.parametrize("path", ["per_microstep", "blocked"])
+@pytest.mark.parametrize("path", ["per_microstep", "blocked", "blocked_both"])
 def test_mid_scale_parity(path):
     """Outputs on all 64 batch columns; gradients on columns 0, 37, 63."""
     w = synthetic.make("mid_scale")
@@ -212,7 +212,8 @@ def _connectome_parity(w, label, path=None):
 @pytest.mark.slow
 def test_connectome_parity():
     """Whole-connectome shape: hubs of in-degree up to 20,000, 80 % positive
-    weights, 64 microsteps; the graph takes the blocked kernels.  fp32
+    weights, 64 microsteps; the graph takes the blocked forward (and the
+    per-microstep backward).  fp32
     evaluations of the definition miss the stated bound on thousands of
     gradient entries here, by amounts that vary several-fold with summation
     order; both forwards form their row sums in fp64 (the blocked one rounds
@@ -247,6 +248,14 @@ def test_connectome_per_microstep_parity():
     """The whole-connectome workload on the per-microstep kernels (pinned)."""
     w = synthetic.make("connectome")
     _connectome_parity(w, "whole-connectome workload", path="per_microstep")
+
+
+@pytest.mark.slow
+def test_connectome_blocked_both_parity():
+    """The whole-connectome workload with the blocked kernels in both
+    directions (pinned)."""
+    w = synthetic.make("connectome")
+    _connectome_parity(w, "whole-connectome workload", path="blocked_both")
 
 
 # ---------------------------------------------------------------- properties

@@ -24,9 +24,10 @@ def _need_gpu():
 def test_path_selection():
     """Graphs of up to 9184 nodes take the resident kernels at every batch
     width (beyond 32 columns each XCD computes several column groups in
-    turn), graphs of 100,000 nodes and more the blocked kernels from 5 to 64
-    columns, the rest the per-microstep kernels; CK_RESIDENT=0 and
-    CK_BLOCKED=0 at creation turn the first two off."""
+    turn), graphs of 100,000 nodes and more the blocked forward (and the
+    per-microstep backward) from 5 to 64 columns, the rest the per-microstep
+    kernels; CK_RESIDENT=0 and CK_BLOCKED=0 at creation turn the first two
+    off, CK_BLOCKED=2 makes the backward blocked too."""
     w = synthetic.make("flygpt", T=2)
     g = make_graph(w)
     log("path selection: flygpt graph")
@@ -48,6 +49,9 @@ def test_path_selection():
     assert ([sgr.recurrence_path(gh, B) for B in (4, 5, 32, 64, 65)]
             == ["per_microstep"] + ["blocked"] * 3 + ["per_microstep"])
     assert sgr.recurrence_path(make_graph(huge, env={"CK_BLOCKED": "0"}), 32) == "per_microstep"
+    g2 = make_graph(huge, env={"CK_BLOCKED": "2"})
+    assert ([sgr.recurrence_path(g2, B) for B in (4, 5, 64, 65)]
+            == ["per_microstep", "blocked_both", "blocked_both", "per_microstep"])
 
 
 def test_largest_resident_graph():
