@@ -290,7 +290,8 @@ typedef struct {
   int32_t decay_shifts[8];   /* each in [0, 31]: V := V - (V >> k), applied in order */
 } ck_lif_params;
 
-/* Workspace bytes of ck_lif_forward on this graph. */
+/* Workspace bytes of ck_lif_forward (and of ck_lif_prepare / ck_lif_run) on
+ * this graph. */
 ck_status ck_lif_workspace_size(ck_graph_t g, size_t* workspace_bytes);
 
 /*
@@ -317,6 +318,25 @@ ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const int32_t* d
                          const ck_lif_params* params, const int32_t* v0, int64_t T,
                          uint8_t* spikes, int32_t* potentials, int64_t* overflow_step,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ck_lif_forward in two parts, for many runs over one set of synapses (the
+ * soup-connectome page's runtime loads a connectome once and runs it many
+ * times).  ck_lif_prepare validates the delays and leaves the synapses,
+ * packed in CSR order, in the workspace (which the caller keeps; argument
+ * meaning as for ck_lif_forward; synchronises the stream; CK_ERR_BAD_VALUE
+ * for a delay outside [1, 32767]).  ck_lif_run runs T steps from v0 on
+ * synapses a ck_lif_prepare (or ck_lif_forward) left in that workspace for
+ * this graph, with the spike lookup that prepare chose; it leaves them in
+ * place, so runs can follow one another.  It returns CK_ERR_BAD_VALUE when the
+ * workspace holds no prepared synapses of this graph, and otherwise as
+ * ck_lif_forward.  Results equal ck_lif_forward's bit for bit.
+ */
+ck_status ck_lif_prepare(ck_graph_t g, const int16_t* impulses, const int32_t* delays,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+ck_status ck_lif_run(ck_graph_t g, const ck_lif_params* params, const int32_t* v0, int64_t T,
+                     uint8_t* spikes, int32_t* potentials, int64_t* overflow_step,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Measurement hook for the LIF forward: summed durations (ms) and counts of
  * the per-step gather and update launches recorded while ck_profile_enable

@@ -40,7 +40,8 @@ STATUS_NAMES = {
 EXPORTED = ("ck_graph_create", "ck_graph_destroy", "ck_graph_sizes", "ck_graph_export",
             "ck_recurrence_sizes", "ck_recurrence_path", "ck_recurrence_forward",
             "ck_recurrence_backward", "ck_recurrence_status", "ck_recurrence_forward_noalloc",
-            "ck_lif_workspace_size", "ck_lif_forward", "ck_profile_collect_lif",
+            "ck_lif_workspace_size", "ck_lif_forward", "ck_lif_prepare", "ck_lif_run",
+            "ck_profile_collect_lif",
             "ck_profile_enable", "ck_profile_collect", "ck_status_string", "ck_last_error")
 
 
@@ -87,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.ck_lif_workspace_size.argtypes = [p, ctypes.POINTER(sz)]
         L.ck_lif_forward.argtypes = [p, p, p, ctypes.POINTER(LifParams), p, i64, p, p,
                                      ctypes.POINTER(i64), p, sz, p]
+        L.ck_lif_prepare.argtypes = [p, p, p, p, sz, p]
+        L.ck_lif_run.argtypes = [p, ctypes.POINTER(LifParams), p, i64, p, p, ctypes.POINTER(i64),
+                                 p, sz, p]
         L.ck_profile_enable.argtypes = [ctypes.c_int]
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(i64)
@@ -315,6 +319,32 @@ def profile_collect() -> dict:
             "bwd_launches": bn.value}
 
 
+def _lif_params(threshold, reset, refractory_steps, decay_shifts):
+    shifts = list(decay_shifts)
+    if len(shifts) > 8:
+        raise ValueError("at most 8 decay shifts")
+    return LifParams(int(threshold), int(reset), int(refractory_steps), len(shifts),
+                     (ctypes.c_int32 * 8)(*shifts))
+
+
+def lif_workspace(graph: SparseGraph, device="cuda") -> torch.Tensor:
+    """A workspace of ``ck_lif_workspace_size`` bytes for this graph."""
+    wb = ctypes.c_size_t()
+    _check(lib().ck_lif_workspace_size(graph.handle, ctypes.byref(wb)))
+    return _byte_buffer(wb.value, device)
+
+
+def _lif_outputs(N, T, device):
+    return (torch.empty((int(T), N), dtype=torch.uint8, device=device),
+            torch.empty((int(T), N), dtype=torch.int32, device=device))
+
+
+def _lif_raise(st, step):
+    err = CkError(st, lib().ck_last_error().decode())
+    err.step = step.value
+    raise err
+
+
 def lif_forward(graph: SparseGraph, impulses, delays, v0, T: int, threshold: int, reset: int,
                 refractory_steps: int, decay_shifts=(), workspace=None, stream=None):
     """Run ``ck_lif_forward`` (fixed-point leaky integrate-and-fire on the
@@ -327,25 +357,45 @@ def lif_forward(graph: SparseGraph, impulses, delays, v0, T: int, threshold: int
     _dev(impulses, "impulses", torch.int16, (E,))
     _dev(delays, "delays", torch.int32, (E,))
     _dev(v0, "v0", torch.int32, (N,))
-    shifts = list(decay_shifts)
-    if len(shifts) > 8:
-        raise ValueError("at most 8 decay shifts")
-    prm = LifParams(int(threshold), int(reset), int(refractory_steps), len(shifts),
-                    (ctypes.c_int32 * 8)(*shifts))
-    wb = ctypes.c_size_t()
-    _check(lib().ck_lif_workspace_size(graph.handle, ctypes.byref(wb)))
-    workspace = _byte_buffer(wb.value, v0.device) if workspace is None else workspace
-    spikes = torch.empty((int(T), N), dtype=torch.uint8, device=v0.device)
-    pot = torch.empty((int(T), N), dtype=torch.int32, device=v0.device)
+    prm = _lif_params(threshold, reset, refractory_steps, decay_shifts)
+    workspace = lif_workspace(graph, v0.device) if workspace is None else workspace
+    spikes, pot = _lif_outputs(N, T, v0.device)
     step = ctypes.c_int64(-1)
     st = lib().ck_lif_forward(graph.handle, _ptr(impulses), _ptr(delays), ctypes.byref(prm),
                               _ptr(v0), int(T), _ptr(spikes), _ptr(pot), ctypes.byref(step),
                               _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream))
     if st != 0:
-        err = CkError(st, lib().ck_last_error().decode())
-        err.step = step.value
-        raise err
+        _lif_raise(st, step)
+    return spikes, pot
+
+
+def lif_prepare(graph: SparseGraph, impulses, delays, workspace=None, stream=None) -> torch.Tensor:
+    """``ck_lif_prepare``: validate the delays and pack the synapses into a
+    workspace (allocated when None), returned for ``lif_run``."""
+    E = graph.num_edges
+    _dev(impulses, "impulses", torch.int16, (E,))
+    _dev(delays, "delays", torch.int32, (E,))
+    workspace = lif_workspace(graph, impulses.device) if workspace is None else workspace
+    _check(lib().ck_lif_prepare(graph.handle, _ptr(impulses), _ptr(delays), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return workspace
+
+
+def lif_run(graph: SparseGraph, workspace, v0, T: int, threshold: int, reset: int,
+            refractory_steps: int, decay_shifts=(), stream=None):
+    """``ck_lif_run``: T steps from v0 on the synapses ``lif_prepare`` left in
+    ``workspace``; returns and raises as ``lif_forward``."""
+    N = graph.num_nodes
+    _dev(v0, "v0", torch.int32, (N,))
+    prm = _lif_params(threshold, reset, refractory_steps, decay_shifts)
+    spikes, pot = _lif_outputs(N, T, v0.device)
+    step = ctypes.c_int64(-1)
+    st = lib().ck_lif_run(graph.handle, ctypes.byref(prm), _ptr(v0), int(T), _ptr(spikes),
+                          _ptr(pot), ctypes.byref(step), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        _lif_raise(st, step)
     return spikes, pot
 
 

@@ -43,7 +43,11 @@ namespace {
 // flags[0]: first timestep whose update left the int32 range (INT_MAX: none)
 // flags[1]: set when a delay is outside [1, 32767]
 // flags[2]: the largest delay
+// flags[3..7]: what a prepare left in the workspace: kLifMark, E and N (low
+//   31 bits), the lookup (R: the bit rows' count, 0 for byte lookups) and the
+//   low 32 bits of the graph's row-pointer address
 constexpr int kLifFlags = 64;
+constexpr int32_t kLifMark = 0x4C494650;
 // Spike bit rows kept for the LDS lookups: step t's row is slot t % R of the
 // ring, R = the largest delay (at most kLifRing); a workgroup holds the
 // R rows in LDS, at most kLifLdsBytes.
@@ -73,6 +77,8 @@ LifWs lif_layout(int64_t N, int64_t E) {
   return w;
 }
 
+// Start of a run: potentials from v0, refractory counts and accumulators
+// cleared, no overflow seen.
 __global__ void lif_init(const int32_t* __restrict__ v0, int64_t N, int32_t* __restrict__ v,
                          int32_t* __restrict__ r, long long* __restrict__ acc,
                          int32_t* __restrict__ flags) {
@@ -82,10 +88,20 @@ __global__ void lif_init(const int32_t* __restrict__ v0, int64_t N, int32_t* __r
     r[i] = 0;
     acc[i] = 0;
   }
-  if (i == 0) {
-    flags[0] = INT_MAX;
+  if (i == 0) flags[0] = INT_MAX;
+}
+
+// Flags of a prepare: first cleared (mark included), then marked once done.
+__global__ void lif_flags(int32_t* __restrict__ flags, int32_t m0, int32_t m1, int32_t m2,
+                          int32_t m3, int32_t m4) {
+  if (threadIdx.x == 0) {
     flags[1] = 0;
     flags[2] = 0;
+    flags[3] = m0;
+    flags[4] = m1;
+    flags[5] = m2;
+    flags[6] = m3;
+    flags[7] = m4;
   }
 }
 
@@ -365,65 +381,56 @@ extern "C" ck_status ck_lif_workspace_size(ck_graph_t g, size_t* workspace_bytes
   return CK_OK;
 }
 
-extern "C" ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const int32_t* delays,
-                                    const ck_lif_params* params, const int32_t* v0, int64_t T,
-                                    uint8_t* spikes, int32_t* potentials, int64_t* overflow_step,
-                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  clear_error();
-  ck_status rc = check_graph(g);
-  if (rc != CK_OK) return rc;
-  if (overflow_step) *overflow_step = -1;
-  const int64_t N = g->N, E = g->E;
-  if (T <= 0 || T > INT_MAX) {
-    set_error("T must be in [1, 2^31 - 1] (got %lld)", (long long)T);
-    return CK_ERR_BAD_SIZE;
-  }
-  if ((E > 0 && (!impulses || !delays)) || !params || !v0 || !spikes || !potentials ||
-      !workspace) {
-    set_error("NULL pointer for a non-empty tensor in the LIF forward");
+namespace {
+
+struct LifBufs {
+  int2* rec;
+  int32_t* dst;
+  uint32_t* words;
+  long long* acc;
+  int32_t *v, *r, *flags;
+  uint32_t* bits;
+};
+
+LifBufs lif_bufs(void* workspace, const LifWs& ws) {
+  char* b = static_cast<char*>(workspace);
+  return LifBufs{reinterpret_cast<int2*>(b + ws.rec),       reinterpret_cast<int32_t*>(b + ws.dst),
+                 reinterpret_cast<uint32_t*>(b + ws.words), reinterpret_cast<long long*>(b + ws.acc),
+                 reinterpret_cast<int32_t*>(b + ws.v),      reinterpret_cast<int32_t*>(b + ws.r),
+                 reinterpret_cast<int32_t*>(b + ws.flags),  reinterpret_cast<uint32_t*>(b + ws.bits)};
+}
+
+ck_status lif_check_ws(const ck_graph* g, void* workspace, size_t workspace_bytes, LifWs* ws) {
+  if (!workspace) {
+    set_error("workspace is NULL");
     return CK_ERR_NULL_ARG;
   }
-  if (params->num_decay_shifts < 0 || params->num_decay_shifts > 8 ||
-      params->refractory_steps < 0) {
-    set_error("num_decay_shifts must be in [0, 8] and refractory_steps >= 0");
-    return CK_ERR_BAD_VALUE;
-  }
-  LifParams p{};
-  p.threshold = params->threshold;
-  p.reset = params->reset;
-  p.refractory = params->refractory_steps;
-  p.nshift = params->num_decay_shifts;
-  for (int j = 0; j < p.nshift; ++j) {
-    if (params->decay_shifts[j] < 0 || params->decay_shifts[j] > 31) {
-      set_error("decay shift %d is outside [0, 31]", params->decay_shifts[j]);
-      return CK_ERR_BAD_VALUE;
-    }
-    p.shift[j] = params->decay_shifts[j];
-  }
-  const LifWs ws = lif_layout(N, E);
-  if (workspace_bytes < ws.total) {
-    set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, ws.total);
+  *ws = lif_layout(g->N, g->E);
+  if (workspace_bytes < ws->total) {
+    set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, ws->total);
     return CK_ERR_WORKSPACE;
   }
-  char* wsb = static_cast<char*>(workspace);
-  int2* rec = reinterpret_cast<int2*>(wsb + ws.rec);
-  int32_t* dst = reinterpret_cast<int32_t*>(wsb + ws.dst);
-  uint32_t* words = reinterpret_cast<uint32_t*>(wsb + ws.words);
-  long long* acc = reinterpret_cast<long long*>(wsb + ws.acc);
-  int32_t* v = reinterpret_cast<int32_t*>(wsb + ws.v);
-  int32_t* r = reinterpret_cast<int32_t*>(wsb + ws.r);
-  int32_t* flags = reinterpret_cast<int32_t*>(wsb + ws.flags);
-  uint32_t* bitring = reinterpret_cast<uint32_t*>(wsb + ws.bits);
-  lif_init<<<blocks(N), 256, 0, stream>>>(v0, N, v, r, acc, flags);
-  // The delays are validated, and the largest one read back, before the
-  // first step: it picks the lookup (LDS bit rows when they fit).
-  int R = 0;
+  return CK_OK;
+}
+
+int32_t lif_graph_tag(const ck_graph* g) {
+  return (int32_t)(uint32_t)(reinterpret_cast<uintptr_t>(g->row_ptr) & 0xFFFFFFFFu);
+}
+
+// Validate the delays, write the destinations and the CSR-order records, and
+// leave the mark; *R = the bit rows of the LDS lookups (0: byte lookups).
+ck_status lif_prepare_body(const ck_graph* g, const int16_t* impulses, const int32_t* delays,
+                           const LifBufs& b, hipStream_t stream, int* R) {
+  const int64_t N = g->N, E = g->E;
+  *R = 0;
+  lif_flags<<<1, 64, 0, stream>>>(b.flags, 0, 0, 0, 0, 0);
   if (E > 0) {
-    lif_words<<<std::min(blocks(E), 4096u), 256, 0, stream>>>(impulses, delays, E, words, flags);
-    lif_rows<<<blocks(N * 64), 256, 0, stream>>>(g->row_ptr, N, dst);
+    lif_words<<<std::min(blocks(E), 4096u), 256, 0, stream>>>(impulses, delays, E, b.words,
+                                                              b.flags);
+    lif_rows<<<blocks(N * 64), 256, 0, stream>>>(g->row_ptr, N, b.dst);
     CK_HIP_TRY(hipGetLastError());
     int32_t fl[3] = {0, 0, 0};
-    CK_HIP_TRY(hipMemcpyAsync(fl, flags, sizeof(fl), hipMemcpyDeviceToHost, stream));
+    CK_HIP_TRY(hipMemcpyAsync(fl, b.flags, sizeof(fl), hipMemcpyDeviceToHost, stream));
     CK_HIP_TRY(hipStreamSynchronize(stream));
     if (fl[1]) {
       set_error("an edge delay is outside [1, 32767]");
@@ -433,12 +440,46 @@ extern "C" ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const
     // of lif_pack_lds need; it is checked on its own all the same)
     if (fl[2] >= 1 && fl[2] <= kLifRing && (int64_t)fl[2] * lif_row_words(N) * 4 <= kLifLdsBytes &&
         N <= (int64_t(1) << 20) && lif_lds_enabled())
-      R = fl[2];
-    if (R > 0)
-      lif_pack_lds<<<blocks(E), 256, 0, stream>>>(g->col_idx, g->perm, words, dst, E, rec);
+      *R = fl[2];
+    if (*R > 0)
+      lif_pack_lds<<<blocks(E), 256, 0, stream>>>(g->col_idx, g->perm, b.words, b.dst, E, b.rec);
     else
-      lif_pack<<<blocks(E), 256, 0, stream>>>(g->col_idx, g->perm, words, E, rec);
+      lif_pack<<<blocks(E), 256, 0, stream>>>(g->col_idx, g->perm, b.words, E, b.rec);
   }
+  lif_flags<<<1, 64, 0, stream>>>(b.flags, kLifMark, (int32_t)(E & INT_MAX),
+                                  (int32_t)(N & INT_MAX), *R, lif_graph_tag(g));
+  CK_HIP_TRY(hipGetLastError());
+  return CK_OK;
+}
+
+ck_status lif_params(const ck_lif_params* params, LifParams* p) {
+  if (params->num_decay_shifts < 0 || params->num_decay_shifts > 8 ||
+      params->refractory_steps < 0) {
+    set_error("num_decay_shifts must be in [0, 8] and refractory_steps >= 0");
+    return CK_ERR_BAD_VALUE;
+  }
+  *p = LifParams{};
+  p->threshold = params->threshold;
+  p->reset = params->reset;
+  p->refractory = params->refractory_steps;
+  p->nshift = params->num_decay_shifts;
+  for (int j = 0; j < p->nshift; ++j) {
+    if (params->decay_shifts[j] < 0 || params->decay_shifts[j] > 31) {
+      set_error("decay shift %d is outside [0, 31]", params->decay_shifts[j]);
+      return CK_ERR_BAD_VALUE;
+    }
+    p->shift[j] = params->decay_shifts[j];
+  }
+  return CK_OK;
+}
+
+// T steps on prepared records (R as the prepare chose), then the overflow
+// check.
+ck_status lif_run_body(const ck_graph* g, const LifParams& p, const int32_t* v0, int64_t T,
+                       uint8_t* spikes, int32_t* potentials, int64_t* overflow_step,
+                       const LifBufs& b, int R, hipStream_t stream) {
+  const int64_t N = g->N, E = g->E;
+  lif_init<<<blocks(N), 256, 0, stream>>>(v0, N, b.v, b.r, b.acc, b.flags);
   const int64_t wsw = lif_row_words(N);
   const int lds = R > 0 ? (int)(R * wsw * 4) : 0;
   unsigned lds_grid = 0;
@@ -451,28 +492,29 @@ extern "C" ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const
     const int64_t chunks = (E + (int64_t)kLifU * 1024 - 1) / ((int64_t)kLifU * 1024);
     lds_grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((int64_t)cus * per_cu, chunks));
   }
+  ck_status rc = CK_OK;
   for (int64_t t = 0; t < T; ++t) {
     if (t >= 1 && E > 0) {
       rc = timed_launch(g_profile.lif_gather, stream, [&] {
         if (R > 0)
-          lif_gather_lds<<<lds_grid, 1024, lds, stream>>>(rec, E, (int)wsw, (int)t, R,
-                                                          reinterpret_cast<const uint4*>(bitring),
-                                                          acc);
+          lif_gather_lds<<<lds_grid, 1024, lds, stream>>>(b.rec, E, (int)wsw, (int)t, R,
+                                                          reinterpret_cast<const uint4*>(b.bits),
+                                                          b.acc);
         else
-          lif_gather<<<blocks(E), 256, 0, stream>>>(rec, dst, E, N, (int)t, spikes, acc);
+          lif_gather<<<blocks(E), 256, 0, stream>>>(b.rec, b.dst, E, N, (int)t, spikes, b.acc);
       });
       if (rc != CK_OK) return rc;
     }
     rc = timed_launch(g_profile.lif_update, stream, [&] {
-      lif_update<<<blocks(N), 256, 0, stream>>>(N, (int)t, p, acc, v, r, spikes, potentials,
-                                               R > 0 ? bitring : nullptr, wsw, std::max(R, 1),
-                                               flags);
+      lif_update<<<blocks(N), 256, 0, stream>>>(N, (int)t, p, b.acc, b.v, b.r, spikes, potentials,
+                                               R > 0 ? b.bits : nullptr, wsw, std::max(R, 1),
+                                               b.flags);
     });
     if (rc != CK_OK) return rc;
   }
   CK_HIP_TRY(hipGetLastError());
   int32_t fl[1] = {0};
-  CK_HIP_TRY(hipMemcpyAsync(fl, flags, sizeof(fl), hipMemcpyDeviceToHost, stream));
+  CK_HIP_TRY(hipMemcpyAsync(fl, b.flags, sizeof(fl), hipMemcpyDeviceToHost, stream));
   CK_HIP_TRY(hipStreamSynchronize(stream));
   if (fl[0] != INT_MAX) {
     if (overflow_step) *overflow_step = fl[0];
@@ -481,4 +523,94 @@ extern "C" ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const
     return CK_ERR_OVERFLOW;
   }
   return CK_OK;
+}
+
+ck_status lif_run_checks(const ck_lif_params* params, const int32_t* v0, int64_t T,
+                         uint8_t* spikes, int32_t* potentials) {
+  if (T <= 0 || T > INT_MAX) {
+    set_error("T must be in [1, 2^31 - 1] (got %lld)", (long long)T);
+    return CK_ERR_BAD_SIZE;
+  }
+  if (!params || !v0 || !spikes || !potentials) {
+    set_error("NULL pointer for a non-empty tensor in the LIF run");
+    return CK_ERR_NULL_ARG;
+  }
+  return CK_OK;
+}
+
+}  // namespace
+
+extern "C" ck_status ck_lif_prepare(ck_graph_t g, const int16_t* impulses, const int32_t* delays,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  ck_status rc = check_graph(g);
+  if (rc != CK_OK) return rc;
+  if (g->E > 0 && (!impulses || !delays)) {
+    set_error("impulses or delays is NULL");
+    return CK_ERR_NULL_ARG;
+  }
+  LifWs ws;
+  rc = lif_check_ws(g, workspace, workspace_bytes, &ws);
+  if (rc != CK_OK) return rc;
+  int R = 0;
+  rc = lif_prepare_body(g, impulses, delays, lif_bufs(workspace, ws), stream, &R);
+  if (rc != CK_OK) return rc;
+  CK_HIP_TRY(hipStreamSynchronize(stream));
+  return CK_OK;
+}
+
+extern "C" ck_status ck_lif_run(ck_graph_t g, const ck_lif_params* params, const int32_t* v0,
+                                int64_t T, uint8_t* spikes, int32_t* potentials,
+                                int64_t* overflow_step, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  clear_error();
+  ck_status rc = check_graph(g);
+  if (rc != CK_OK) return rc;
+  if (overflow_step) *overflow_step = -1;
+  rc = lif_run_checks(params, v0, T, spikes, potentials);
+  if (rc != CK_OK) return rc;
+  LifParams p;
+  rc = lif_params(params, &p);
+  if (rc != CK_OK) return rc;
+  LifWs ws;
+  rc = lif_check_ws(g, workspace, workspace_bytes, &ws);
+  if (rc != CK_OK) return rc;
+  const LifBufs b = lif_bufs(workspace, ws);
+  int32_t mk[5] = {0, 0, 0, 0, 0};
+  CK_HIP_TRY(hipMemcpyAsync(mk, b.flags + 3, sizeof(mk), hipMemcpyDeviceToHost, stream));
+  CK_HIP_TRY(hipStreamSynchronize(stream));
+  if (mk[0] != kLifMark || mk[1] != (int32_t)(g->E & INT_MAX) ||
+      mk[2] != (int32_t)(g->N & INT_MAX) || mk[3] < 0 || mk[3] > kLifRing ||
+      mk[4] != lif_graph_tag(g)) {
+    set_error("the workspace holds no prepared synapses of this graph (ck_lif_prepare)");
+    return CK_ERR_BAD_VALUE;
+  }
+  return lif_run_body(g, p, v0, T, spikes, potentials, overflow_step, b, mk[3], stream);
+}
+
+extern "C" ck_status ck_lif_forward(ck_graph_t g, const int16_t* impulses, const int32_t* delays,
+                                    const ck_lif_params* params, const int32_t* v0, int64_t T,
+                                    uint8_t* spikes, int32_t* potentials, int64_t* overflow_step,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  ck_status rc = check_graph(g);
+  if (rc != CK_OK) return rc;
+  if (overflow_step) *overflow_step = -1;
+  rc = lif_run_checks(params, v0, T, spikes, potentials);
+  if (rc != CK_OK) return rc;
+  if (g->E > 0 && (!impulses || !delays)) {
+    set_error("NULL pointer for a non-empty tensor in the LIF forward");
+    return CK_ERR_NULL_ARG;
+  }
+  LifParams p;
+  rc = lif_params(params, &p);
+  if (rc != CK_OK) return rc;
+  LifWs ws;
+  rc = lif_check_ws(g, workspace, workspace_bytes, &ws);
+  if (rc != CK_OK) return rc;
+  const LifBufs b = lif_bufs(workspace, ws);
+  int R = 0;
+  rc = lif_prepare_body(g, impulses, delays, b, stream, &R);
+  if (rc != CK_OK) return rc;
+  return lif_run_body(g, p, v0, T, spikes, potentials, overflow_step, b, R, stream);
 }

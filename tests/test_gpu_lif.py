@@ -164,6 +164,55 @@ def test_active_run_on_connectome():
     assert (s.sum(axis=1) > 1000).all()
 
 
+@pytest.mark.parametrize("lookups", ["lds", "bytes"])
+def test_prepare_then_runs(lookups, monkeypatch):
+    """ck_lif_prepare once, then ck_lif_run several times from different
+    initial potentials and parameters: each run equals the oracle bit for
+    bit, with either spike lookup."""
+    if lookups == "bytes":
+        monkeypatch.setenv("CK_LIF_LDS", "0")
+    rng = np.random.default_rng(61)
+    N, E = 3000, 80000
+    src, dst = rng.integers(0, N, E), rng.integers(0, N, E)
+    w = (np.where(rng.random(E) < 0.8, 1, -1) * rng.integers(1, 120, E)).astype(np.int16)
+    d = rng.integers(1, 6, E).astype(np.int32)
+    g = _graph(src, dst, N)
+    log(f"LIF: prepare once, three runs ({lookups} lookups)")
+    ws = sgr.lif_prepare(g, to_dev(w), to_dev(d))
+    for k, (thr, refr, shifts) in enumerate(((100, 2, [2]), (60, 0, [1, 3]), (150, 3, []))):
+        v0 = rng.integers(-200, 600, N).astype(np.int32)
+        s, p = sgr.lif_run(g, ws, to_dev(v0), 12, thr, -20, refr, shifts)
+        s2, p2 = oracle.lif_run(src, dst, N, w, d, v0, 12, thr, -20, refr, shifts)
+        np.testing.assert_array_equal(s.cpu().numpy(), s2, err_msg=f"run {k}")
+        np.testing.assert_array_equal(p.cpu().numpy(), p2, err_msg=f"run {k}")
+        assert s2[6:].sum() > 0
+
+
+def test_run_needs_prepared_synapses_of_the_graph():
+    rng = np.random.default_rng(62)
+    src, dst = rng.integers(0, 500, 4000), rng.integers(0, 500, 4000)
+    g, g2 = _graph(src, dst, 500), _graph(src, dst, 500)
+    w = to_dev(np.full(4000, 7, np.int16))
+    d = to_dev(np.ones(4000, np.int32))
+    v0 = to_dev(np.zeros(500, np.int32))
+    fresh = sgr.lif_workspace(g)
+    fresh.zero_()
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.lif_run(g, fresh, v0, 3, 10, 0, 0, [])
+    assert ei.value.status == 12
+    ws = sgr.lif_prepare(g, w, d)
+    sgr.lif_run(g, ws, v0, 3, 10, 0, 0, [])
+    with pytest.raises(sgr.CkError) as ei:   # prepared for another graph of the same size
+        sgr.lif_run(g2, ws, v0, 3, 10, 0, 0, [])
+    assert ei.value.status == 12
+    with pytest.raises(sgr.CkError) as ei:   # a failed prepare leaves no synapses behind
+        sgr.lif_prepare(g, w, to_dev(np.zeros(4000, np.int32)), workspace=ws)
+    assert ei.value.status == 12
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.lif_run(g, ws, v0, 3, 10, 0, 0, [])
+    assert ei.value.status == 12
+
+
 @pytest.mark.parametrize("sign", [1, -1])
 def test_overflow_is_rejected_at_the_same_step(sign):
     v0 = [I32_MAX, sign * (I32_MAX - 500), 5]
