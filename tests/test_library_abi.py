@@ -75,6 +75,11 @@ def test_null_handles_are_rejected(L):
     assert L.ck_recurrence_forward(None, *([None] * 5), 1, 1, 1, None, None, None, 0, None) == 9
     assert L.ck_recurrence_backward(None, None, None, None, 1, 1, 1, *([None] * 8), 0, None) == 9
     assert "handle" in L.ck_last_error().decode()
+    assert L.ck_lif_workspace_size(None, ctypes.byref(s)) == 9
+    assert L.ck_lif_forward(None, None, None, None, None, 1, None, None, None, None, 0, None) == 9
+    assert L.ck_lif_prepare(None, None, None, None, 0, None) == 9
+    assert L.ck_lif_run(None, None, None, 1, None, None, None, None, 0, None) == 9
+    assert "handle" in L.ck_last_error().decode()
 
 
 def test_oracle_and_header_agree_on_status_values():
