@@ -59,21 +59,24 @@ def algorithmic_bytes(N, E, n_in, B, T, M):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "flygpt_traffic.md")
+LIF_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "lif_traffic.md")
 CSRC = os.path.join(ROOT, "sparse_graph_recurrent_amd", "csrc")
 
 
 def kernel_source(kernel: str) -> str:
     if kernel.startswith("blk_"):
         return os.path.join(CSRC, "blocked.hip")
+    if kernel.startswith("lif_"):
+        return os.path.join(CSRC, "lif.hip")
     return os.path.join(CSRC, "resident.hip" if kernel.startswith("res_") else "recurrence.hip")
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, profile: str = TRAFFIC_PROFILE):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when the kernel source changed since it was taken."""
     import hashlib
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(profile) as f:
             text = f.read()
         with open(kernel_source(kernel), "rb") as f:
             digest = hashlib.sha256(f.read()).hexdigest()
@@ -204,6 +207,9 @@ def lif_bench(args, torch, sgr, synthetic, np):
     lds_path = maxd <= 16 and maxd * row_words * 4 <= 128 * 1024 and os.environ.get("CK_LIF_LDS") != "0"
     per_launch = (8 * E + 8 * N + maxd * row_words * 4) if lds_path else (12 * E + 9 * N)
     ach = per_launch / (gather_us * 1e-6) / 1e9
+    gname = "lif_gather_lds" if lds_path else "lif_gather"
+    tr = measured_traffic(gname, LIF_TRAFFIC_PROFILE)
+    m = None if tr is None else tr / (gather_us * 1e-6) / 1e9
     res = {"metric": "LIF forward: ms per timestep & edge-visits/s, synthetic whole-connectome "
                      "graph N=211,577 E=24,678,466; HBM GB/s",
            "value": E * T / (ms * 1e-3), "unit": "edge-visits/s", "n_gpus": 1,
@@ -220,10 +226,10 @@ def lif_bench(args, torch, sgr, synthetic, np):
            "kernels": {"gather_launch_us": gather_us, "update_launch_us": update_us,
                        "gather_launches_per_forward": prof["gather_launches"] // args.steps,
                        "update_launches_per_forward": prof["update_launches"] // args.steps},
-           "roofline": {"bound": "hbm", "kernel": "lif_gather_lds" if lds_path else "lif_gather",
-                        "achieved": ach,
+           "roofline": {"bound": "hbm", "kernel": gname, "achieved": ach,
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                        "traffic": None}}
+                        "traffic": tr, "measured_GBps": m,
+                        "measured_frac": None if m is None else m / HBM_PEAK_GBS}}
     if not args.no_cpu:
         import oracle
         t0 = time.perf_counter()
