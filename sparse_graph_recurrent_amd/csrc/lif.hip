@@ -26,7 +26,8 @@
 //   lif_update   one thread per neuron: the state update above; writes the
 //                step's spikes and potentials (and the step's spike bits into
 //                a ring of kLifRing bit rows), clears I.
-// A per-call prologue validates the delays, writes each position's
+// A prologue (in every ck_lif_forward, or once in ck_lif_prepare for any
+// number of ck_lif_run calls) validates the delays, writes each position's
 // destination, and packs {source, impulse, delay} (and, for the LDS lookups,
 // the destination) into 8-byte records in CSR order (the caller's edge order
 // stays invisible: impulse and delay are first packed into one word per
