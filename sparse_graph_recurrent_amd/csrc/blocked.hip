@@ -423,7 +423,7 @@ struct BlkBwdEpiArgs {
   const float* leak;
   const int32_t* input_slot;
   float* gh;                 // in: g^(s) (ignored without an edge pass), out: g^(s-1)
-  const float* G_t;          // [B][N] upstream gradient entering at microstep s-1, or nullptr
+  const float* G_t;          // [N][Bp] upstream gradient entering at microstep s-1, or nullptr
   // elementwise pass of microstep s-1 (a_k1 == nullptr when s-1 == 0)
   const float* a_k1;         // a^(s-1)
   const float* h_k1;         // h^(s-2)
@@ -496,13 +496,20 @@ __global__ __launch_bounds__(256) void blk_bwd_epi(BlkBwdEpiArgs p) {
       gold[2] = o.z;
       gold[3] = o.w;
     }
+    float gin[4] = {0.f, 0.f, 0.f, 0.f};
+    if (p.G_t != nullptr) {  // (padding columns of the planes are zero)
+      const float4 o = reinterpret_cast<const float4*>(p.G_t)[off];
+      gin[0] = o.x;
+      gin[1] = o.y;
+      gin[2] = o.z;
+      gin[3] = o.w;
+    }
     float g[4], ga[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int c = 4 * sub + q;
       g[q] = acc[q];
       if (p.partial != nullptr) g[q] = fmaf(1.0f - lam, gold[q], g[q]);
-      if (p.G_t && c < p.B) g[q] += p.G_t[(size_t)c * p.N + row];
+      if (p.G_t) g[q] += gin[q];
       ga[q] = 0.f;
     }
     if (p.a_k1 == nullptr) {
@@ -575,11 +582,17 @@ __global__ void blk_zero(float* __restrict__ p, int64_t n) {
 
 // Tiled transposes between [B][N] and [N][Bp] (32 x 32 tiles through LDS).
 constexpr int kT = 32;
+// (blockIdx.z: the z-th [B][N] matrix, bm_stride floats apart, into the z-th
+// plane, plane_stride floats apart)
 __global__ __launch_bounds__(256) void blk_to_planes(const float* __restrict__ bm, int N, int B,
-                                                     int Bp, float* __restrict__ plane) {
+                                                     int Bp, float* __restrict__ plane,
+                                                     size_t bm_stride = 0,
+                                                     size_t plane_stride = 0) {
   __shared__ float tile[kT][kT + 1];
   const int tx = threadIdx.x % kT, ty = threadIdx.x / kT;
   const int n0 = blockIdx.x * kT, b0 = blockIdx.y * kT;
+  bm += blockIdx.z * bm_stride;
+  plane += blockIdx.z * plane_stride;
   for (int i = ty; i < kT; i += blockDim.x / kT) {
     const int b = b0 + i, n = n0 + tx;
     tile[i][tx] = (b < B && n < N) ? bm[(size_t)b * N + n] : 0.0f;
@@ -648,6 +661,7 @@ BlkWs blk_ws_layout(const ck_graph* g, const BlkDims& d) {
   w.gh = o;   o = al256(o + d.plane * 4);
   w.ga0 = o;  o = al256(o + d.plane * 4);
   w.ga1 = o;  o = al256(o + d.plane * 4);
+  w.gt = o;   o = al256(o + (size_t)d.T * d.plane * 4);  // upstream gradient, node-major
   w.total = o;
   return w;
 }
@@ -752,6 +766,12 @@ ck_status blk_backward(const ck_graph* g, const BlkDims& d, const float* edge_va
     blk_pack<<<blocks_for(d.E + 1), 256, 0, stream>>>(edge_values, bb.pnode, bb.pperm, d.E, pe);
   blk_to_planes<<<dim3(blocks_for(d.N, kT), (unsigned)((d.Bp + kT - 1) / kT)), 256, 0, stream>>>(
       state0, (int)d.N, (int)d.B, (int)d.Bp, h0);
+  // the upstream gradient [T][B][N] as node-major planes: a row's epilogue
+  // lane reads its 4 columns with one 16-byte load
+  float* gt = reinterpret_cast<float*>(wsb + ws.gt);
+  blk_to_planes<<<dim3(blocks_for(d.N, kT), (unsigned)((d.Bp + kT - 1) / kT), (unsigned)d.T), 256,
+                  0, stream>>>(grad_out, (int)d.N, (int)d.B, (int)d.Bp, gt,
+                               (size_t)d.B * d.N, d.plane);
   if (d.n_in > 0)
     blk_zero<<<blocks_for(d.T * d.n_in * d.B), 256, 0, stream>>>(grad_drives, d.T * d.n_in * d.B);
   const PartFn part = BT::bpart[d.L - 2];
@@ -797,7 +817,7 @@ ck_status blk_backward(const ck_graph* g, const BlkDims& d, const float* edge_va
     e.partial = init ? nullptr : partial;
     e.first_k1 = init ? 1 : 0;
     const int64_t k1 = s - 1;  // microstep whose elementwise pass runs here
-    e.G_t = (k1 >= 1 && k1 % d.M == 0) ? grad_out + (size_t)((k1 - 1) / d.M) * d.B * d.N : nullptr;
+    e.G_t = (k1 >= 1 && k1 % d.M == 0) ? gt + (size_t)((k1 - 1) / d.M) * d.plane : nullptr;
     if (k1 >= 1) {
       e.a_k1 = aplane(k1);
       e.h_k1 = hplane(k1 - 1);

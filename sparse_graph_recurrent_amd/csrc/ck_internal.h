@@ -196,7 +196,7 @@ struct BlkDims {
 };
 // Workspace of the blocked path, byte offsets; a forward uses [0, fwd_end).
 struct BlkWs {
-  size_t pe, part, h0, fwd_end, gv, gh, ga0, ga1, total;
+  size_t pe, part, h0, fwd_end, gv, gh, ga0, ga1, gt, total;
 };
 BlkWs blk_ws_layout(const ck_graph* g, const BlkDims& d);
 // True when the graph has blocked plans and a call of Bp padded columns fits

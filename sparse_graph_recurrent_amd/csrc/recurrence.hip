@@ -529,7 +529,7 @@ struct BwdArgs {
   const float* ga_in;     // ga^(s) [N][Bp] (gathered); nullptr: no edge pass (init)
   const float* h_sm1;     // h^(s-1) [N][Bp]
   float* gh;              // in: g^(s) (ignored when ga_in == nullptr), out: g^(s-1)
-  const float* G_t;       // [B][N] upstream gradient entering at microstep s-1, or nullptr
+  const float* G_t;       // [N][Bp] upstream gradient entering at microstep s-1, or nullptr
   // elementwise pass of microstep s-1 (skipped when a_k1 == nullptr, i.e. s-1 == 0)
   const float* a_k1;      // a^(s-1)
   const float* h_k1;      // h^(s-2)
@@ -570,7 +570,7 @@ __device__ __forceinline__ BwdEpi bwd_epi_load(const BwdArgs& p, const Lanes& ln
   [[maybe_unused]] const size_t NBp = (size_t)p.N * p.Bp;
   if (p.ga_in != nullptr) e.gold = CK_AT(p.gh, off, NBp, 12);
   if (c < p.B) {
-    if (p.G_t) e.gin = CK_AT(p.G_t, (size_t)c * p.N + row, (size_t)p.B * p.N, 13);
+    if (p.G_t) e.gin = CK_AT(p.G_t, off, NBp, 13);
     if (p.a_k1 != nullptr) {
       e.ak = CK_AT(p.a_k1, off, NBp, 14);
       e.qk = CK_AT(p.h_k1, off, NBp, 15);
@@ -887,7 +887,7 @@ struct Dims {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t v, gv, h0, gh, ga0, ga1, part, total;
+  size_t v, gv, h0, gh, ga0, ga1, part, gt, total;
 };
 
 WsLayout ws_layout(const Dims& d) {
@@ -901,6 +901,8 @@ WsLayout ws_layout(const Dims& d) {
   w.ga1 = o; o = align256(o + d.plane * 4);
   w.part = o;  // per-chunk leak/bias partial sums when the batch spans several chunks
   if (d.chunks > 1) o = align256(o + 2 * (size_t)d.chunks * d.N * 4);
+  w.gt = o;  // the upstream gradient as T node-major planes (backward only)
+  o = align256(o + (size_t)d.T * d.plane * 4);
   w.total = o;
   return w;
 }
@@ -1196,6 +1198,11 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
     pack_edges<<<grid1(sc.slots), 256, 0, stream>>>(edge_values, sc.pcol, sc.pperm, sc.slots, pedge);
   batch_major_to_planes<<<transpose_grid(d.N, d.Bp, 1), 256, 0, stream>>>(
       state0, 1, (int)d.N, (int)d.B, (int)d.Bp, d.plane, h0);
+  // the upstream gradient [T][B][N] as node-major planes, so each row's
+  // epilogue reads its B values from one place instead of B cache lines
+  float* gt = reinterpret_cast<float*>(wsb + ws.gt);
+  batch_major_to_planes<<<transpose_grid(d.N, d.Bp, d.T), 256, 0, stream>>>(
+      grad_out, d.T, (int)d.N, (int)d.B, (int)d.Bp, d.plane, gt);
   if (d.n_in > 0)
     zero_f32<<<grid1(d.T * d.n_in * d.B), 256, 0, stream>>>(grad_drives, d.T * d.n_in * d.B);
   const BwdFn kern = KT::bwd[d.L - 1];
@@ -1225,7 +1232,7 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
     a.first_gv = s == d.S ? 1 : 0;
     a.first_k1 = init ? 1 : 0;
     const int64_t k1 = s - 1;  // microstep whose elementwise pass runs here
-    a.G_t = (k1 >= 1 && k1 % d.M == 0) ? grad_out + (size_t)((k1 - 1) / d.M) * d.B * d.N : nullptr;
+    a.G_t = (k1 >= 1 && k1 % d.M == 0) ? gt + (size_t)((k1 - 1) / d.M) * d.plane : nullptr;
     if (k1 >= 1) {
       a.a_k1 = aplane(k1);
       a.h_k1 = hplane(k1 - 1);
