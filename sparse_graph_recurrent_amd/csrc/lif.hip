@@ -66,7 +66,9 @@ LifWs lif_layout(int64_t N, int64_t E) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   LifWs w;
   size_t o = 0;
-  w.rec = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 8);
+  // (16 spare bytes: lif_gather_lds reads positions in pairs, and an odd E
+  // leaves the last pair half past the records)
+  w.rec = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 8 + 16);
   w.dst = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 4);
   w.words = o; o = al(o + (size_t)std::max<int64_t>(E, 1) * 4);
   w.acc = o;   o = al(o + (size_t)N * 8);
@@ -219,16 +221,24 @@ __device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
 // delay d, then each position tests its source's bit.  Bit rows are `ws`
 // words apart (a multiple of 4), so the copy moves 16-byte words, at most
 // kLifCopy of them per lane, all loads in flight together.  Grid-stride over
-// the positions in chunks of kLifU * 1024, each chunk's records loaded while
-// the previous chunk is summed.  Per wave and position group: the run starts
-// (lane 0 and every row change) as a ballot, the impulses summed by a prefix
-// sum (one wave's run holds at most 64 impulses, |impulse| < 2^15, so 32 bits
-// are exact), and the last lane of each run adds its run's total (the prefix
-// at the lane minus the prefix before the run's first lane) with one 64-bit
-// atomic.  Each stage runs over a lane's kLifU positions at once, so their
-// LDS reads, prefix sums and shuffles overlap.
-constexpr int kLifU = 6;
+// the positions in chunks of kLifChunk; a lane takes two neighbouring
+// positions per 16-byte load, so a wave covers 128 positions per load, and
+// each chunk's records are loaded while the previous chunk is summed.  Per
+// wave and group of 128 positions: one prefix sum over the lanes' pair sums
+// (a wave's group holds at most 128 impulses, |impulse| < 2^15, so 32 bits
+// are exact) gives the prefix at every position; the run starts (the group's
+// first position and every row change) come from two ballots, and the last
+// position of each run adds its run's total (its prefix minus the prefix
+// before the run's first position, found in the lane of the run's start)
+// with one 64-bit atomic.  Each stage runs over a lane's kLifPairs pairs at
+// once, so their LDS reads, prefix sums and shuffles overlap.
+constexpr int kLifPairs = 3;
+constexpr int kLifChunk = kLifPairs * 2 * 1024;
 constexpr int kLifCopy = kLifLdsBytes / 16 / 1024;
+
+__device__ __forceinline__ int lif_rec_row(int x, int y) {
+  return (int)(((uint32_t)x >> 20) | ((uint32_t)y >> 20) << 12);
+}
 
 __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ rec,
                                                       int64_t E, int ws, int t, int R,
@@ -253,56 +263,87 @@ __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ 
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int64_t chunk = (int64_t)kLifU * blockDim.x;
-  const int64_t stride = (int64_t)gridDim.x * chunk;
-  int2 x[kLifU];
-  int64_t base = (int64_t)blockIdx.x * chunk;
+  // pair j of a chunk starting at `base`: positions base + 2048 j + 2 tid and
+  // the next; the 16-byte loads start at an even position no later than the
+  // last even one, which the record region's 16 spare bytes keep in range
+  const int4* rec4 = reinterpret_cast<const int4*>(rec);
+  const int64_t last_pair = (E - 1) >> 1;
+  const int64_t stride = (int64_t)gridDim.x * kLifChunk;
+  int4 x[kLifPairs];
+  int64_t base = (int64_t)blockIdx.x * kLifChunk;
 #pragma unroll
-  for (int j = 0; j < kLifU; ++j)
-    x[j] = rec[std::min<int64_t>(base + j * blockDim.x + threadIdx.x, E - 1)];
+  for (int j = 0; j < kLifPairs; ++j)
+    x[j] = rec4[std::min<int64_t>((base >> 1) + j * 1024 + threadIdx.x, last_pair)];
   for (; base < E; base += stride) {
     // the next chunk's records (clamped into range: the loads are unconditional)
-    int2 xn[kLifU];
+    int4 xn[kLifPairs];
 #pragma unroll
-    for (int j = 0; j < kLifU; ++j)
-      xn[j] = rec[std::min<int64_t>(base + stride + j * blockDim.x + threadIdx.x, E - 1)];
-    bool live[kLifU];
-    int c[kLifU], rj[kLifU], prev[kLifU], P[kLifU], first[kLifU], before[kLifU];
-    uint32_t w[kLifU];
-    unsigned long long B[kLifU];
+    for (int j = 0; j < kLifPairs; ++j)
+      xn[j] = rec4[std::min<int64_t>(((base + stride) >> 1) + j * 1024 + threadIdx.x, last_pair)];
+    int r0[kLifPairs], r1[kLifPairs], c0[kLifPairs], c1[kLifPairs];
+    uint32_t w0[kLifPairs], w1[kLifPairs];
 #pragma unroll
-    for (int j = 0; j < kLifU; ++j) {
-      live[j] = base + j * blockDim.x + threadIdx.x < E;
-      const uint32_t xx = (uint32_t)x[j].x, y = (uint32_t)x[j].y;
-      rj[j] = live[j] ? (int)((xx >> 20) | (y >> 20) << 12) : -1;
-      w[j] = sb[(int)((y >> 16) & 15u) * ws + (int)((xx & 0xFFFFFu) >> 5)];
+    for (int j = 0; j < kLifPairs; ++j) {
+      const int64_t p = base + 2 * (j * 1024 + (int64_t)threadIdx.x);
+      // a position past the records (the clamped last pair's second half may
+      // be the spare bytes) looks up word 0 and counts nothing
+      if (p + 1 >= E) {
+        x[j].z = 0;
+        x[j].w = 0;
+      }
+      r0[j] = p < E ? lif_rec_row(x[j].x, x[j].y) : -1;
+      r1[j] = p + 1 < E ? lif_rec_row(x[j].z, x[j].w) : -1;
+      w0[j] = sb[(int)(((uint32_t)x[j].y >> 16) & 15u) * ws + (int)(((uint32_t)x[j].x & 0xFFFFFu) >> 5)];
+      w1[j] = sb[(int)(((uint32_t)x[j].w >> 16) & 15u) * ws + (int)(((uint32_t)x[j].z & 0xFFFFFu) >> 5)];
     }
 #pragma unroll
-    for (int j = 0; j < kLifU; ++j) {
-      const uint32_t src = (uint32_t)x[j].x;  // (bits 0-4 of the source)
-      c[j] = live[j] && ((w[j] >> (src & 31)) & 1u) ? (int)(int16_t)(x[j].y & 0xFFFF) : 0;
+    for (int j = 0; j < kLifPairs; ++j) {
+      c0[j] = r0[j] >= 0 && ((w0[j] >> (x[j].x & 31)) & 1u) ? (int)(int16_t)(x[j].y & 0xFFFF) : 0;
+      c1[j] = r1[j] >= 0 && ((w1[j] >> (x[j].z & 31)) & 1u) ? (int)(int16_t)(x[j].w & 0xFFFF) : 0;
+    }
+    int rprev[kLifPairs], Pin[kLifPairs];
+#pragma unroll
+    for (int j = 0; j < kLifPairs; ++j) rprev[j] = __shfl_up(r1[j], 1);
+#pragma unroll
+    for (int j = 0; j < kLifPairs; ++j) Pin[j] = wave_prefix_sum(c0[j] + c1[j], lane);
+    bool s0[kLifPairs], s1[kLifPairs];
+    int Ex[kLifPairs], P0[kLifPairs], bprev[kLifPairs];
+    unsigned long long S0[kLifPairs];
+#pragma unroll
+    for (int j = 0; j < kLifPairs; ++j) {
+      // prefixes: before the pair (Ex), through its first position (P0),
+      // through both (Pin); run starts at the first (s0) and second (s1)
+      Ex[j] = Pin[j] - c0[j] - c1[j];
+      P0[j] = Ex[j] + c0[j];
+      s0[j] = lane == 0 || rprev[j] != r0[j];
+      s1[j] = r1[j] != r0[j];
+      S0[j] = __ballot(s0[j]);
+      const unsigned long long F = __ballot(s0[j] || s1[j]);
+      // the prefix before this lane's last run start, fetched by the lanes
+      // whose first run continues from an earlier lane (lane 0 always starts
+      // a run, so such a lane exists below every lane > 0)
+      const int before_last = s1[j] ? P0[j] : Ex[j];
+      const unsigned long long below = F & ((1ull << lane) - 1ull);
+      const int m = below ? 63 - __clzll(below) : 0;
+      bprev[j] = __shfl(before_last, m);
     }
 #pragma unroll
-    for (int j = 0; j < kLifU; ++j) prev[j] = __shfl_up(rj[j], 1);
-#pragma unroll
-    for (int j = 0; j < kLifU; ++j) P[j] = wave_prefix_sum(c[j], lane);
-#pragma unroll
-    for (int j = 0; j < kLifU; ++j) {
-      B[j] = __ballot(lane == 0 || prev[j] != rj[j]);  // run starts
-      first[j] = 63 - __clzll(B[j] & (~0ull >> (63 - lane)));
+    for (int j = 0; j < kLifPairs; ++j) {
+      // the first position ends a run when the second starts one
+      const int sum0 = P0[j] - (s0[j] ? Ex[j] : bprev[j]);
+      if (r0[j] >= 0 && s1[j] && sum0 != 0)
+        atomicAdd(reinterpret_cast<unsigned long long*>(&acc[r0[j]]),
+                  (unsigned long long)(long long)sum0);
+      // the second ends one when the next lane's first starts one, or at
+      // the group's end
+      const bool end1 = lane == 63 || (((S0[j] >> lane) >> 1) & 1ull) != 0;
+      const int sum1 = Pin[j] - (s1[j] ? P0[j] : (s0[j] ? Ex[j] : bprev[j]));
+      if (r1[j] >= 0 && end1 && sum1 != 0)
+        atomicAdd(reinterpret_cast<unsigned long long*>(&acc[r1[j]]),
+                  (unsigned long long)(long long)sum1);
     }
 #pragma unroll
-    for (int j = 0; j < kLifU; ++j) before[j] = __shfl(P[j], first[j] > 0 ? first[j] - 1 : 0);
-#pragma unroll
-    for (int j = 0; j < kLifU; ++j) {
-      const int sum = P[j] - (first[j] > 0 ? before[j] : 0);
-      const bool last = lane == 63 || (((B[j] >> lane) >> 1) & 1ull) != 0;
-      if (rj[j] >= 0 && last && sum != 0)
-        atomicAdd(reinterpret_cast<unsigned long long*>(&acc[rj[j]]),
-                  (unsigned long long)(long long)sum);
-    }
-#pragma unroll
-    for (int j = 0; j < kLifU; ++j) x[j] = xn[j];
+    for (int j = 0; j < kLifPairs; ++j) x[j] = xn[j];
   }
 }
 
@@ -490,7 +531,7 @@ ck_status lif_run_body(const ck_graph* g, const LifParams& p, const int32_t* v0,
     int cus = 0;
     CK_HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, g->device));
     const int per_cu = lds <= 80 * 1024 ? 2 : 1;  // workgroups whose LDS fits a 160 KB CU
-    const int64_t chunks = (E + (int64_t)kLifU * 1024 - 1) / ((int64_t)kLifU * 1024);
+    const int64_t chunks = (E + kLifChunk - 1) / kLifChunk;
     lds_grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((int64_t)cus * per_cu, chunks));
   }
   ck_status rc = CK_OK;
