@@ -246,6 +246,20 @@ __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ 
                                                       long long* __restrict__ acc) {
   extern __shared__ uint4 sb4[];  // [R][ws / 4]
   const uint32_t* sb = reinterpret_cast<const uint32_t*>(sb4);
+  const int lane = threadIdx.x & 63;
+  // pair j of a chunk starting at `base`: positions base + 2048 j + 2 tid and
+  // the next; the 16-byte loads start at an even position no later than the
+  // last even one, which the record region's 16 spare bytes keep in range.
+  // The first chunk's records are requested before the bit rows, so both
+  // round trips overlap.
+  const int4* rec4 = reinterpret_cast<const int4*>(rec);
+  const int64_t last_pair = (E - 1) >> 1;
+  const int64_t stride = (int64_t)gridDim.x * kLifChunk;
+  int4 x[kLifPairs];
+  int64_t base = (int64_t)blockIdx.x * kLifChunk;
+#pragma unroll
+  for (int j = 0; j < kLifPairs; ++j)
+    x[j] = rec4[std::min<int64_t>((base >> 1) + j * 1024 + threadIdx.x, last_pair)];
   {
     const int w4 = ws / 4, n4 = R * w4;
     uint4 tmp[kLifCopy];
@@ -262,18 +276,6 @@ __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ 
     }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  // pair j of a chunk starting at `base`: positions base + 2048 j + 2 tid and
-  // the next; the 16-byte loads start at an even position no later than the
-  // last even one, which the record region's 16 spare bytes keep in range
-  const int4* rec4 = reinterpret_cast<const int4*>(rec);
-  const int64_t last_pair = (E - 1) >> 1;
-  const int64_t stride = (int64_t)gridDim.x * kLifChunk;
-  int4 x[kLifPairs];
-  int64_t base = (int64_t)blockIdx.x * kLifChunk;
-#pragma unroll
-  for (int j = 0; j < kLifPairs; ++j)
-    x[j] = rec4[std::min<int64_t>((base >> 1) + j * 1024 + threadIdx.x, last_pair)];
   for (; base < E; base += stride) {
     // the next chunk's records (clamped into range: the loads are unconditional)
     int4 xn[kLifPairs];
