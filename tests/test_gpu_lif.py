@@ -105,6 +105,22 @@ def test_lookup_boundaries(seed, N, E, max_delay, T):
     assert s[1:].sum() > 0
 
 
+@pytest.mark.parametrize("E", [1, 2, 3, 127, 129, 2049, 6143, 6145, 12289])
+def test_odd_and_ragged_edge_counts(E):
+    """The LDS-lookup gather reads two positions per lane in one 16-byte load
+    and walks the positions in chunks of 6,144: odd edge counts (the last
+    pair half past the records) and counts just around a pair, a wave's 128
+    positions and a chunk, bit-exact against the oracle."""
+    log(f"LIF: edge count {E}")
+    N = 64 if E < 100 else 300
+    rng = np.random.default_rng(E)
+    src, dst = rng.integers(0, N, E), rng.integers(0, N, E)
+    w = rng.integers(30, 120, E).astype(np.int16)
+    d = rng.integers(1, 4, E).astype(np.int32)
+    v0 = rng.integers(0, 100, N).astype(np.int32)
+    _both(src, dst, N, w, d, v0, 12, 100, 0, 1, [3])
+
+
 @pytest.mark.parametrize("gap", [2, 63, 4096])
 def test_empty_row_gaps(gap):
     """In-edges into rows 0, gap, 2 gap, 2 gap + 2 and 3 gap + 2 only: long
