@@ -380,17 +380,18 @@ __global__ __launch_bounds__(256) void blk_fwd_epi(BlkFwdEpiArgs p) {
   const size_t w4 = (size_t)p.Bp / 4;  // float4 per row
   const float4* part = reinterpret_cast<const float4*>(p.partial);
   double4 acc = d4(0.0);
-  // eight partial rows at a time, all requested at once (past the row's
-  // last item the loads repeat it and the sums skip it)
-  for (int c = i0; c < i1; c += 8) {
-    int id[8];
+  // sixteen partial rows at a time (most rows have at most 16 items), all
+  // requested at once (past the row's last item the loads repeat it and the
+  // sums skip it); 16 measured faster than 8, 12 or 24
+  for (int c = i0; c < i1; c += 16) {
+    int id[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) id[u] = p.item_ids[min(c + u, i1 - 1)];
-    float4 q[8];
+    for (int u = 0; u < 16; ++u) id[u] = p.item_ids[min(c + u, i1 - 1)];
+    float4 q[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) q[u] = part[(size_t)id[u] * w4 + sub];
+    for (int u = 0; u < 16; ++u) q[u] = part[(size_t)id[u] * w4 + sub];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const bool in = c + u < i1;
       acc.x += in ? (double)q[u].x : 0.0;
       acc.y += in ? (double)q[u].y : 0.0;
