@@ -29,6 +29,10 @@
 //      exchange planes of the backward);
 //   3. the XCD's workgroups meet at a counter barrier, and every workgroup
 //      copies the new plane into its LDS (global -> LDS loads, 16 B per lane).
+//      What no other workgroup reads -- the saved pre-activation and the
+//      outputs of the forward, the drive gradients of the backward -- is
+//      stored after the workgroup's arrival, so the barrier does not wait
+//      for it.
 // Every sum has a fixed order, so results are bitwise reproducible.  Every
 // wait is bounded: a workgroup that waits too long raises an error flag and
 // leaves; the call's last kernel then writes NaN to every output.
@@ -73,6 +77,7 @@ struct ResFwdArgs {
   const float* h0;      // [G][Np] float4: the initial state by column group
   float* hplanes;       // [S][G][Np] float4: h^(s)
   float* aplanes;       // [S][G][Np] float4: a^(s)
+  float* out;           // [T][B][N]: h at the last microstep of every input step
 };
 
 struct ResBwdArgs {
@@ -154,17 +159,24 @@ __device__ int res_join(const ResCommon& c, int xcc, int* s_rank) {
   return *s_rank;
 }
 
-// Barrier of the XCD's workgroups, the `round`-th of the launch (1-based).
-// Stores issued before it are complete in the XCD's L2 when it returns, and
-// this CU's vector L1 holds no line older than that.  Returns false (after
-// raising the error flag) if the other workgroups did not all arrive in time.
-__device__ bool res_barrier(const ResCommon& c, int xcc, int round, volatile int* s_fail) {
+// Barrier of the XCD's workgroups, the `round`-th of the launch (1-based),
+// in two halves: res_arrive counts the workgroup in once its stores are
+// complete in the XCD's L2; res_wait waits for the others and leaves no line
+// older than that in this CU's vector L1.  Stores issued between the two are
+// not covered (nor waited for).  res_wait returns false (after raising the
+// error flag) if the other workgroups did not all arrive in time.
+__device__ void res_arrive(const ResCommon& c, int xcc) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(&c.ctl[kCtlCount + xcc * kCtlStride], 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ bool res_wait(const ResCommon& c, int xcc, int round, volatile int* s_fail) {
   if (threadIdx.x == 0) {
     unsigned* cnt = &c.ctl[kCtlCount + xcc * kCtlStride];
     const unsigned target = (unsigned)c.ranks * (unsigned)round;
-    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int spins = 0;
     while (c.spin_limit < 0 ||
            __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -180,6 +192,11 @@ __device__ bool res_barrier(const ResCommon& c, int xcc, int round, volatile int
   if (*s_fail) return false;
   asm volatile("buffer_inv sc0" ::: "memory");
   return true;
+}
+
+__device__ bool res_barrier(const ResCommon& c, int xcc, int round, volatile int* s_fail) {
+  res_arrive(c, xcc);
+  return res_wait(c, xcc, round, s_fail);
 }
 
 // Rows [0, N) of a plane of float4 rows into LDS, 64 rows per wave
@@ -305,7 +322,8 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
   const bool wlive = __ballot(prow >= 0) != 0ull;
   const bool owner = r0 + tid < r1;
   const int row = owner ? r0 + tid : 0;
-  const uint32_t rowb = (uint32_t)row * 16u;
+  const uint32_t rowb = (uint32_t)row * 16u, rowf = (uint32_t)row * 4u;
+  const uint32_t colN = (uint32_t)N * 4u;  // bytes between batch columns of [B][N] tensors
   int pb = 0, pe = 0, ks = -1;
   float lam = 0.f, beta = 0.f;
   if (owner) {
@@ -349,6 +367,7 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
       }
       part[tid] = acc;
       __syncthreads();
+      float4 ast = f4(0.f), hst = f4(0.f);
       if (owner) {
         const float4 sum = row_sum(part, pb, pe);
         const float4 hp = plane[row];
@@ -361,11 +380,28 @@ __global__ __launch_bounds__(kResLanes) void res_fwd(ResFwdArgs p) {
         h.y = (1.0f - lam) * hp.y + lam * ftanh(a.y);
         h.z = (1.0f - lam) * hp.z + lam * ftanh(a.z);
         h.w = (1.0f - lam) * hp.w + lam * ftanh(a.w);
-        bst4(a, p.aplanes + (size_t)(s - 1) * psz + goff, rowb, 0);
         bst4(h, p.hplanes + (size_t)(s - 1) * psz + goff, rowb, 0);
+        ast = a;
+        hst = h;
+      }
+      // only the new state is exchanged: the saved a and the outputs are
+      // stored after this workgroup has arrived at the barrier
+      if (s < p.c.S) res_arrive(p.c, xcc);
+      if (owner) {
+        bst4(ast, p.aplanes + (size_t)(s - 1) * psz + goff, rowb, 0);
+        if (s % p.c.M == 0) {
+          // the output of input step s / M - 1, column by column (consecutive
+          // owners hold consecutive rows, so each store is contiguous)
+          float* o = p.out + (size_t)(s / p.c.M - 1) * B * N;
+          const uint32_t cb = (uint32_t)b0 * colN;
+          if (b0 < B) bst1(hst.x, o, rowf, cb);
+          if (b0 + 1 < B) bst1(hst.y, o, rowf, cb + colN);
+          if (b0 + 2 < B) bst1(hst.z, o, rowf, cb + 2 * colN);
+          if (b0 + 3 < B) bst1(hst.w, o, rowf, cb + 3 * colN);
+        }
       }
       if (s == p.c.S) break;
-      if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
+      if (!res_wait(p.c, xcc, ++round, &s_fail)) return;
       res_load_plane(plane, p.hplanes + (size_t)(s - 1) * psz + goff, N, rank * ((N + 63) / 64) / p.c.ranks);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -436,6 +472,7 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
   };
   float4 gh = f4(0.f), gd = f4(0.f);
   float gl = 0.f, gb = 0.f;
+  int gd_step = -1;  // input step whose drive gradient gd holds, complete and not yet stored
   // elementwise pass of microstep k on the owner's row, given g^(k) before
   // its seed, the seed, a^(k) and h^(k-1): leak/bias row sums, drive gradient,
   // and ga^(k) to the exchange plane
@@ -467,16 +504,22 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
     const float4 ga4 = make_float4(ga[0], ga[1], ga[2], ga[3]);
     if (ks >= 0) {
       gd = add4(gd, ga4);
-      if ((k - 1) % M == 0) {
-        float* o = p.gdrives + (size_t)((k - 1) / M) * p.c.n_in * B;
-        if (live > 0) bst1(gd.x, o, ksb, (uint32_t)b0 * 4u);
-        if (live > 1) bst1(gd.y, o, ksb, (uint32_t)(b0 + 1) * 4u);
-        if (live > 2) bst1(gd.z, o, ksb, (uint32_t)(b0 + 2) * 4u);
-        if (live > 3) bst1(gd.w, o, ksb, (uint32_t)(b0 + 3) * 4u);
-        gd = f4(0.f);
-      }
+      // the input step's drive gradient is complete: stored by flush_gd,
+      // after the barrier's arrival (no other workgroup reads it)
+      if ((k - 1) % M == 0) gd_step = (k - 1) / M;
     }
     bst4(ga4, gapl(k), rowb, 0);
+  };
+  auto flush_gd = [&]() {
+    if (gd_step >= 0) {
+      float* o = p.gdrives + (size_t)gd_step * p.c.n_in * B;
+      if (live > 0) bst1(gd.x, o, ksb, (uint32_t)b0 * 4u);
+      if (live > 1) bst1(gd.y, o, ksb, (uint32_t)(b0 + 1) * 4u);
+      if (live > 2) bst1(gd.z, o, ksb, (uint32_t)(b0 + 2) * 4u);
+      if (live > 3) bst1(gd.w, o, ksb, (uint32_t)(b0 + 3) * 4u);
+      gd = f4(0.f);
+      gd_step = -1;
+    }
   };
   int round = 0;
   const int gend = MULTI ? p.c.G : xcc + 1;
@@ -494,7 +537,9 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
     // the last microstep's elementwise pass seeds the reverse sweep
     if (owner) k1(S, f4(0.f), gin(S), bld4(apl(S), rowb, 0), bld4(hpl(S - 1), rowb, 0));
     float4 hq = prow >= 0 ? bld4(hpl(S - 1), prowb, 0) : f4(0.f);
-    if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
+    res_arrive(p.c, xcc);
+    if (owner) flush_gd();
+    if (!res_wait(p.c, xcc, ++round, &s_fail)) return;
     res_load_plane(plane, gapl(S), N, rank * ((N + 63) / 64) / p.c.ranks);
     if (tid < kResZeroRows) plane[N + tid] = f4(0.f);
     __builtin_amdgcn_s_waitcnt(0);
@@ -551,8 +596,10 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
         }
       }
       hq = hq_next;
+      if (s > 1) res_arrive(p.c, xcc);
+      if (owner) flush_gd();
       if (s == 1) break;
-      if (!res_barrier(p.c, xcc, ++round, &s_fail)) return;
+      if (!res_wait(p.c, xcc, ++round, &s_fail)) return;
       res_load_plane(plane, gapl(s - 1), N, rank * ((N + 63) / 64) / p.c.ranks);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -601,24 +648,17 @@ __global__ void res_prologue(const float* __restrict__ values, const int32_t* __
 // out[t][b][i] = h^((t+1) M)[b / 4][i][b % 4], or NaN everywhere if the
 // resident kernel raised its error flag.  The flag is also copied into the
 // saved arena's status word, so that a backward given this arena knows.
-__global__ void res_out(const float* __restrict__ hplanes, size_t psz, size_t gsz, int M,
-                        int64_t T, int N, int B, int G, const unsigned* __restrict__ ctl,
-                        float* __restrict__ out, unsigned* __restrict__ saved_status) {
-  const bool bad = ctl[kCtlErr] != 0u;
-  if (blockIdx.x == 0 && threadIdx.x == 0) saved_status[0] = ctl[kCtlErr];
-  const int64_t n = T * G * (int64_t)N;
+// After the resident forward (whose owners wrote the outputs): the saved
+// arena's status word, and NaN in every output if the kernel raised its
+// error flag.
+__global__ void res_fwd_status(const unsigned* __restrict__ ctl, int64_t n,
+                               float* __restrict__ out, unsigned* __restrict__ saved_status) {
+  const unsigned err = ctl[kCtlErr];
+  if (blockIdx.x == 0 && threadIdx.x == 0) saved_status[0] = err;
+  if (err == 0u) return;
   for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n;
-       k += (int64_t)gridDim.x * blockDim.x) {
-    const int i = (int)(k % N);
-    const int64_t tg = k / N;
-    const int g = (int)(tg % G);
-    const int64_t t = tg / G;
-    const float4 h = ldf4(hplanes + (size_t)((t + 1) * M - 1) * psz + (size_t)g * gsz, i);
-    for (int c = 0; c < 4; ++c) {
-      const int b = g * 4 + c;
-      if (b < B) out[((size_t)t * B + b) * N + i] = bad ? NAN : comp(h, c);
-    }
-  }
+       k += (int64_t)gridDim.x * blockDim.x)
+    out[k] = NAN;
 }
 
 // After the resident backward: edge gradients to caller order and the leak /
@@ -801,6 +841,7 @@ ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_val
   a.h0 = h0;
   a.hplanes = static_cast<float*>(saved);
   a.aplanes = a.hplanes + (size_t)d.S * d.G * d.Np * 4;
+  a.out = out;
   const size_t lds = res_lds_bytes((int)d.N);
   const unsigned wgs = (unsigned)(r.ranks * kResXcds);
   ck_status rc = CK_OK;
@@ -811,10 +852,9 @@ ck_status res_forward(const ck_graph* g, const ResDims& d, const float* edge_val
   else
     hipLaunchKernelGGL(kern, dim3(wgs), dim3(kResLanes), lds, stream, a);
   if (rc != CK_OK) return rc;
-  const size_t gsz = (size_t)d.Np * 4, psz = gsz * d.G;
-  res_out<<<res_grid(d.T * d.G * d.N), 256, 0, stream>>>(a.hplanes, psz, gsz, (int)d.M, d.T,
-                                                         (int)d.N, (int)d.B, (int)d.G, ctl, out,
-                                                         saved_status(saved, d));
+  const int64_t nout = d.T * d.B * d.N;
+  res_fwd_status<<<(unsigned)std::min<int64_t>(res_grid(nout), 1024), 256, 0, stream>>>(
+      ctl, nout, out, saved_status(saved, d));
   CK_HIP_TRY(hipGetLastError());
   return CK_OK;
 }
