@@ -372,7 +372,9 @@ def main():
     names = {"resident": ("res_fwd", "res_bwd"), "blocked": ("blk_fwd", "bwd_step"),
              "blocked_both": ("blk_fwd", "blk_bwd")}.get(path, ("fwd_step", "bwd_step"))
     per_kernel = {}
-    for kname, per_b, us in ((names[0], fwd_b * S / fwd_n, fwd_us),
+    # the resident forward also writes the outputs [T][B][N] itself
+    fwd_launch_b = fwd_b * S / fwd_n + (4 * T * N * B if path == "resident" else 0)
+    for kname, per_b, us in ((names[0], fwd_launch_b, fwd_us),
                              (names[1], bwd_b * S / bwd_n, bwd_us)):
         a = per_b / (us * 1e-6) / 1e9
         tr = measured_traffic(kname)
