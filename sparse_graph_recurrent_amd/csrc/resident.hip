@@ -547,14 +547,11 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
     for (int s = S; s >= 1; --s) {
       // operands of this iteration's elementwise pass (microstep s-1) and of the
       // next iteration's edge pass, requested before the gathers
-      float4 seed = f4(0.f), ak = f4(0.f), qk = f4(0.f), hq_next = f4(0.f);
-      if (s >= 2) {
-        if (owner) {
-          seed = gin(s - 1);
-          ak = bld4(apl(s - 1), rowb, 0);
-          qk = bld4(hpl(s - 2), rowb, 0);
-        }
-        if (prow >= 0) hq_next = bld4(hpl(s - 2), prowb, 0);
+      float4 seed = f4(0.f), ak = f4(0.f), qk = f4(0.f);
+      if (s >= 2 && owner) {
+        seed = gin(s - 1);
+        ak = bld4(apl(s - 1), rowb, 0);
+        qk = bld4(hpl(s - 2), rowb, 0);
       }
       pc.launder();
       // gathers in groups of 4 rows, so that at most 4 gathered rows occupy
@@ -595,11 +592,16 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
           if (live > 3) bst1(g.w, p.gstate0, rowf, cb + 3 * colN);
         }
       }
-      hq = hq_next;
       if (s > 1) res_arrive(p.c, xcc);
       if (owner) flush_gd();
       if (s == 1) break;
+      // the next iteration's piece rows h^(s-2): a piece's row is one of this
+      // workgroup's rows, whose owner has just used that row as qk -- passed
+      // through LDS (the partial sums are all read once every wave has
+      // arrived) instead of loaded again by every piece lane
+      if (owner) part[tid] = qk;
       if (!res_wait(p.c, xcc, ++round, &s_fail)) return;
+      if (prow >= 0) hq = part[prow - r0];
       res_load_plane(plane, gapl(s - 1), N, rank * ((N + 63) / 64) / p.c.ranks);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
