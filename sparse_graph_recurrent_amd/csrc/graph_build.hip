@@ -447,10 +447,10 @@ bool xcds_as_expected(int num_cus, hipStream_t stream) {
 }
 
 ck_status build_resident(const std::vector<int32_t>& ptr, int64_t N, const int32_t* col,
-                         const int32_t* perm, int ranks, int max_lens, hipStream_t stream,
-                         Resident* out, bool* planned) {
+                         const int32_t* perm, int ranks, int max_D, bool every_wave_gathers,
+                         hipStream_t stream, Resident* out, bool* planned) {
   ResidentPlan plan;
-  *planned = plan_resident(ptr.data(), N, ranks, max_lens, &plan);
+  *planned = plan_resident(ptr.data(), N, ranks, max_D, every_wave_gathers, &plan);
   if (!*planned) return CK_OK;
   {
     // order each piece's edges against LDS bank conflicts (needs the rows read)
@@ -635,11 +635,13 @@ extern "C" ck_status ck_graph_create(const int64_t* src, const int64_t* dst, int
     if (wanted && N <= kResMaxN && num_cus <= 32 * kResXcds && xcds_as_expected(num_cus, stream)) {
       const int ranks = num_cus / kResXcds;
       bool pf = false, pb = false;
-      rc = build_resident(hptr, N, g->col_idx, g->perm, ranks, kResNumPieceLens, stream,
+      // (the forward's waves without pieces skip their gathers; every wave of
+      // the backward gathers)
+      rc = build_resident(hptr, N, g->col_idx, g->perm, ranks, kResFwdMaxD, false, stream,
                           &g->res_fwd, &pf);
       if (rc != CK_OK) return fail(rc);
       if (pf)
-        rc = build_resident(htptr, N, g->t_col_idx, g->t_perm, ranks, kResBwdPieceLens, stream,
+        rc = build_resident(htptr, N, g->t_col_idx, g->t_perm, ranks, kResBwdMaxD, true, stream,
                             &g->res_bwd, &pb);
       if (rc != CK_OK) return fail(rc);
       g->res_ok = pf && pb && res_prepare() == CK_OK ? 1 : 0;

@@ -559,11 +559,14 @@ __global__ __launch_bounds__(kResLanes) void res_bwd(ResBwdArgs p) {
       float4 acc = f4(0.f);
 #pragma unroll
       for (int j0 = 0; j0 < D; j0 += 4) {
+        // (the last group holds D mod 4 rows when D is not a multiple of 4)
         float4 x[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = plane[pc.at(j0 + u)];
+        for (int u = 0; u < 4; ++u)
+          if (j0 + u < D) x[u] = plane[pc.at(j0 + u)];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+          if (j0 + u >= D) break;
           acc = fma4(pc.val[j0 + u], x[u], acc);
           gvacc[j0 + u] += dot4(x[u], hq);
           // keep the update here (the optimiser would otherwise sink it past
@@ -718,6 +721,7 @@ ResFwdFn fwd_kernel(int D, bool multi) {
     case 8: return multi ? &res_fwd<8, true> : &res_fwd<8, false>;
     case 12: return multi ? &res_fwd<12, true> : &res_fwd<12, false>;
     case 16: return multi ? &res_fwd<16, true> : &res_fwd<16, false>;
+    case 18: return multi ? &res_fwd<18, true> : &res_fwd<18, false>;
     case 20: return multi ? &res_fwd<20, true> : &res_fwd<20, false>;
     case 24: return multi ? &res_fwd<24, true> : &res_fwd<24, false>;
   }
@@ -728,6 +732,7 @@ ResBwdFn bwd_kernel(int D, bool multi) {
     case 8: return multi ? &res_bwd<8, true> : &res_bwd<8, false>;
     case 12: return multi ? &res_bwd<12, true> : &res_bwd<12, false>;
     case 16: return multi ? &res_bwd<16, true> : &res_bwd<16, false>;
+    case 18: return multi ? &res_bwd<18, true> : &res_bwd<18, false>;
     case 20: return multi ? &res_bwd<20, true> : &res_bwd<20, false>;
     case 24: return multi ? &res_bwd<24, true> : &res_bwd<24, false>;
   }

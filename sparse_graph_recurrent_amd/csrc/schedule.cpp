@@ -187,14 +187,15 @@ bool pack_ranges(const std::vector<int64_t>& pc, int ranks, int64_t cap, std::ve
 
 }  // namespace
 
-bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_lens, ResidentPlan* out) {
+bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_D, bool every_wave_gathers,
+                   ResidentPlan* out) {
   if (ranks <= 0 || N <= 0) return false;
-  max_lens = std::min(max_lens, kResNumPieceLens);
   int best_D = 0;
   int64_t best_cap = 0, best_cost = -1;
   std::vector<int64_t> pc(N);
-  for (int li = 0; li < max_lens; ++li) {
+  for (int li = 0; li < kResNumPieceLens; ++li) {
     const int D = kResPieceLens[li];
+    if (D > max_D) continue;
     int64_t lo = 0;
     for (int64_t i = 0; i < N; ++i) {
       pc[i] = (ptr[i + 1] - ptr[i] + D - 1) / D;
@@ -207,7 +208,7 @@ bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_lens, Resid
       if (pack_ranges(pc, ranks, mid, nullptr)) hi = mid;
       else lo = mid + 1;
     }
-    const int64_t cost = hi * (D + 4);
+    const int64_t cost = every_wave_gathers ? (int64_t)D * kResLanes + hi : hi * (D + 4);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
       best_cap = hi;

@@ -89,11 +89,12 @@ void plan_schedule(const int32_t* ptr, int64_t N, int num_cus, int waves, Schedu
 // the last of them, and the owner adds these in wave order.
 constexpr int kResLanes = 1024;
 // Piece lengths the kernels are built for.
-constexpr int kResPieceLens[] = {8, 12, 16, 20, 24};
-constexpr int kResNumPieceLens = 5;
+constexpr int kResPieceLens[] = {8, 12, 16, 18, 20, 24};
+constexpr int kResNumPieceLens = 6;
+constexpr int kResFwdMaxD = 24;
 // The backward kernel also keeps D edge-gradient sums per lane; past D = 20
 // it no longer fits in 128 registers.
-constexpr int kResBwdPieceLens = 4;
+constexpr int kResBwdMaxD = 20;
 
 struct ResidentPlan {
   int D = 0;                        // edges per piece
@@ -146,11 +147,14 @@ void order_resident_slots(const int32_t* col, int64_t N, ResidentPlan* out);
 int64_t resident_conflict_cost(const int32_t* col, int64_t N, const ResidentPlan& p);
 
 // Plan the pieces of ptr[0..N] for `ranks` workgroups, choosing the piece
-// length among kResPieceLens[0 .. max_lens) that minimises the busiest
-// workgroup's (pieces x (D + 4)), an estimate of its gather work plus the
-// owners' combining.  Returns false when no length fits (a range needs more
-// than kResLanes pieces or rows).
-bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_lens, ResidentPlan* out);
+// length D among kResPieceLens up to max_D.  When only the waves holding
+// pieces gather (the forward), D minimises the busiest workgroup's
+// pieces x (D + 4), an estimate of its gather work plus the owners'
+// combining; when every wave gathers (the backward), the smallest D that
+// fits wins (fewer pieces on a tie).  Returns false when no length fits (a
+// range needs more than kResLanes pieces or rows).
+bool plan_resident(const int32_t* ptr, int64_t N, int ranks, int max_D, bool every_wave_gathers,
+                   ResidentPlan* out);
 
 // ---------------------------------------------------------------------------
 // Blocked plan: the per-microstep kernels of graphs whose state plane is far

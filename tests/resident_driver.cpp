@@ -1,4 +1,5 @@
-// CPU driver for the resident planner: reads "N ranks max_lens order" and the
+// CPU driver for the resident planner: reads "N ranks max_D every order" (every
+// = 1: every wave gathers, as in the backward) and the
 // N + 1 row pointers from stdin, then (order = 1) the row read by each
 // compressed edge; prints "none", or "D ranks max_pieces cost cost_ordered misses"
 // (bank-conflict costs of the slot table in compressed order and after
@@ -17,8 +18,8 @@ static void put(const std::vector<int32_t>& v) {
 
 int main() {
   long long N = 0;
-  int ranks = 0, lens = 0, order = 0;
-  if (std::scanf("%lld %d %d %d", &N, &ranks, &lens, &order) != 4 || N < 0) return 2;
+  int ranks = 0, max_D = 0, every = 0, order = 0;
+  if (std::scanf("%lld %d %d %d %d", &N, &ranks, &max_D, &every, &order) != 5 || N < 0) return 2;
   std::vector<int32_t> ptr(N + 1);
   for (auto& v : ptr)
     if (std::scanf("%d", &v) != 1) return 2;
@@ -29,7 +30,7 @@ int main() {
       if (std::scanf("%d", &v) != 1) return 2;
   }
   ckhip::ResidentPlan plan;
-  if (!ckhip::plan_resident(ptr.data(), N, ranks, lens, &plan)) {
+  if (!ckhip::plan_resident(ptr.data(), N, ranks, max_D, every != 0, &plan)) {
     std::printf("none\n");
     return 0;
   }

@@ -10,7 +10,9 @@ lanes [owner_pbeg[o], owner_pbeg[o + 1]), adds the run ends of those lanes
 wave by wave.  The replay must give every
 row sum exactly once, every edge must lie in exactly one piece, and the plan
 must stay inside the limits the kernels rely on (1024 lanes and 1024 rows
-per workgroup, D among the built piece lengths).
+per workgroup, D among the built piece lengths, at most 24 in the forward and
+20 in the backward, whose every wave gathers: there the smallest D that fits
+is chosen).
 """
 import os
 import shutil
@@ -24,7 +26,8 @@ import synthetic
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "sparse_graph_recurrent_amd", "csrc")
 LANES = 1024
-LENS = (8, 12, 16, 20, 24)
+LENS = (8, 12, 16, 18, 20, 24)
+FWD, BWD = (24, False), (20, True)  # (largest D, every wave gathers)
 
 
 @pytest.fixture(scope="module")
@@ -39,9 +42,11 @@ def driver(tmp_path_factory):
     return exe
 
 
-def plan(driver, ptr, ranks, lens, col=None):
+def plan(driver, ptr, ranks, kind, col=None):
     N = len(ptr) - 1
-    text = f"{N} {ranks} {lens} {0 if col is None else 1}\n" + " ".join(map(str, ptr)) + "\n"
+    max_d, every = kind
+    text = (f"{N} {ranks} {max_d} {int(every)} {0 if col is None else 1}\n"
+            + " ".join(map(str, ptr)) + "\n")
     if col is not None:
         text += " ".join(map(str, col)) + "\n"
     out = subprocess.run([driver], input=text, capture_output=True, text=True, check=True).stdout
@@ -56,7 +61,7 @@ def plan(driver, ptr, ranks, lens, col=None):
                 piece_cnt=arr[4].reshape(r, LANES), slot_edge=arr[5].reshape(r, D, LANES))
 
 
-def replay(driver, major, N, ranks=32, lens=5, minor=None):
+def replay(driver, major, N, ranks=32, kind=FWD, minor=None):
     """Plan and replay; with `minor` (the other endpoint of each edge) the
     slots are also ordered against bank conflicts, and the replay sums each
     lane's piece through its slot table."""
@@ -67,11 +72,11 @@ def replay(driver, major, N, ranks=32, lens=5, minor=None):
     if minor is not None:
         order = np.lexsort((np.asarray(minor), major))
         col = np.asarray(minor, dtype=np.int64)[order]
-    p = plan(driver, ptr.tolist(), ranks, lens, None if col is None else col.tolist())
+    p = plan(driver, ptr.tolist(), ranks, kind, None if col is None else col.tolist())
     if p is None:
         return None
     D = p["D"]
-    assert D in LENS[:lens] and p["ranks"] == ranks
+    assert D in LENS and D <= kind[0] and p["ranks"] == ranks
     rr = p["rank_rows"]
     assert rr[0] == 0 and rr[-1] == N and (np.diff(rr) >= 0).all() and (np.diff(rr) <= LANES).all()
     E = int(ptr[-1])
@@ -136,8 +141,8 @@ def test_flygpt_slot_order(driver):
     within each 16-lane group (sum over slots and groups of the most distinct
     rows sharing a bank group) to at most 80 % of the compressed order's."""
     w = synthetic.make("flygpt", synthetic.DEFAULT_SEEDS["flygpt"])
-    for major, minor, lens, most in ((w.dst, w.src, 5, 0.24), (w.src, w.dst, 4, 0.28)):
-        p = replay(driver, major, w.num_nodes, lens=lens, minor=minor)
+    for major, minor, kind, most in ((w.dst, w.src, FWD, 0.24), (w.src, w.dst, BWD, 0.28)):
+        p = replay(driver, major, w.num_nodes, kind=kind, minor=minor)
         live_waves = int((p["piece_cnt"].reshape(32, 16, 64).max(axis=2) > 0).sum())
         assert p["misses"] <= most * live_waves * 64 * p["D"], p["misses"]
         assert p["cost_ordered"] <= 0.80 * p["cost"], (p["cost"], p["cost_ordered"])
@@ -146,8 +151,8 @@ def test_flygpt_slot_order(driver):
 @pytest.mark.parametrize("name", ["tiny", "flygpt", "edge_cases"])
 def test_workload_plans(driver, name):
     w = synthetic.make(name, synthetic.DEFAULT_SEEDS[name])
-    for major, minor, lens in ((w.dst, w.src, 5), (w.src, w.dst, 4)):
-        p = replay(driver, major, w.num_nodes, lens=lens, minor=minor)
+    for major, minor, kind in ((w.dst, w.src, FWD), (w.src, w.dst, BWD)):
+        p = replay(driver, major, w.num_nodes, kind=kind, minor=minor)
         assert p is not None and p["cost_ordered"] <= p["cost"]
 
 
@@ -155,10 +160,23 @@ def test_flygpt_plan_balance(driver):
     """FlyGPT shape: the busiest workgroup's gather work (pieces x D) is within
     15 % of the average padded edge count per workgroup."""
     w = synthetic.make("flygpt", synthetic.DEFAULT_SEEDS["flygpt"])
-    for major, lens in ((w.dst, 5), (w.src, 4)):
-        p = replay(driver, major, w.num_nodes, lens=lens)
+    for major, kind in ((w.dst, FWD), (w.src, BWD)):
+        p = replay(driver, major, w.num_nodes, kind=kind)
         avg = len(major) / 32
         assert p["max_pieces"] * p["D"] <= 1.15 * avg + p["D"] * 160
+
+
+def test_flygpt_piece_lengths(driver):
+    """FlyGPT shape: the forward, whose waves without pieces skip their
+    gathers, takes D = 24 by the pieces x (D + 4) estimate; the backward,
+    whose every wave gathers D rows, takes the smallest D that fits, 18 (16
+    would need more than 1,024 pieces in some workgroup)."""
+    w = synthetic.make("flygpt", synthetic.DEFAULT_SEEDS["flygpt"])
+    assert replay(driver, w.dst, w.num_nodes, kind=FWD)["D"] == 24
+    p = replay(driver, w.src, w.num_nodes, kind=BWD)
+    assert p["D"] == 18
+    deg = np.bincount(w.src, minlength=w.num_nodes)
+    assert ((deg + 15) // 16).sum() > 32 * LANES
 
 
 @pytest.mark.parametrize("case", ["empty", "one_node", "single_edge", "one_row", "hub",
@@ -182,8 +200,8 @@ def test_row_beyond_a_workgroup(driver):
     """A row of more than 1024 x D edges fits no workgroup at any piece
     length: no plan (the per-microstep kernels run instead)."""
     assert replay(driver, [0] * (LANES * 24 + 1), 2) is None
-    assert replay(driver, [0] * (LANES * 20 + 1), 2, lens=4) is None
-    assert replay(driver, [0] * (LANES * 20 + 1), 2, lens=5) is not None
+    assert replay(driver, [0] * (LANES * 20 + 1), 2, kind=BWD) is None
+    assert replay(driver, [0] * (LANES * 20 + 1), 2) is not None
 
 
 def test_random_plans(driver):
@@ -194,5 +212,5 @@ def test_random_plans(driver):
         p = np.arange(1, N + 1, dtype=np.float64) ** -float(rng.choice([0.0, 1.0, 2.0]))
         major = rng.choice(N, size=E, p=p / p.sum())
         minor = rng.integers(0, N, size=E)
-        replay(driver, major, N, ranks=int(rng.choice([32, 8, 1])), lens=int(rng.choice([4, 5])),
+        replay(driver, major, N, ranks=int(rng.choice([32, 8, 1])), kind=[FWD, BWD][rng.integers(2)],
                minor=minor)
