@@ -20,6 +20,8 @@
  *   - Every tensor pointer is caller-owned device memory (hipMalloc'ed or
  *     torch CUDA storage), contiguous, fp32 for values and int64 for indices.
  *     A NULL pointer is accepted only for a tensor of zero elements.
+ *   - The `saved` and `workspace` buffers must start on a 256-byte boundary
+ *     (hipMalloc and torch allocations do); otherwise CK_ERR_BAD_VALUE.
  *   - Errors are returned as ck_status; no exception crosses the ABI.
  *     ck_last_error() gives a thread-local detail string of the last failure.
  *   - Forward and backward are asynchronous on `stream` and validate only

@@ -114,6 +114,17 @@ void set_error(const char* fmt, ...);
 void clear_error();
 ck_status check_graph(const ck_graph* g);
 
+// `saved` and workspace buffers start on a 256-byte boundary (as hipMalloc
+// and torch allocations do): the kernels address their parts with 16-byte
+// vector accesses at offsets that are multiples of 256.
+inline ck_status check_aligned(const void* p, const char* what) {
+  if (reinterpret_cast<uintptr_t>(p) % 256 != 0) {
+    set_error("%s does not start on a 256-byte boundary", what);
+    return CK_ERR_BAD_VALUE;
+  }
+  return CK_OK;
+}
+
 }  // namespace ckhip
 
 #define CK_HIP_TRY(expr)                                                            \

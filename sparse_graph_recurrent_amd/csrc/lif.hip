@@ -449,6 +449,8 @@ ck_status lif_check_ws(const ck_graph* g, void* workspace, size_t workspace_byte
     set_error("workspace is NULL");
     return CK_ERR_NULL_ARG;
   }
+  const ck_status rc = check_aligned(workspace, "workspace");
+  if (rc != CK_OK) return rc;
   *ws = lif_layout(g->N, g->E);
   if (workspace_bytes < ws->total) {
     set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, ws->total);

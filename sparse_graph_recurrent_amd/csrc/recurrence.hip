@@ -1012,7 +1012,7 @@ ck_status forward_checks(ck_graph_t g, const float* edge_values, const float* le
     set_error("NULL pointer for a non-empty tensor in forward");
     return CK_ERR_NULL_ARG;
   }
-  return CK_OK;
+  return check_aligned(saved, "saved");
 }
 
 // The forward once its arguments are checked; `workspace` holds at least
@@ -1106,6 +1106,8 @@ extern "C" ck_status ck_recurrence_forward(ck_graph_t g, const float* edge_value
     set_error("NULL workspace in forward");
     return CK_ERR_NULL_ARG;
   }
+  rc = check_aligned(workspace, "workspace");
+  if (rc != CK_OK) return rc;
   const size_t need = ws_total(g, d);
   if (workspace_bytes < need) {
     set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, need);
@@ -1160,6 +1162,9 @@ extern "C" ck_status ck_recurrence_backward(ck_graph_t g, const float* edge_valu
     set_error("NULL pointer for a non-empty tensor in backward");
     return CK_ERR_NULL_ARG;
   }
+  rc = check_aligned(saved, "saved");
+  if (rc == CK_OK) rc = check_aligned(workspace, "workspace");
+  if (rc != CK_OK) return rc;
   if (d.resident) {
     const size_t need = res_ws_layout(g, d.rd).total;
     if (workspace_bytes < need) {
@@ -1288,6 +1293,8 @@ extern "C" ck_status ck_recurrence_status(ck_graph_t g, int64_t T, int64_t B,
     set_error("workspace is NULL");
     return CK_ERR_NULL_ARG;
   }
+  rc = check_aligned(workspace, "workspace");
+  if (rc != CK_OK) return rc;
   const size_t need = res_ws_layout(g, d.rd).total;
   if (workspace_bytes < need) {
     set_error("workspace of %zu bytes is below the %zu required", workspace_bytes, need);

@@ -255,6 +255,20 @@ def test_invalid_values_are_rejected():
             assert ei.value.status == 12
 
 
+def test_misaligned_workspace_is_rejected():
+    """A workspace 16 bytes into an allocation (not on a 256-byte boundary)
+    is rejected with CK_ERR_BAD_VALUE before any work is queued."""
+    g = _graph([0, 1], [1, 0], 2)
+    w = to_dev(np.array([5, 5], np.int16))
+    d = to_dev(np.array([1, 1], np.int32))
+    v0 = to_dev(np.zeros(2, np.int32))
+    ws = sgr.lif_workspace(g)
+    big = torch.empty(ws.numel() + 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.lif_forward(g, w, d, v0, 3, 10, 0, 0, [2], workspace=big[16:])
+    assert ei.value.status == 12
+
+
 def test_graph_without_edges():
     log("LIF: graph without edges")
     _both([], [], 7, [], [], [0, 5, 10, 15, 20, -3, 99], 5, 12, 1, 1, [1])

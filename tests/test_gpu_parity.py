@@ -309,6 +309,29 @@ def test_workspace_too_small_is_rejected():
     assert ei.value.status == 6
 
 
+def test_misaligned_buffers_are_rejected():
+    """saved and workspace buffers must start on a 256-byte boundary: a
+    workspace or saved arena 16 bytes into an allocation is rejected with
+    CK_ERR_BAD_VALUE before any work is queued."""
+    w = synthetic.make("tiny")
+    g = make_graph(w)
+    sb, wb = sgr.recurrence_sizes(g, w.T, w.B, w.microsteps)
+    ins = [to_dev(x) for x in (w.edge_values, w.leak, w.bias, w.drives, w.state0)]
+    ws = torch.empty(wb + 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.recurrence_forward(g, *ins, w.microsteps, workspace=ws[16:])
+    assert ei.value.status == 12
+    saved = torch.empty(sb + 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.recurrence_forward(g, *ins, w.microsteps, saved=saved[16:], workspace=ws[:wb])
+    assert ei.value.status == 12
+    out, sv, w2 = sgr.recurrence_forward(g, *ins, w.microsteps, workspace=ws[:wb])
+    with pytest.raises(sgr.CkError) as ei:
+        sgr.recurrence_backward(g, ins[0], ins[1], ins[4], w.microsteps, sv, to_dev(w.grad_out),
+                                workspace=ws[16:])
+    assert ei.value.status == 12
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_hip_graph_replay_matches_eager(path):
     """Forward+backward captured into a HIP graph (torch.cuda.CUDAGraph on the
