@@ -66,9 +66,9 @@ LifWs lif_layout(int64_t N, int64_t E) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   LifWs w;
   size_t o = 0;
-  // (16 spare bytes: lif_gather_lds reads positions in pairs, and an odd E
-  // leaves the last pair half past the records)
-  w.rec = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 8 + 16);
+  // (32 spare bytes: lif_gather_lds reads positions in groups of 4, and the
+  // last group may reach up to 3 positions past the records)
+  w.rec = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 8 + 32);
   w.dst = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 4);
   w.words = o; o = al(o + (size_t)std::max<int64_t>(E, 1) * 4);
   w.acc = o;   o = al(o + (size_t)N * 8);
@@ -221,19 +221,21 @@ __device__ __forceinline__ int wave_prefix_sum(int v, int lane) {
 // delay d, then each position tests its source's bit.  Bit rows are `ws`
 // words apart (a multiple of 4), so the copy moves 16-byte words, at most
 // kLifCopy of them per lane, all loads in flight together.  Grid-stride over
-// the positions in chunks of kLifChunk; a lane takes two neighbouring
-// positions per 16-byte load, so a wave covers 128 positions per load, and
-// each chunk's records are loaded while the previous chunk is summed.  Per
-// wave and group of 128 positions: one prefix sum over the lanes' pair sums
-// (a wave's group holds at most 128 impulses, |impulse| < 2^15, so 32 bits
-// are exact) gives the prefix at every position; the run starts (the group's
-// first position and every row change) come from two ballots, and the last
-// position of each run adds its run's total (its prefix minus the prefix
-// before the run's first position, found in the lane of the run's start)
-// with one 64-bit atomic.  Each stage runs over a lane's kLifPairs pairs at
-// once, so their LDS reads, prefix sums and shuffles overlap.
-constexpr int kLifPairs = 3;
-constexpr int kLifChunk = kLifPairs * 2 * 1024;
+// the positions in chunks of kLifChunk; a lane takes kLifQ neighbouring
+// positions in kLifQ / 2 16-byte loads, so a wave covers 64 kLifQ positions
+// per group, and each chunk's records are loaded while the previous chunk is
+// summed.  Per wave and group: one prefix sum over the lanes' sums (a group
+// holds at most 256 impulses, |impulse| < 2^15, so 32 bits are exact) gives
+// the prefix at every position; the run starts (the group's first position
+// and every row change) come from two ballots, and the last position of each
+// run adds its run's total (its prefix minus the prefix before the run's
+// first position, found in the lane of the run's start) with one 64-bit
+// atomic.
+constexpr int kLifQ = 4;       // positions per lane and load group (kLifQ / 2 16-byte loads)
+constexpr int kLifGroups = 1;  // load groups per lane and chunk
+constexpr int kLifChunk = kLifGroups * kLifQ * 1024;
+static_assert(kLifQ % 2 == 0 && 8 * (kLifQ - 1) <= 32,
+              "a group's loads reach at most the record region's 32 spare bytes");
 constexpr int kLifCopy = kLifLdsBytes / 16 / 1024;
 
 __device__ __forceinline__ int lif_rec_row(int x, int y) {
@@ -247,19 +249,23 @@ __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ 
   extern __shared__ uint4 sb4[];  // [R][ws / 4]
   const uint32_t* sb = reinterpret_cast<const uint32_t*>(sb4);
   const int lane = threadIdx.x & 63;
-  // pair j of a chunk starting at `base`: positions base + 2048 j + 2 tid and
-  // the next; the 16-byte loads start at an even position no later than the
-  // last even one, which the record region's 16 spare bytes keep in range.
-  // The first chunk's records are requested before the bit rows, so both
-  // round trips overlap.
+  // load group j of a chunk starting at `base`: positions
+  // base + kLifQ (1024 j + tid) + i, i < kLifQ; the loads start at a group of
+  // positions no later than the last one, which the record region's spare
+  // bytes keep in range.  The first chunk's records are requested before the
+  // bit rows, so both round trips overlap.
   const int4* rec4 = reinterpret_cast<const int4*>(rec);
-  const int64_t last_pair = (E - 1) >> 1;
+  const int64_t last_q = (E - 1) / kLifQ;
   const int64_t stride = (int64_t)gridDim.x * kLifChunk;
-  int4 x[kLifPairs];
+  constexpr int NL = kLifQ / 2;
+  int4 x[kLifGroups][NL];
   int64_t base = (int64_t)blockIdx.x * kLifChunk;
 #pragma unroll
-  for (int j = 0; j < kLifPairs; ++j)
-    x[j] = rec4[std::min<int64_t>((base >> 1) + j * 1024 + threadIdx.x, last_pair)];
+  for (int j = 0; j < kLifGroups; ++j) {
+    const int64_t q = std::min<int64_t>(base / kLifQ + j * 1024 + threadIdx.x, last_q);
+#pragma unroll
+    for (int h = 0; h < NL; ++h) x[j][h] = rec4[NL * q + h];
+  }
   {
     const int w4 = ws / 4, n4 = R * w4;
     uint4 tmp[kLifCopy];
@@ -277,75 +283,94 @@ __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ 
   }
   __syncthreads();
   for (; base < E; base += stride) {
-    // the next chunk's records (clamped into range: the loads are unconditional)
-    int4 xn[kLifPairs];
+    int4 xn[kLifGroups][NL];
 #pragma unroll
-    for (int j = 0; j < kLifPairs; ++j)
-      xn[j] = rec4[std::min<int64_t>(((base + stride) >> 1) + j * 1024 + threadIdx.x, last_pair)];
-    int r0[kLifPairs], r1[kLifPairs], c0[kLifPairs], c1[kLifPairs];
-    uint32_t w0[kLifPairs], w1[kLifPairs];
+    for (int j = 0; j < kLifGroups; ++j) {
+      const int64_t q = std::min<int64_t>((base + stride) / kLifQ + j * 1024 + threadIdx.x, last_q);
 #pragma unroll
-    for (int j = 0; j < kLifPairs; ++j) {
-      const int64_t p = base + 2 * (j * 1024 + (int64_t)threadIdx.x);
-      // a position past the records (the clamped last pair's second half may
-      // be the spare bytes) looks up word 0 and counts nothing
-      if (p + 1 >= E) {
-        x[j].z = 0;
-        x[j].w = 0;
+      for (int h = 0; h < NL; ++h) xn[j][h] = rec4[NL * q + h];
+    }
+    int r[kLifGroups][kLifQ], c[kLifGroups][kLifQ];
+#pragma unroll
+    for (int j = 0; j < kLifGroups; ++j) {
+      const int64_t p = base + kLifQ * (j * 1024 + (int64_t)threadIdx.x);
+      int xs[2 * kLifQ];
+#pragma unroll
+      for (int h = 0; h < NL; ++h) {
+        xs[4 * h] = x[j][h].x;
+        xs[4 * h + 1] = x[j][h].y;
+        xs[4 * h + 2] = x[j][h].z;
+        xs[4 * h + 3] = x[j][h].w;
       }
-      r0[j] = p < E ? lif_rec_row(x[j].x, x[j].y) : -1;
-      r1[j] = p + 1 < E ? lif_rec_row(x[j].z, x[j].w) : -1;
-      w0[j] = sb[(int)(((uint32_t)x[j].y >> 16) & 15u) * ws + (int)(((uint32_t)x[j].x & 0xFFFFFu) >> 5)];
-      w1[j] = sb[(int)(((uint32_t)x[j].w >> 16) & 15u) * ws + (int)(((uint32_t)x[j].z & 0xFFFFFu) >> 5)];
+#pragma unroll
+      for (int i = 0; i < kLifQ; ++i) {
+        // a position past the records reads word 0 and counts nothing
+        const bool live = p + i < E;
+        const uint32_t xx = live ? (uint32_t)xs[2 * i] : 0u, yy = live ? (uint32_t)xs[2 * i + 1] : 0u;
+        r[j][i] = live ? lif_rec_row((int)xx, (int)yy) : -1;
+        const uint32_t w = sb[(int)((yy >> 16) & 15u) * ws + (int)((xx & 0xFFFFFu) >> 5)];
+        c[j][i] = live && ((w >> (xx & 31u)) & 1u) ? (int)(int16_t)(yy & 0xFFFFu) : 0;
+      }
+    }
+    int rprev[kLifGroups], Pin[kLifGroups];
+#pragma unroll
+    for (int j = 0; j < kLifGroups; ++j) rprev[j] = __shfl_up(r[j][kLifQ - 1], 1);
+#pragma unroll
+    for (int j = 0; j < kLifGroups; ++j) {
+      int tsum = 0;
+#pragma unroll
+      for (int i = 0; i < kLifQ; ++i) tsum += c[j][i];
+      Pin[j] = wave_prefix_sum(tsum, lane);
     }
 #pragma unroll
-    for (int j = 0; j < kLifPairs; ++j) {
-      c0[j] = r0[j] >= 0 && ((w0[j] >> (x[j].x & 31)) & 1u) ? (int)(int16_t)(x[j].y & 0xFFFF) : 0;
-      c1[j] = r1[j] >= 0 && ((w1[j] >> (x[j].z & 31)) & 1u) ? (int)(int16_t)(x[j].w & 0xFFFF) : 0;
-    }
-    int rprev[kLifPairs], Pin[kLifPairs];
+    for (int j = 0; j < kLifGroups; ++j) {
+      // prefixes at each position (Ex: before the lane's first), run starts
+      // (the first position against the previous lane's last), the prefix
+      // before the lane's last run start (fetched by the lanes whose first
+      // run continues from an earlier lane; lane 0 always starts a run)
+      int P[kLifQ];
+      bool st[kLifQ];
+      int run = 0;
 #pragma unroll
-    for (int j = 0; j < kLifPairs; ++j) rprev[j] = __shfl_up(r1[j], 1);
+      for (int i = 0; i < kLifQ; ++i) run += c[j][i];
+      const int Ex = Pin[j] - run;
+      int acc_i = Ex;
 #pragma unroll
-    for (int j = 0; j < kLifPairs; ++j) Pin[j] = wave_prefix_sum(c0[j] + c1[j], lane);
-    bool s0[kLifPairs], s1[kLifPairs];
-    int Ex[kLifPairs], P0[kLifPairs], bprev[kLifPairs];
-    unsigned long long S0[kLifPairs];
+      for (int i = 0; i < kLifQ; ++i) {
+        acc_i += c[j][i];
+        P[i] = acc_i;
+        st[i] = i == 0 ? (lane == 0 || rprev[j] != r[j][0]) : r[j][i] != r[j][i - 1];
+      }
+      bool any = false;
+      int before_last = Ex;
 #pragma unroll
-    for (int j = 0; j < kLifPairs; ++j) {
-      // prefixes: before the pair (Ex), through its first position (P0),
-      // through both (Pin); run starts at the first (s0) and second (s1)
-      Ex[j] = Pin[j] - c0[j] - c1[j];
-      P0[j] = Ex[j] + c0[j];
-      s0[j] = lane == 0 || rprev[j] != r0[j];
-      s1[j] = r1[j] != r0[j];
-      S0[j] = __ballot(s0[j]);
-      const unsigned long long F = __ballot(s0[j] || s1[j]);
-      // the prefix before this lane's last run start, fetched by the lanes
-      // whose first run continues from an earlier lane (lane 0 always starts
-      // a run, so such a lane exists below every lane > 0)
-      const int before_last = s1[j] ? P0[j] : Ex[j];
+      for (int i = 0; i < kLifQ; ++i)
+        if (st[i]) {
+          any = true;
+          before_last = i == 0 ? Ex : P[i - 1];
+        }
+      const unsigned long long S0 = __ballot(st[0]);
+      const unsigned long long F = __ballot(any);
       const unsigned long long below = F & ((1ull << lane) - 1ull);
       const int m = below ? 63 - __clzll(below) : 0;
-      bprev[j] = __shfl(before_last, m);
+      const int bprev = __shfl(before_last, m);
+      int before = bprev;
+#pragma unroll
+      for (int i = 0; i < kLifQ; ++i) {
+        if (st[i]) before = i == 0 ? Ex : P[i - 1];
+        // a position ends a run when the next one starts one (for the last
+        // position: the next lane's first, or the end of the wave's group)
+        const bool end = i + 1 < kLifQ ? st[i + 1] : (lane == 63 || (((S0 >> lane) >> 1) & 1ull) != 0);
+        const int sum = P[i] - before;
+        if (r[j][i] >= 0 && end && sum != 0)
+          atomicAdd(reinterpret_cast<unsigned long long*>(&acc[r[j][i]]),
+                    (unsigned long long)(long long)sum);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < kLifPairs; ++j) {
-      // the first position ends a run when the second starts one
-      const int sum0 = P0[j] - (s0[j] ? Ex[j] : bprev[j]);
-      if (r0[j] >= 0 && s1[j] && sum0 != 0)
-        atomicAdd(reinterpret_cast<unsigned long long*>(&acc[r0[j]]),
-                  (unsigned long long)(long long)sum0);
-      // the second ends one when the next lane's first starts one, or at
-      // the group's end
-      const bool end1 = lane == 63 || (((S0[j] >> lane) >> 1) & 1ull) != 0;
-      const int sum1 = Pin[j] - (s1[j] ? P0[j] : (s0[j] ? Ex[j] : bprev[j]));
-      if (r1[j] >= 0 && end1 && sum1 != 0)
-        atomicAdd(reinterpret_cast<unsigned long long*>(&acc[r1[j]]),
-                  (unsigned long long)(long long)sum1);
-    }
+    for (int j = 0; j < kLifGroups; ++j)
 #pragma unroll
-    for (int j = 0; j < kLifPairs; ++j) x[j] = xn[j];
+      for (int h = 0; h < NL; ++h) x[j][h] = xn[j][h];
   }
 }
 

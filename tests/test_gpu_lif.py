@@ -105,12 +105,13 @@ def test_lookup_boundaries(seed, N, E, max_delay, T):
     assert s[1:].sum() > 0
 
 
-@pytest.mark.parametrize("E", [1, 2, 3, 127, 129, 2049, 6143, 6145, 12289])
+@pytest.mark.parametrize("E", [1, 2, 3, 5, 127, 129, 255, 257, 4095, 4097, 6145, 8193, 12289])
 def test_odd_and_ragged_edge_counts(E):
-    """The LDS-lookup gather reads two positions per lane in one 16-byte load
-    and walks the positions in chunks of 6,144: odd edge counts (the last
-    pair half past the records) and counts just around a pair, a wave's 128
-    positions and a chunk, bit-exact against the oracle."""
+    """The LDS-lookup gather reads four positions per lane in two 16-byte
+    loads and walks the positions in chunks of 4,096: edge counts that leave
+    the last group of four partly past the records, and counts just around a
+    group, a wave's 256 positions and a chunk, bit-exact against the
+    oracle."""
     log(f"LIF: edge count {E}")
     N = 64 if E < 100 else 300
     rng = np.random.default_rng(E)
