@@ -12,17 +12,17 @@
 //   refractory: drop I, count down; otherwise leak, add I (checked), spike at
 //   the threshold, reset, start the refractory count.
 // Two launches per step:
-//   lif_gather   one thread per CSR position: the edge's impulse if its source
-//                spiked d steps earlier; a segmented sum over each wave's run
-//                of positions of one row, then one 64-bit integer atomic add
-//                per run into I[row].  Integer sums are exact and associative,
+//   lif_gather   four CSR positions per lane: each edge's impulse if its
+//                source spiked d steps earlier (one byte read of the spike
+//                history), a DPP prefix sum over the wave's positions, and
+//                one 64-bit integer atomic add per run of positions of one
+//                row into I[row].  Integer sums are exact and associative,
 //                so the result does not depend on the order of the atomics.
 //                When the bit rows of the steps the delays reach fit in LDS
 //                (lif_gather_lds), each workgroup first copies them there and
 //                looks the spikes up in LDS instead of one scattered byte
-//                read per edge, reads 8-byte records that carry the row
-//                (no separate destination), and sums the runs with DPP
-//                prefix sums.
+//                read per edge, and reads 8-byte records that carry the row
+//                (no separate destination).
 //   lif_update   one thread per neuron: the state update above; writes the
 //                step's spikes and potentials (and the step's spike bits into
 //                a ring of kLifRing bit rows), clears I.
@@ -69,7 +69,8 @@ LifWs lif_layout(int64_t N, int64_t E) {
   // (32 spare bytes: lif_gather_lds reads positions in groups of 4, and the
   // last group may reach up to 3 positions past the records)
   w.rec = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 8 + 32);
-  w.dst = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 4);
+  // (16 spare bytes: lif_gather reads the rows of 4 positions at once)
+  w.dst = o;   o = al(o + (size_t)std::max<int64_t>(E, 1) * 4 + 16);
   w.words = o; o = al(o + (size_t)std::max<int64_t>(E, 1) * 4);
   w.acc = o;   o = al(o + (size_t)N * 8);
   w.v = o;     o = al(o + (size_t)N * 4);
@@ -172,35 +173,6 @@ __global__ __launch_bounds__(256) void lif_rows(const int32_t* __restrict__ row_
   const int lane = threadIdx.x & 63;
   const int32_t b = row_ptr[i], e = row_ptr[i + 1];
   for (int32_t k = b + lane; k < e; k += 64) dst[k] = (int32_t)i;
-}
-
-__global__ __launch_bounds__(256) void lif_gather(const int2* __restrict__ rec,
-                                                  const int32_t* __restrict__ dst, int64_t E,
-                                                  int64_t N, int t,
-                                                  const uint8_t* __restrict__ spikes,
-                                                  long long* __restrict__ acc) {
-  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int lane = threadIdx.x & 63;
-  int row = -1;
-  long long c = 0;
-  if (k < E) {
-    const int2 x = rec[k];
-    row = dst[k];
-    const int d = (int)((uint32_t)x.y >> 16);
-    if (t >= d && spikes[(size_t)(t - d) * N + x.x]) c = (long long)(int16_t)(x.y & 0xFFFF);
-  }
-  // inclusive segmented sum over lanes holding the same row (rows are
-  // non-decreasing along the positions, so a row's lanes are contiguous)
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const long long v = __shfl_up(c, off);
-    const int rr = __shfl_up(row, off);
-    if (lane >= off && rr == row) c += v;
-  }
-  const int next = __shfl_down(row, 1);
-  const bool last = lane == 63 || next != row;
-  if (row >= 0 && last && c != 0)
-    atomicAdd(reinterpret_cast<unsigned long long*>(&acc[row]), (unsigned long long)c);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts within
@@ -371,6 +343,84 @@ __global__ __launch_bounds__(1024) void lif_gather_lds(const int2* __restrict__ 
     for (int j = 0; j < kLifGroups; ++j)
 #pragma unroll
       for (int h = 0; h < NL; ++h) x[j][h] = xn[j][h];
+  }
+}
+
+
+// lif_gather with one byte read of the spike history per position (delays
+// beyond the bit ring, or graphs too large for the LDS bit rows): a lane
+// takes kLifQ neighbouring positions (their records in kLifQ / 2 16-byte
+// loads, their rows in one), and the run sums are formed as in
+// lif_gather_lds.
+__global__ __launch_bounds__(256) void lif_gather(const int2* __restrict__ rec,
+                                                  const int32_t* __restrict__ dst, int64_t E,
+                                                  int64_t N, int t,
+                                                  const uint8_t* __restrict__ spikes,
+                                                  long long* __restrict__ acc) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t p = g * kLifQ;
+  // (groups past the records load the last group, within the spare bytes)
+  const int64_t q = std::min<int64_t>(g, (E - 1) / kLifQ);
+  constexpr int NL = kLifQ / 2;
+  const int4* rec4 = reinterpret_cast<const int4*>(rec);
+  int xs[2 * kLifQ];
+#pragma unroll
+  for (int h = 0; h < NL; ++h) {
+    const int4 v = rec4[NL * q + h];
+    xs[4 * h] = v.x;
+    xs[4 * h + 1] = v.y;
+    xs[4 * h + 2] = v.z;
+    xs[4 * h + 3] = v.w;
+  }
+  static_assert(kLifQ == 4, "one 16-byte load of rows per group");
+  const int4 rd = reinterpret_cast<const int4*>(dst)[q];
+  const int rows[kLifQ] = {rd.x, rd.y, rd.z, rd.w};
+  int r[kLifQ], c[kLifQ];
+#pragma unroll
+  for (int i = 0; i < kLifQ; ++i) {
+    const bool live = p + i < E;
+    const uint32_t x = (uint32_t)xs[2 * i], y = (uint32_t)xs[2 * i + 1];
+    const int d = (int)(y >> 16);
+    r[i] = live ? rows[i] : -1;
+    c[i] = live && t >= d && spikes[(size_t)(t - d) * N + x] ? (int)(int16_t)(y & 0xFFFFu) : 0;
+  }
+  const int rprev = __shfl_up(r[kLifQ - 1], 1);
+  int tsum = 0;
+#pragma unroll
+  for (int i = 0; i < kLifQ; ++i) tsum += c[i];
+  const int Pin = wave_prefix_sum(tsum, lane);
+  const int Ex = Pin - tsum;
+  int P[kLifQ];
+  bool st[kLifQ];
+  int run = Ex;
+#pragma unroll
+  for (int i = 0; i < kLifQ; ++i) {
+    run += c[i];
+    P[i] = run;
+    st[i] = i == 0 ? (lane == 0 || rprev != r[0]) : r[i] != r[i - 1];
+  }
+  bool any = false;
+  int before_last = Ex;
+#pragma unroll
+  for (int i = 0; i < kLifQ; ++i)
+    if (st[i]) {
+      any = true;
+      before_last = i == 0 ? Ex : P[i - 1];
+    }
+  const unsigned long long S0 = __ballot(st[0]);
+  const unsigned long long F = __ballot(any);
+  const unsigned long long below = F & ((1ull << lane) - 1ull);
+  const int bprev = __shfl(before_last, below ? 63 - __clzll(below) : 0);
+  int before = bprev;
+#pragma unroll
+  for (int i = 0; i < kLifQ; ++i) {
+    if (st[i]) before = i == 0 ? Ex : P[i - 1];
+    const bool end = i + 1 < kLifQ ? st[i + 1] : (lane == 63 || (((S0 >> lane) >> 1) & 1ull) != 0);
+    const int sum = P[i] - before;
+    if (r[i] >= 0 && end && sum != 0)
+      atomicAdd(reinterpret_cast<unsigned long long*>(&acc[r[i]]),
+                (unsigned long long)(long long)sum);
   }
 }
 
@@ -572,7 +622,8 @@ ck_status lif_run_body(const ck_graph* g, const LifParams& p, const int32_t* v0,
                                                           reinterpret_cast<const uint4*>(b.bits),
                                                           b.acc);
         else
-          lif_gather<<<blocks(E), 256, 0, stream>>>(b.rec, b.dst, E, N, (int)t, spikes, b.acc);
+          lif_gather<<<blocks((E + kLifQ - 1) / kLifQ), 256, 0, stream>>>(b.rec, b.dst, E, N,
+                                                                         (int)t, spikes, b.acc);
       });
       if (rc != CK_OK) return rc;
     }
