@@ -650,12 +650,9 @@ __global__ void res_prologue(const float* __restrict__ values, const int32_t* __
   }
 }
 
-// out[t][b][i] = h^((t+1) M)[b / 4][i][b % 4], or NaN everywhere if the
-// resident kernel raised its error flag.  The flag is also copied into the
-// saved arena's status word, so that a backward given this arena knows.
-// After the resident forward (whose owners wrote the outputs): the saved
-// arena's status word, and NaN in every output if the kernel raised its
-// error flag.
+// After the resident forward (whose owners wrote the outputs): the kernel's
+// error flag copied into the saved arena's status word (so that a backward
+// given this arena knows), and NaN in every output if the flag is raised.
 __global__ void res_fwd_status(const unsigned* __restrict__ ctl, int64_t n,
                                float* __restrict__ out, unsigned* __restrict__ saved_status) {
   const unsigned err = ctl[kCtlErr];
